@@ -1,0 +1,209 @@
+/*
+ * mla_absorb.h -- C ABI of the MI355X (gfx950) absorbed-MLA decode library.
+ *
+ * One decode step of DeepSeek Multi-head Latent Attention in "absorb" mode,
+ * for one layer, split into four calls that launch hand-written HIP kernels
+ * on the caller's stream:
+ *
+ *   mla_absorb_q        q_lat[b,h,:]  = q_nope[b,h,:] . W_UK[h]            (key absorption)
+ *   mla_decode_latent   scores of every head against the shared 576-wide
+ *                       latent cache (512 latent + 64 decoupled-RoPE key),
+ *                       online softmax, o_lat = sum_t p_t c_t in latent space
+ *   mla_combine_splits  log-sum-exp merge of split-KV partial results
+ *   mla_expand_v        out[b,h,:] = W_UV[h] . o_lat[b,h,:]                 (value absorption)
+ *
+ * The method is the one described on the source pages (cited by title):
+ *   [AUDIT]  "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界":
+ *            §2.2 moves W_UK onto the query, §2.3 applies W_UV after the
+ *            latent aggregation, §2.4 keeps the 64-wide RoPE key cached
+ *            separately, §6.1 describes absorbed decode as MQA with a
+ *            576-wide key and a 512-wide value.
+ *   [MLA80]  "80 行 PyTorch 从零写 DeepSeek 的 MLA ..." §4-§5: the absorbed
+ *            decode (Q_abs = q . W_UK, content + rope scores, latent context
+ *            then W_UV).
+ *   [G5SPEC] "G5 MLA KV 访存建模设计规格": eq:gmkv-cache (bytes per cached
+ *            token), eq:gmkv-read (bytes one decode step reads, no head
+ *            term), and Appendix C (required fields, error naming the field).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named "device" are HIP device pointers; the library never
+ *   dereferences them on the host.  All device buffers are owned by the
+ *   caller, who allocates and frees them; the library allocates nothing,
+ *   frees nothing, keeps no state between calls and never synchronises.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every kernel is launched asynchronously on it.
+ * - bf16 = IEEE bfloat16 stored as uint16; fp8 = OCP FP8 E4M3 ("FN") stored
+ *   as uint8; fp32 = IEEE binary32.
+ * - Every argument check runs on the host before anything is launched.  On
+ *   failure the call returns a non-zero mla_status, launches nothing, and
+ *   mla_last_error() returns a message naming the offending field.  The
+ *   message is thread-local and stays valid until the next call on the same
+ *   thread.
+ * - Dimensions have no defaults: a zero or missing dimension is
+ *   MLA_ERR_MISSING_DIM, never silently replaced ([G5SPEC] constraints).
+ * - Supported shapes: kv_lora_rank 512, qk_rope_head_dim 64,
+ *   qk_nope_head_dim 128, v_head_dim 128, num_heads in {16, 32, 64, 128}.
+ *   Others return MLA_ERR_UNSUPPORTED.
+ * - Device pointers to bf16/fp8/fp32 tensors must be 16-byte aligned.
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,          /* a required pointer is NULL                    */
+  MLA_ERR_MISSING_DIM = 2,   /* a required dimension is zero / missing        */
+  MLA_ERR_UNSUPPORTED = 3,   /* a shape or option this library does not build */
+  MLA_ERR_BAD_LENGTH = 4,    /* max_seq_len / split / block-size arguments    */
+  MLA_ERR_BUFFER = 5,        /* inconsistent buffer description               */
+  MLA_ERR_ALIGN = 6,         /* pointer or stride not 16-byte aligned         */
+  MLA_ERR_HIP = 7            /* the HIP runtime reported an error at launch   */
+} mla_status;
+
+typedef enum {
+  MLA_DTYPE_BF16 = 0,        /* cache elements are bfloat16                   */
+  MLA_DTYPE_FP8_E4M3 = 1     /* cache elements are E4M3 with a per-token fp32
+                                scale: value = e4m3(code) * token_scale[slot] */
+} mla_dtype;
+
+/* Shape of one MLA attention layer.  All fields are required. */
+typedef struct mla_dims {
+  int32_t batch;             /* B: sequences decoded in this step            */
+  int32_t num_heads;         /* H: query heads (16, 32, 64 or 128)           */
+  int32_t kv_lora_rank;      /* d_c: latent width, must be 512              */
+  int32_t qk_rope_head_dim;  /* d_r: decoupled RoPE key width, must be 64    */
+  int32_t qk_nope_head_dim;  /* d_n: per-head no-RoPE query width, 128       */
+  int32_t v_head_dim;        /* d_v: per-head value width, 128               */
+  float softmax_scale;       /* multiplies q.k before the softmax; > 0       */
+} mla_dims;
+
+/*
+ * Where the cached rows of the latent cache live.
+ *
+ * Token t of sequence b is stored in "slot"
+ *     slot = b * seq_stride + t                                   (contiguous)
+ *     slot = block_table[b * max_blocks_per_seq + t / block_size]
+ *              * block_size + t % block_size                      (paged)
+ * Its 512 latent elements start at kv + slot * kv_stride and its 64 RoPE-key
+ * elements at pe + slot * pe_stride (strides in elements).  A fused
+ * [.., 576] row layout is kv = base, pe = base + 512, both strides 576.
+ * The RoPE half holds keys that are already rotated.
+ *
+ * Paged mode: block_table is a device int32 array [batch, max_blocks_per_seq]
+ * of physical block ids; block_size must be a positive multiple of 32.  Only
+ * entries covering tokens < seq_lens[b] are read.  Contiguous mode: block_table
+ * is NULL and seq_stride >= every seq_lens[b].
+ */
+typedef struct mla_cache {
+  int32_t dtype;               /* mla_dtype                                   */
+  const void *kv;              /* device: latent element 0 of slot 0          */
+  const void *pe;              /* device: RoPE-key element 0 of slot 0        */
+  int64_t kv_stride;           /* elements between consecutive slots (kv)     */
+  int64_t pe_stride;           /* elements between consecutive slots (pe)     */
+  const float *token_scale;    /* device [num_slots] fp32, fp8 only, else NULL*/
+  int64_t seq_stride;          /* contiguous: slots per sequence              */
+  const int32_t *block_table;  /* device, paged only; NULL = contiguous       */
+  int32_t block_size;          /* paged: tokens per block                     */
+  int32_t max_blocks_per_seq;  /* paged: row length of block_table            */
+} mla_cache;
+
+/* Message for the last failed call on this thread ("" after success). */
+const char *mla_last_error(void);
+
+/* Library version string. */
+const char *mla_version(void);
+
+/*
+ * Bytes one cached token occupies in one layer: (d_c + d_r) * e, plus 4 for
+ * the fp32 token scale of an fp8 cache ([G5SPEC] eq:gmkv-cache).  Only
+ * dims->kv_lora_rank and dims->qk_rope_head_dim are read; both are required.
+ * Host-only; launches nothing.
+ */
+mla_status mla_kv_cache_bytes(const mla_dims *dims, int32_t dtype, size_t *bytes_per_token);
+
+/*
+ * Bytes one decode step reads from the latent cache of one layer:
+ * sum_b seq_lens[b] * bytes_per_token ([G5SPEC] eq:gmkv-read; no head term).
+ * host_seq_lens is a HOST array of dims->batch lengths.  Host-only.
+ */
+mla_status mla_decode_kv_read_bytes(const mla_dims *dims, int32_t dtype, const int32_t *host_seq_lens,
+                                    size_t *bytes);
+
+/*
+ * Key absorption ([AUDIT] §2.2): q_lat[b,h,c] = sum_d q_nope[b,h,d] * W_UK[h,d,c],
+ * fp32 accumulation, rounded to bf16.
+ *   q_nope  device bf16 [B, H, 128]
+ *   w_uk    device bf16 [H, 128, 512]
+ *   q_lat   device bf16 [B, H, 512] (output)
+ */
+mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_uk, void *q_lat,
+                        void *stream);
+
+/*
+ * Latent attention ([AUDIT] §2.2-§2.4, §6.1): for every sequence b and head h
+ *   s_t     = softmax_scale * (q_lat[b,h] . c_t + q_pe[b,h] . kR_t),  t < seq_lens[b]
+ *   o_lat   = sum_t softmax(s)_t * c_t          (512 wide, latent space)
+ *   lse     = ln sum_t exp(s_t)
+ * The decode query attends to every cached token of its sequence.
+ *
+ *   q_lat     device bf16 [B, H, 512]
+ *   q_pe      device bf16 [B, H, 64]   (already rotated)
+ *   seq_lens  device int32 [B], each in [1, max_seq_len]
+ *   max_seq_len  host int: an upper bound of seq_lens, sizes the launch
+ *   num_splits   P >= 1.  Split-KV: token range of split i is
+ *                [i*chunk, min((i+1)*chunk, seq_lens[b])) with
+ *                chunk = 32 * ceil(ceil(max_seq_len / P) / 32).
+ *   P == 1: writes o_lat (device bf16 [B, H, 512]) and lse (device fp32 [B, H]);
+ *           o_part / lse_part must be NULL.
+ *   P  > 1: writes o_part (device fp32 [B, P, H, 512], each split normalised
+ *           by its own softmax sum) and lse_part (device fp32 [B, P, H]); an
+ *           empty split gets o = 0 and lse = -inf.  o_lat / lse must be NULL;
+ *           merge with mla_combine_splits.
+ * fp8 caches are not built yet (MLA_ERR_UNSUPPORTED).
+ */
+mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
+                             const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,
+                             int32_t num_splits, float *o_part, float *lse_part, void *o_lat,
+                             float *lse, void *stream);
+
+/*
+ * Split-KV merge: LSE = ln sum_i exp(lse_part[b,i,h]),
+ * o_lat[b,h] = sum_i exp(lse_part[b,i,h] - LSE) * o_part[b,i,h]; splits with
+ * lse = -inf carry no weight.
+ *   o_part device fp32 [B, P, H, 512], lse_part device fp32 [B, P, H]
+ *   o_lat  device bf16 [B, H, 512] (output), lse device fp32 [B, H] (output,
+ *          may be NULL)
+ */
+mla_status mla_combine_splits(const mla_dims *dims, const float *o_part, const float *lse_part,
+                              int32_t num_splits, void *o_lat, float *lse, void *stream);
+
+/*
+ * Value absorption ([AUDIT] §2.3): out[b,h,j] = sum_c W_UV[h,j,c] * o_lat[b,h,c],
+ * fp32 accumulation, rounded to bf16.
+ *   o_lat device bf16 [B, H, 512]
+ *   w_uv  device bf16 [H, 128, 512]
+ *   out   device bf16 [B, H, 128] (output)
+ */
+mla_status mla_expand_v(const mla_dims *dims, const void *o_lat, const void *w_uv, void *out,
+                        void *stream);
+
+/*
+ * Recommended num_splits for mla_decode_latent on a device with `num_cus`
+ * compute units: enough workgroups to fill the chip, each split at least
+ * 256 tokens.  Host-only.
+ */
+int32_t mla_recommended_splits(const mla_dims *dims, int32_t max_seq_len, int32_t num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

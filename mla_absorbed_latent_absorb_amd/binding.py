@@ -1,0 +1,291 @@
+"""Thin Python binding of libmla_absorb.so (the C ABI in include/mla_absorb.h).
+
+Argument marshalling only: each function checks the torch tensors it is given
+(device, dtype, shape, contiguity), passes their data pointers and the current
+HIP stream to the C function of the same name, and raises MlaError with the
+library's message on a non-zero status.  Every step of the decode runs in the
+library's HIP kernels; there is no fallback path.  PyTorch provides device
+memory and streams only.
+"""
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+MLA_DTYPE_BF16 = 0
+MLA_DTYPE_FP8_E4M3 = 1
+
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR_UNSUPPORTED",
+           4: "MLA_ERR_BAD_LENGTH", 5: "MLA_ERR_BUFFER", 6: "MLA_ERR_ALIGN", 7: "MLA_ERR_HIP"}
+
+EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
+            "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
+            "mla_recommended_splits"]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("kv_lora_rank", ctypes.c_int32), ("qk_rope_head_dim", ctypes.c_int32),
+                ("qk_nope_head_dim", ctypes.c_int32), ("v_head_dim", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class MlaCache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("kv", ctypes.c_void_p), ("pe", ctypes.c_void_p),
+                ("kv_stride", ctypes.c_int64), ("pe_stride", ctypes.c_int64),
+                ("token_scale", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path():
+    return _build.LIB_PATH
+
+
+def load():
+    """Load libmla_absorb.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m mla_absorbed_latent_absorb_amd.build "
+                           "or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    st = ctypes.c_int
+    D = ctypes.POINTER(MlaDims)
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_version.restype = ctypes.c_char_p
+    lib.mla_version.argtypes = []
+    lib.mla_kv_cache_bytes.restype = st
+    lib.mla_kv_cache_bytes.argtypes = [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_decode_kv_read_bytes.restype = st
+    lib.mla_decode_kv_read_bytes.argtypes = [D, ctypes.c_int32, P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_absorb_q.restype = st
+    lib.mla_absorb_q.argtypes = [D, P, P, P, P]
+    lib.mla_decode_latent.restype = st
+    lib.mla_decode_latent.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                      P, P, P, P, P]
+    lib.mla_combine_splits.restype = st
+    lib.mla_combine_splits.argtypes = [D, P, P, ctypes.c_int32, P, P, P]
+    lib.mla_expand_v.restype = st
+    lib.mla_expand_v.argtypes = [D, P, P, P, P]
+    lib.mla_recommended_splits.restype = ctypes.c_int32
+    lib.mla_recommended_splits.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise MlaError(status, load().mla_last_error().decode())
+
+
+def dims(batch, num_heads, softmax_scale, kv_lora_rank=512, qk_rope_head_dim=64, qk_nope_head_dim=128,
+         v_head_dim=128):
+    return MlaDims(batch, num_heads, kv_lora_rank, qk_rope_head_dim, qk_nope_head_dim, v_head_dim,
+                   softmax_scale)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _expect(t, name, dtype, shape, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def mla_version():
+    return load().mla_version().decode()
+
+
+def mla_last_error():
+    return load().mla_last_error().decode()
+
+
+def mla_kv_cache_bytes(d, dtype=MLA_DTYPE_BF16):
+    out = ctypes.c_size_t(0)
+    _check(load().mla_kv_cache_bytes(ctypes.byref(d), dtype, ctypes.byref(out)))
+    return out.value
+
+
+def mla_decode_kv_read_bytes(d, host_seq_lens, dtype=MLA_DTYPE_BF16):
+    lens = (ctypes.c_int32 * len(host_seq_lens))(*[int(x) for x in host_seq_lens])
+    out = ctypes.c_size_t(0)
+    _check(load().mla_decode_kv_read_bytes(ctypes.byref(d), dtype, ctypes.cast(lens, ctypes.c_void_p),
+                                           ctypes.byref(out)))
+    return out.value
+
+
+def mla_recommended_splits(d, max_seq_len, num_cus):
+    return int(load().mla_recommended_splits(ctypes.byref(d), int(max_seq_len), int(num_cus)))
+
+
+def mla_absorb_q(d, q_nope, w_uk, q_lat=None, stream=None):
+    """q_lat[b,h,:] = q_nope[b,h,:] . W_UK[h] (bf16 in, fp32 accumulate, bf16 out)."""
+    B, H = d.batch, d.num_heads
+    _expect(q_nope, "q_nope", torch.bfloat16, (B, H, d.qk_nope_head_dim))
+    _expect(w_uk, "w_uk", torch.bfloat16, (H, d.qk_nope_head_dim, d.kv_lora_rank), q_nope.device)
+    if q_lat is None:
+        q_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=q_nope.device)
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, d.kv_lora_rank), q_nope.device)
+    _check(load().mla_absorb_q(ctypes.byref(d), _ptr(q_nope), _ptr(w_uk), _ptr(q_lat), _stream(stream)))
+    return q_lat
+
+
+def make_cache(kv_rows, pe_rows, seq_stride=0, block_table=None, block_size=0, token_scale=None):
+    """Describe a latent cache given [num_slots, 512] / [num_slots, 64] row views."""
+    if kv_rows.dtype == torch.bfloat16:
+        dt = MLA_DTYPE_BF16
+    elif kv_rows.dtype == torch.uint8:
+        dt = MLA_DTYPE_FP8_E4M3
+    else:
+        raise TypeError(f"cache rows must be bfloat16 or uint8 (E4M3 codes), got {kv_rows.dtype}")
+    if pe_rows.dtype != kv_rows.dtype:
+        raise TypeError("kv and pe rows must share a dtype")
+    for name, t in (("kv_rows", kv_rows), ("pe_rows", pe_rows)):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be a 2-D view with unit element stride")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    mb = 0
+    if block_table is not None:
+        _expect(block_table, "block_table", torch.int32, None, kv_rows.device)
+        mb = block_table.shape[1]
+    if token_scale is not None:
+        _expect(token_scale, "token_scale", torch.float32, None, kv_rows.device)
+    c = MlaCache(dt, kv_rows.data_ptr(), pe_rows.data_ptr(), kv_rows.stride(0), pe_rows.stride(0),
+                 None if token_scale is None else token_scale.data_ptr(), int(seq_stride),
+                 None if block_table is None else block_table.data_ptr(), int(block_size), int(mb))
+    c._keep = (kv_rows, pe_rows, block_table, token_scale)
+    return c
+
+
+def mla_decode_latent(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_splits=1, o_part=None, lse_part=None,
+                      o_lat=None, lse=None, stream=None):
+    """Latent attention of one decode step.  num_splits == 1 returns (o_lat, lse);
+    num_splits > 1 returns the split partials (o_part, lse_part)."""
+    B, H = d.batch, d.num_heads
+    dev = q_lat.device
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, d.kv_lora_rank))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if num_splits == 1:
+        if o_lat is None:
+            o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+        _expect(lse, "lse", torch.float32, (B, H), dev)
+    else:
+        if o_part is None:
+            o_part = torch.empty((B, num_splits, H, d.kv_lora_rank), dtype=torch.float32, device=dev)
+        if lse_part is None:
+            lse_part = torch.empty((B, num_splits, H), dtype=torch.float32, device=dev)
+        _expect(o_part, "o_part", torch.float32, (B, num_splits, H, d.kv_lora_rank), dev)
+        _expect(lse_part, "lse_part", torch.float32, (B, num_splits, H), dev)
+    _check(load().mla_decode_latent(ctypes.byref(d), ctypes.byref(cache), _ptr(q_lat), _ptr(q_pe), _ptr(seq_lens),
+                                    int(max_seq_len), int(num_splits),
+                                    _ptr(o_part) if num_splits > 1 else None,
+                                    _ptr(lse_part) if num_splits > 1 else None,
+                                    _ptr(o_lat) if num_splits == 1 else None,
+                                    _ptr(lse) if num_splits == 1 else None, _stream(stream)))
+    return (o_lat, lse) if num_splits == 1 else (o_part, lse_part)
+
+
+def mla_combine_splits(d, o_part, lse_part, o_lat=None, lse=None, stream=None):
+    """Log-sum-exp merge of split partials -> (o_lat bf16, lse fp32)."""
+    B, H = d.batch, d.num_heads
+    P = o_part.shape[1]
+    dev = o_part.device
+    _expect(o_part, "o_part", torch.float32, (B, P, H, d.kv_lora_rank))
+    _expect(lse_part, "lse_part", torch.float32, (B, P, H), dev)
+    if o_lat is None:
+        o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_combine_splits(ctypes.byref(d), _ptr(o_part), _ptr(lse_part), int(P), _ptr(o_lat), _ptr(lse),
+                                     _stream(stream)))
+    return o_lat, lse
+
+
+def mla_expand_v(d, o_lat, w_uv, out=None, stream=None):
+    """out[b,h,:] = W_UV[h] . o_lat[b,h,:] (bf16 in, fp32 accumulate, bf16 out)."""
+    B, H = d.batch, d.num_heads
+    _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank))
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, d.v_head_dim, d.kv_lora_rank), o_lat.device)
+    if out is None:
+        out = torch.empty((B, H, d.v_head_dim), dtype=torch.bfloat16, device=o_lat.device)
+    _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), o_lat.device)
+    _check(load().mla_expand_v(ctypes.byref(d), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream)))
+    return out
+
+
+class DecodeStep:
+    """The four calls of one absorbed decode step with preallocated buffers
+    (so a timed or captured step allocates nothing)."""
+
+    def __init__(self, d, cache, seq_lens, max_seq_len, num_splits, device):
+        B, H = d.batch, d.num_heads
+        self.d, self.cache, self.seq_lens = d, cache, seq_lens
+        self.max_seq_len, self.num_splits = int(max_seq_len), int(num_splits)
+        bf, f32 = torch.bfloat16, torch.float32
+        self.q_lat = torch.empty((B, H, d.kv_lora_rank), dtype=bf, device=device)
+        self.o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=bf, device=device)
+        self.lse = torch.empty((B, H), dtype=f32, device=device)
+        self.out = torch.empty((B, H, d.v_head_dim), dtype=bf, device=device)
+        if self.num_splits > 1:
+            self.o_part = torch.empty((B, self.num_splits, H, d.kv_lora_rank), dtype=f32, device=device)
+            self.lse_part = torch.empty((B, self.num_splits, H), dtype=f32, device=device)
+        else:
+            self.o_part = self.lse_part = None
+
+    def attend(self, q_pe, stream=None):
+        """Latent attention (+ combine) given self.q_lat."""
+        if self.num_splits > 1:
+            mla_decode_latent(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len,
+                              self.num_splits, o_part=self.o_part, lse_part=self.lse_part, stream=stream)
+            mla_combine_splits(self.d, self.o_part, self.lse_part, o_lat=self.o_lat, lse=self.lse, stream=stream)
+        else:
+            mla_decode_latent(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len, 1,
+                              o_lat=self.o_lat, lse=self.lse, stream=stream)
+
+    def __call__(self, q_nope, q_pe, w_uk, w_uv, stream=None):
+        mla_absorb_q(self.d, q_nope, w_uk, q_lat=self.q_lat, stream=stream)
+        self.attend(q_pe, stream=stream)
+        mla_expand_v(self.d, self.o_lat, w_uv, out=self.out, stream=stream)
+        return self.out

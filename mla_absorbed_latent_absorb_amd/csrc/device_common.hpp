@@ -1,0 +1,105 @@
+// Device-side building blocks shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kDc = 512;            // kv_lora_rank
+constexpr int kDr = 64;             // qk_rope_head_dim
+constexpr int kDk = kDc + kDr;      // 576: width of one cached token
+constexpr int kDn = 128;            // qk_nope_head_dim
+constexpr int kDv = 128;            // v_head_dim
+
+// 16x16x32 bf16 MFMA: D[16x16] += A[16x32] * B[32x16] in fp32.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) + j][l%16] for j = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS read at a byte offset into the LDS window.
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+      (uintptr_t)byte_off);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// if lane i points at row i/4, columns 4*(i%4) .. +3 of a 4 x 16 block of
+// 16-bit elements, lane j receives column j of the four rows.
+__device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t byte_off) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)byte_off);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4, scalar
+// base + 32-bit per-lane offset).  Lane i reads sbase + voff and writes bytes
+// [lds_base + 16*i, +16).  lds_base and sbase must be wave-uniform.  It is
+// issued through inline asm so the compiler does not add a conservative
+// vmcnt(0) before every later LDS read; completion is tracked explicitly with
+// wait_vmcnt() followed by a workgroup barrier.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+// Make a pointer that is uniform in value also uniform in register class.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+// XOR swizzles of the 16-byte chunk index inside the rows of an LDS cache
+// tile, as functions of the row.  gfx950's LDS has 64 four-byte banks, i.e.
+// 16 sixteen-byte bank slots.
+//
+// Latent rows are 1024 bytes (every row starts in bank 0).  kv_swizzle keeps
+// both read patterns of the decode kernel conflict-free:
+//   - 16 consecutive rows, one chunk each (K fragment of the score MFMA):
+//     the XOR value is a bijection of row % 16;
+//   - 8 consecutive rows x 2 adjacent chunks {2m, 2m+1} (two transposing reads
+//     of the V fragment of the P.V MFMA): the XOR value / 2 differs for the 8
+//     rows, so the 16 chunk reads land in 16 different slots.
+__device__ __forceinline__ uint32_t kv_swizzle(uint32_t row) {
+  return ((row & 7u) << 1) | ((row >> 3) & 1u);
+}
+// RoPE rows are 128 bytes (8 chunks; odd rows start half a bank sweep after
+// even rows): the XOR value is a bijection of (row / 2) % 8.
+__device__ __forceinline__ uint32_t pe_swizzle(uint32_t row) { return (row >> 1) & 7u; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace mla

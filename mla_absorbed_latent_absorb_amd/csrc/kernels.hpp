@@ -1,0 +1,57 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeArgs {
+  const uint16_t* q_lat;      // [B, H, 512] bf16
+  const uint16_t* q_pe;       // [B, H, 64] bf16
+  const char* kv;             // latent element 0 of slot 0
+  const char* pe;             // rope element 0 of slot 0
+  int64_t kv_sb;              // bytes between consecutive slots (kv)
+  int64_t pe_sb;              // bytes between consecutive slots (pe)
+  int64_t seq_stride;         // contiguous: slots per sequence
+  const int32_t* block_table; // paged: [B, max_blocks]; null = contiguous
+  int32_t block_size;
+  int32_t max_blocks;
+  const int32_t* seq_lens;    // [B]
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_splits;
+  int32_t chunk;              // tokens per split, multiple of 32
+  int32_t max_seq_len;
+  float scale;                // softmax scale
+  float scale_log2;           // softmax scale * log2(e)
+  float* o_part;              // [B, P, H, 512] fp32 (P > 1)
+  float* lse_part;            // [B, P, H] fp32 (P > 1)
+  uint16_t* o_lat;            // [B, H, 512] bf16 (P == 1)
+  float* lse;                 // [B, H] fp32 (P == 1)
+};
+
+struct ProjArgs {
+  const uint16_t* x;     // absorb: q_nope [B, H, 128]; expand: o_lat [B, H, 512]
+  const uint16_t* w;     // absorb: W_UK [H, 128, 512]; expand: W_UV [H, 128, 512]
+  uint16_t* y;           // absorb: q_lat [B, H, 512]; expand: out [B, H, 128]
+  int32_t batch;
+  int32_t num_heads;
+};
+
+struct CombineArgs {
+  const float* o_part;   // [B, P, H, 512]
+  const float* lse_part; // [B, P, H]
+  uint16_t* o_lat;       // [B, H, 512]
+  float* lse;            // [B, H] or null
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_splits;
+};
+
+hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);
+hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,258 @@
+// Host side of the C ABI declared in include/mla_absorb.h: argument checks,
+// split planning and kernel launches on the caller's stream.  Nothing here
+// allocates, frees or synchronises.
+#include "../../include/mla_absorb.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status ok() {
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p, name, where)                                                              \
+  do {                                                                                           \
+    if ((p) == nullptr) return fail(MLA_ERR_NULL, "%s is NULL (%s)", name, where);               \
+    if (!aligned16(p)) return fail(MLA_ERR_ALIGN, "%s is not 16-byte aligned (%s)", name, where); \
+  } while (0)
+
+// Required-dimension checks: zero means missing, and nothing is defaulted.
+mla_status check_latent_dims(const mla_dims* d, const char* where) {
+  if (d == nullptr) return fail(MLA_ERR_NULL, "dims is NULL (%s)", where);
+  if (d->kv_lora_rank <= 0) return fail(MLA_ERR_MISSING_DIM, "kv_lora_rank missing (mla_dims, %s)", where);
+  if (d->qk_rope_head_dim <= 0)
+    return fail(MLA_ERR_MISSING_DIM, "qk_rope_head_dim missing (mla_dims, %s)", where);
+  return MLA_OK;
+}
+
+mla_status check_dims(const mla_dims* d, const char* where) {
+  mla_status st = check_latent_dims(d, where);
+  if (st != MLA_OK) return st;
+  if (d->batch <= 0) return fail(MLA_ERR_MISSING_DIM, "batch missing (mla_dims, %s)", where);
+  if (d->num_heads <= 0) return fail(MLA_ERR_MISSING_DIM, "num_heads missing (mla_dims, %s)", where);
+  if (d->qk_nope_head_dim <= 0)
+    return fail(MLA_ERR_MISSING_DIM, "qk_nope_head_dim missing (mla_dims, %s)", where);
+  if (d->v_head_dim <= 0) return fail(MLA_ERR_MISSING_DIM, "v_head_dim missing (mla_dims, %s)", where);
+  if (d->softmax_scale == 0.0f) return fail(MLA_ERR_MISSING_DIM, "softmax_scale missing (mla_dims, %s)", where);
+  if (!(d->softmax_scale > 0.0f) || !std::isfinite(d->softmax_scale))
+    return fail(MLA_ERR_UNSUPPORTED, "softmax_scale must be positive and finite (mla_dims, %s)", where);
+  if (d->kv_lora_rank != 512)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_lora_rank %d not supported, built for 512 (%s)", d->kv_lora_rank, where);
+  if (d->qk_rope_head_dim != 64)
+    return fail(MLA_ERR_UNSUPPORTED, "qk_rope_head_dim %d not supported, built for 64 (%s)", d->qk_rope_head_dim,
+                where);
+  if (d->qk_nope_head_dim != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "qk_nope_head_dim %d not supported, built for 128 (%s)", d->qk_nope_head_dim,
+                where);
+  if (d->v_head_dim != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "v_head_dim %d not supported, built for 128 (%s)", d->v_head_dim, where);
+  const int H = d->num_heads;
+  if (H != 16 && H != 32 && H != 64 && H != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "num_heads %d not supported (16, 32, 64 or 128) (%s)", H, where);
+  return MLA_OK;
+}
+
+size_t bytes_per_token(const mla_dims* d, int32_t dtype) {
+  const size_t e = dtype == MLA_DTYPE_FP8_E4M3 ? 1 : 2;
+  return (size_t)(d->kv_lora_rank + d->qk_rope_head_dim) * e + (dtype == MLA_DTYPE_FP8_E4M3 ? 4 : 0);
+}
+
+mla_status launch_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int32_t split_chunk(int32_t max_seq_len, int32_t num_splits) {
+  const int64_t per = ((int64_t)max_seq_len + num_splits - 1) / num_splits;
+  return (int32_t)(((per + 31) / 32) * 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_err; }
+
+const char* mla_version(void) { return "mla_absorb gfx950 0.1"; }
+
+mla_status mla_kv_cache_bytes(const mla_dims* dims, int32_t dtype, size_t* bytes) {
+  mla_status st = check_latent_dims(dims, "mla_kv_cache_bytes");
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr) return fail(MLA_ERR_NULL, "bytes_per_token is NULL (mla_kv_cache_bytes)");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d unknown (mla_kv_cache_bytes)", dtype);
+  *bytes = bytes_per_token(dims, dtype);
+  return ok();
+}
+
+mla_status mla_decode_kv_read_bytes(const mla_dims* dims, int32_t dtype, const int32_t* host_seq_lens,
+                                    size_t* bytes) {
+  mla_status st = check_latent_dims(dims, "mla_decode_kv_read_bytes");
+  if (st != MLA_OK) return st;
+  if (dims->batch <= 0) return fail(MLA_ERR_MISSING_DIM, "batch missing (mla_dims, mla_decode_kv_read_bytes)");
+  if (host_seq_lens == nullptr) return fail(MLA_ERR_NULL, "host_seq_lens is NULL (mla_decode_kv_read_bytes)");
+  if (bytes == nullptr) return fail(MLA_ERR_NULL, "bytes is NULL (mla_decode_kv_read_bytes)");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "dtype %d unknown (mla_decode_kv_read_bytes)", dtype);
+  size_t tokens = 0;
+  for (int32_t b = 0; b < dims->batch; ++b) {
+    if (host_seq_lens[b] < 0)
+      return fail(MLA_ERR_BAD_LENGTH, "host_seq_lens[%d] = %d is negative (mla_decode_kv_read_bytes)", b,
+                  host_seq_lens[b]);
+    tokens += (size_t)host_seq_lens[b];
+  }
+  *bytes = tokens * bytes_per_token(dims, dtype);
+  return ok();
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* w_uk, void* q_lat, void* stream) {
+  const char* where = "mla_absorb_q";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  REQUIRE_PTR(q_nope, "q_nope", where);
+  REQUIRE_PTR(w_uk, "w_uk", where);
+  REQUIRE_PTR(q_lat, "q_lat", where);
+  mla::ProjArgs a{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(w_uk),
+                  static_cast<uint16_t*>(q_lat), dims->batch, dims->num_heads};
+  return launch_result(mla::launch_absorb_q(a, static_cast<hipStream_t>(stream)), where);
+}
+
+mla_status mla_expand_v(const mla_dims* dims, const void* o_lat, const void* w_uv, void* out, void* stream) {
+  const char* where = "mla_expand_v";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  REQUIRE_PTR(o_lat, "o_lat", where);
+  REQUIRE_PTR(w_uv, "w_uv", where);
+  REQUIRE_PTR(out, "out", where);
+  mla::ProjArgs a{static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(w_uv),
+                  static_cast<uint16_t*>(out), dims->batch, dims->num_heads};
+  return launch_result(mla::launch_expand_v(a, static_cast<hipStream_t>(stream)), where);
+}
+
+mla_status mla_combine_splits(const mla_dims* dims, const float* o_part, const float* lse_part, int32_t num_splits,
+                              void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_combine_splits";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
+  REQUIRE_PTR(o_part, "o_part", where);
+  if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+  REQUIRE_PTR(o_lat, "o_lat", where);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  mla::CombineArgs a{o_part, lse_part, static_cast<uint16_t*>(o_lat), lse, dims->batch, dims->num_heads,
+                     num_splits};
+  return launch_result(mla::launch_combine(a, static_cast<hipStream_t>(stream)), where);
+}
+
+mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_part,
+                             float* lse_part, void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_decode_latent";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
+  if (cache->dtype == MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "fp8 cache not built yet (mla_cache.dtype, %s)", where);
+  if (cache->dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  REQUIRE_PTR(cache->kv, "mla_cache.kv", where);
+  REQUIRE_PTR(cache->pe, "mla_cache.pe", where);
+  REQUIRE_PTR(q_lat, "q_lat", where);
+  REQUIRE_PTR(q_pe, "q_pe", where);
+  if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
+  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % 8 != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of 8 elements (%s)",
+                (long long)cache->kv_stride, dims->kv_lora_rank, where);
+  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % 8 != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of 8 elements (%s)",
+                (long long)cache->pe_stride, dims->qk_rope_head_dim, where);
+  if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
+  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
+  if ((int64_t)dims->batch * num_splits > (int64_t)1 << 30)
+    return fail(MLA_ERR_BAD_LENGTH, "batch * num_splits too large (%s)", where);
+  if (cache->block_table != nullptr) {
+    if (cache->block_size <= 0 || cache->block_size % 32 != 0)
+      return fail(MLA_ERR_BAD_LENGTH, "mla_cache.block_size %d must be a positive multiple of 32 (%s)",
+                  cache->block_size, where);
+    const int64_t need = ((int64_t)max_seq_len + cache->block_size - 1) / cache->block_size;
+    if (cache->max_blocks_per_seq < need)
+      return fail(MLA_ERR_BUFFER, "mla_cache.max_blocks_per_seq %d < %lld blocks for max_seq_len %d (%s)",
+                  cache->max_blocks_per_seq, (long long)need, max_seq_len, where);
+  } else {
+    if (cache->seq_stride < max_seq_len)
+      return fail(MLA_ERR_BUFFER, "mla_cache.seq_stride %lld < max_seq_len %d (contiguous cache, %s)",
+                  (long long)cache->seq_stride, max_seq_len, where);
+  }
+  if (num_splits == 1) {
+    REQUIRE_PTR(o_lat, "o_lat", where);
+    if (lse == nullptr) return fail(MLA_ERR_NULL, "lse is NULL (%s)", where);
+    if (o_part != nullptr || lse_part != nullptr)
+      return fail(MLA_ERR_BUFFER, "o_part/lse_part must be NULL when num_splits == 1 (%s)", where);
+  } else {
+    REQUIRE_PTR(o_part, "o_part", where);
+    if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+    if (o_lat != nullptr || lse != nullptr)
+      return fail(MLA_ERR_BUFFER, "o_lat/lse must be NULL when num_splits > 1; merge with mla_combine_splits (%s)",
+                  where);
+  }
+
+  mla::DecodeArgs a{};
+  a.q_lat = static_cast<const uint16_t*>(q_lat);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.kv = static_cast<const char*>(cache->kv);
+  a.pe = static_cast<const char*>(cache->pe);
+  a.kv_sb = cache->kv_stride * 2;
+  a.pe_sb = cache->pe_stride * 2;
+  a.seq_stride = cache->seq_stride;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.batch = dims->batch;
+  a.num_heads = dims->num_heads;
+  a.num_splits = num_splits;
+  a.chunk = split_chunk(max_seq_len, num_splits);
+  a.max_seq_len = max_seq_len;
+  a.scale = dims->softmax_scale;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.o_lat = static_cast<uint16_t*>(o_lat);
+  a.lse = lse;
+  return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
+}
+
+int32_t mla_recommended_splits(const mla_dims* dims, int32_t max_seq_len, int32_t num_cus) {
+  if (dims == nullptr || dims->batch <= 0 || dims->num_heads <= 0 || max_seq_len <= 0 || num_cus <= 0) return 1;
+  // workgroups resident per CU: 8 waves of 16 heads at most
+  const int wg_per_cu = dims->num_heads >= 128 ? 1 : (dims->num_heads >= 64 ? 2 : 4);
+  const int64_t want = (int64_t)num_cus * wg_per_cu;
+  int64_t p = (want + dims->batch - 1) / dims->batch;
+  const int64_t max_p = (max_seq_len + 255) / 256;
+  if (p > max_p) p = max_p;
+  if (p < 1) p = 1;
+  return (int32_t)p;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/mla_absorb.h declares, and its host-side checks reject bad
+arguments (naming the field) before anything is launched.  No call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_absorbed_latent_absorb_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        pytest.fail("libmla_absorb.so is not built: run __graft_entry__.build()")
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_cache_byte_helpers_match_oracle(lib):
+    d = binding.dims(32, 128, 0.07)
+    assert binding.mla_kv_cache_bytes(d) == oracle.latent_cache_bytes_per_token(512, 64, 2) == 1152
+    assert binding.mla_kv_cache_bytes(d, binding.MLA_DTYPE_FP8_E4M3) == oracle.latent_cache_bytes_per_token(512, 64, 1) + 4
+    assert binding.mla_decode_kv_read_bytes(d, [4096] * 32) == oracle.decode_kv_read_bytes(32, 4096, 512, 64, 2)
+    d1 = binding.dims(1, 16, 0.07)
+    assert binding.mla_decode_kv_read_bytes(d1, [26]) == 29952  # 26-token V2-Lite active cache
+    lens = np.random.default_rng(0).integers(1024, 16385, 128)
+    d4 = binding.dims(128, 128, 0.07)
+    assert binding.mla_decode_kv_read_bytes(d4, lens) == int(lens.sum()) * 1152
+
+
+@pytest.mark.parametrize("field", ["kv_lora_rank", "qk_rope_head_dim"])
+def test_missing_required_dim_names_the_field(lib, field):
+    kw = {field: 0}
+    d = binding.dims(4, 16, 0.07, **kw)
+    with pytest.raises(binding.MlaError) as e:
+        binding.mla_kv_cache_bytes(d)
+    assert e.value.status == 2 and field in e.value.message
+
+
+def _call_absorb(lib, d, a=16, b=16, c=16):
+    return lib.mla_absorb_q(ctypes.byref(d), ctypes.c_void_p(a), ctypes.c_void_p(b), ctypes.c_void_p(c), None)
+
+
+def test_validation_rejects_before_launch(lib):
+    good = binding.dims(4, 16, 0.07)
+    cases = [
+        (binding.dims(0, 16, 0.07), 2, "batch"),
+        (binding.dims(4, 0, 0.07), 2, "num_heads"),
+        (binding.dims(4, 16, 0.0), 2, "softmax_scale"),
+        (binding.dims(4, 16, -1.0), 3, "softmax_scale"),
+        (binding.dims(4, 16, 0.07, kv_lora_rank=256), 3, "kv_lora_rank"),
+        (binding.dims(4, 16, 0.07, qk_rope_head_dim=32), 3, "qk_rope_head_dim"),
+        (binding.dims(4, 24, 0.07), 3, "num_heads"),
+        (binding.dims(4, 16, 0.07, v_head_dim=0), 2, "v_head_dim"),
+    ]
+    for d, status, word in cases:
+        st = _call_absorb(lib, d)
+        assert st == status, (word, st)
+        assert word in lib.mla_last_error().decode()
+    assert _call_absorb(lib, good, a=0) == 1 and "q_nope" in lib.mla_last_error().decode()
+    assert _call_absorb(lib, good, b=8) == 6 and "w_uk" in lib.mla_last_error().decode()
+
+
+def _decode(lib, d, cache, max_len=64, splits=1, o_part=0, lse_part=0, o_lat=64, lse=64, q=16, qpe=16, lens=16):
+    P = ctypes.c_void_p
+    return lib.mla_decode_latent(ctypes.byref(d), ctypes.byref(cache) if cache is not None else None, P(q), P(qpe),
+                                 P(lens), max_len, splits, P(o_part) if o_part else None,
+                                 P(lse_part) if lse_part else None, P(o_lat) if o_lat else None,
+                                 P(lse) if lse else None, None)
+
+
+def test_decode_latent_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    base = dict(dtype=0, kv=1024, pe=2048, kv_stride=576, pe_stride=576, token_scale=None, seq_stride=64,
+                block_table=None, block_size=0, max_blocks_per_seq=0)
+
+    def cache(**kw):
+        c = dict(base)
+        c.update(kw)
+        return binding.MlaCache(**c)
+
+    assert _decode(lib, d, None) == 1
+    assert _decode(lib, d, cache(dtype=1)) == 3 and "fp8" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(kv=None)) == 1
+    assert _decode(lib, d, cache(kv=1032)) == 6
+    assert _decode(lib, d, cache(kv_stride=500)) == 5 and "kv_stride" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(pe_stride=60)) == 5
+    assert _decode(lib, d, cache(seq_stride=32), max_len=64) == 5 and "seq_stride" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(), max_len=0) == 4
+    assert _decode(lib, d, cache(), splits=0) == 4
+    assert _decode(lib, d, cache(block_table=4096, block_size=48, max_blocks_per_seq=4)) == 4
+    assert _decode(lib, d, cache(block_table=4096, block_size=64, max_blocks_per_seq=0)) == 5
+    # split outputs must match num_splits
+    assert _decode(lib, d, cache(), splits=2) == 1 and "o_part" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(), splits=2, o_part=4096, lse_part=4096) == 5  # o_lat given with P > 1
+    assert _decode(lib, d, cache(), splits=1, o_part=4096) == 5
+    assert _decode(lib, d, cache(), lens=0) == 1 and "seq_lens" in lib.mla_last_error().decode()
+
+
+def test_combine_and_expand_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    P = ctypes.c_void_p
+    assert lib.mla_combine_splits(ctypes.byref(d), P(16), P(16), 0, P(16), P(16), None) == 4
+    assert lib.mla_combine_splits(ctypes.byref(d), None, P(16), 2, P(16), P(16), None) == 1
+    assert lib.mla_expand_v(ctypes.byref(d), P(16), None, P(16), None) == 1
+    assert "w_uv" in lib.mla_last_error().decode()
+
+
+def test_recommended_splits(lib):
+    assert binding.mla_recommended_splits(binding.dims(32, 128, 0.07), 4096, 256) == 8
+    assert binding.mla_recommended_splits(binding.dims(64, 16, 0.07), 4096, 256) == 16
+    assert binding.mla_recommended_splits(binding.dims(1, 16, 0.07), 26, 256) == 1

@@ -1,0 +1,305 @@
+"""Parity of the HIP library (through its C ABI) with the float64 oracle.
+
+Every case draws seeded inputs with the generator module, runs the GPU path,
+and compares element by element with the oracle on the same stored bytes:
+max |gpu - oracle| / max |oracle| <= 2e-2 for bf16 outputs (fp32
+accumulation), lse within 2e-2 absolute.  Full-size workloads are checked on
+a spread of sampled sequences (all heads, all 512 latent columns each).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_absorbed_latent_absorb_amd import binding, datagen
+from tests.gpu_helpers import TOL_BF16, bits16, cache_args, f64, rel_err, sample_batch, split_bounds
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _inputs(workload, **kw):
+    return datagen.make_inputs(workload, device=DEV, **kw)
+
+
+# ---------------------------------------------------------------------------
+# mla_absorb_q / mla_expand_v
+# ---------------------------------------------------------------------------
+
+PROJ_CASES = [(1, 16), (5, 16), (64, 16), (3, 32), (17, 64), (32, 128), (128, 128)]
+
+
+@pytest.mark.parametrize("B,H", PROJ_CASES)
+def test_absorb_q(B, H):
+    announce(f"absorb_q B={B} H={H}")
+    x = _inputs("v3_b32_s4096", batch=B, seq_len=32, heads=H)
+    d = binding.dims(B, H, x.scale)
+    q_lat = binding.mla_absorb_q(d, x.q_nope, x.w_uk)
+    torch.cuda.synchronize()
+    ref = oracle.absorb_q(f64(x.q_nope), f64(x.w_uk))
+    err = rel_err(f64(q_lat), ref)
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("B,H", PROJ_CASES)
+def test_expand_v(B, H):
+    announce(f"expand_v B={B} H={H}")
+    x = _inputs("v3_b32_s4096", batch=B, seq_len=32, heads=H)
+    o_lat = datagen.random_latent_queries(B, H, seed=77 + B, device=DEV)
+    d = binding.dims(B, H, x.scale)
+    out = binding.mla_expand_v(d, o_lat, x.w_uv)
+    torch.cuda.synchronize()
+    ref = oracle.expand_v(f64(o_lat), f64(x.w_uv))
+    err = rel_err(f64(out), ref)
+    assert err <= TOL_BF16, err
+
+
+# ---------------------------------------------------------------------------
+# mla_decode_latent, one split
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # (workload for layout, H, B, T)  T covers one row, ragged tails, exact tiles, many tiles
+    ("v2lite_b1_s26", 16, 1, 26),
+    ("v2lite_b1_s26", 16, 2, 1),
+    ("v3_b32_s4096", 16, 3, 31),
+    ("v3_b32_s4096", 32, 2, 32),
+    ("v3_b32_s4096", 64, 2, 33),
+    ("v3_b32_s4096", 128, 2, 100),
+    ("v3_b32_s4096", 128, 3, 257),
+    ("v3_b32_s4096", 128, 1, 1000),
+    ("v3_b32_s4096", 64, 3, 777),
+    ("v3_b128_paged", 128, 3, 300),
+    ("v3_b128_paged", 16, 4, 200),
+]
+
+
+def _latent_case(workload, H, B, T, seed):
+    x = _inputs(workload, batch=B, seq_len=T, heads=H)
+    q_lat = datagen.random_latent_queries(B, H, seed=seed, device=DEV)
+    return x, q_lat
+
+
+@pytest.mark.parametrize("workload,H,B,T", DECODE_CASES)
+def test_decode_latent_single_split(workload, H, B, T):
+    announce(f"decode_latent P=1 {workload} H={H} B={B} T={T}")
+    x, q_lat = _latent_case(workload, H, B, T, seed=1000 + T)
+    d = binding.dims(B, H, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
+                               block_size=x.block_size)
+    o_lat, lse = binding.mla_decode_latent(d, cache, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, 1)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=x.seq_lens.cpu().numpy(),
+                                        scale=x.scale, **cache_args(x))
+    err = rel_err(f64(o_lat), ref_o)
+    lerr = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
+    assert err <= TOL_BF16 and lerr <= TOL_BF16, (err, lerr)
+
+
+# ---------------------------------------------------------------------------
+# split-KV partials and their merge
+# ---------------------------------------------------------------------------
+
+SPLIT_CASES = [
+    ("v3_b32_s4096", 128, 2, 1000, 3),
+    ("v3_b32_s4096", 128, 2, 257, 8),    # later splits empty for short sequences? (all equal lengths here)
+    ("v3_b128_paged", 128, 5, 2000, 8),  # varied lengths: some splits empty
+    ("v3_b32_s4096", 16, 3, 4096, 16),
+    ("v3_b32_s4096", 64, 2, 95, 2),
+]
+
+
+@pytest.mark.parametrize("workload,H,B,T,P", SPLIT_CASES)
+def test_decode_latent_splits_and_combine(workload, H, B, T, P):
+    announce(f"decode_latent P={P} + combine {workload} H={H} B={B} T={T}")
+    x, q_lat = _latent_case(workload, H, B, T, seed=2000 + P)
+    d = binding.dims(B, H, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
+                               block_size=x.block_size)
+    o_part, lse_part = binding.mla_decode_latent(d, cache, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, P)
+    o_lat, lse = binding.mla_combine_splits(d, o_part, lse_part)
+    torch.cuda.synchronize()
+    args = cache_args(x)
+    lens = x.seq_lens.cpu().numpy()
+    q64, qpe64 = f64(q_lat), f64(x.q_pe)
+    o_part_h, lse_part_h = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    for b in range(B):
+        slots = oracle.token_slots(b, int(lens[b]), args["seq_stride"], args["block_table"], args["block_size"])
+        c, k_r = oracle.load_rows(args["kv_codes"], args["pe_codes"], slots, args["dtype"], args["token_scale"])
+        bounds = split_bounds(int(lens[b]), x.max_seq_len, P)
+        ro, rl = oracle.latent_attention_ranges(q64[b], qpe64[b], c, k_r, x.scale, bounds)
+        for i in range(P):
+            if np.isneginf(rl[i]).all():
+                assert np.isneginf(lse_part_h[b, i]).all() and np.all(o_part_h[b, i] == 0), (b, i)
+            else:
+                assert rel_err(o_part_h[b, i], ro[i]) <= TOL_BF16, (b, i)
+                assert np.max(np.abs(lse_part_h[b, i] - rl[i])) <= TOL_BF16, (b, i)
+    ref_o, ref_l = oracle.latent_decode(q64, qpe64, seq_lens=lens, scale=x.scale, **args)
+    assert rel_err(f64(o_lat), ref_o) <= TOL_BF16
+    assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B,P,H", [(2, 3, 16), (4, 8, 128), (1, 1, 64), (3, 16, 32)])
+def test_combine_random_partials(B, P, H):
+    announce(f"combine random partials B={B} P={P} H={H}")
+    o_part, lse_part = datagen.random_partials(B, P, H, seed=31 + P, device=DEV)
+    d = binding.dims(B, H, 0.07)
+    o_lat, lse = binding.mla_combine_splits(d, o_part, lse_part)
+    torch.cuda.synchronize()
+    op, lp = o_part.cpu().double().numpy(), lse_part.cpu().double().numpy()
+    for b in range(B):
+        ro, rl = oracle.combine_splits(op[b], lp[b])
+        assert rel_err(f64(o_lat[b]), ro) <= TOL_BF16
+        assert np.max(np.abs(lse[b].cpu().numpy() - rl)) <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# properties that hold at any size
+# ---------------------------------------------------------------------------
+
+def test_paged_matches_contiguous_bitwise():
+    """The same token rows behind a permuted block table give bit-identical
+    outputs (the kernel reads the same values in the same order)."""
+    announce("paged == contiguous bitwise, H=128 B=3 T=700")
+    B, H, T = 3, 128, 700
+    x = _inputs("v3_b32_s4096", batch=B, seq_len=T, heads=H)
+    q_lat = datagen.random_latent_queries(B, H, seed=5, device=DEV)
+    d = binding.dims(B, H, x.scale)
+    contig = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+    bs = 64
+    nblk = -(-T // bs)
+    g = torch.Generator(device="cpu").manual_seed(9)
+    perm = torch.randperm(B * nblk, generator=g)
+    pool = torch.zeros((B * nblk * bs, 576), dtype=torch.bfloat16, device=DEV)
+    table = torch.empty((B, nblk), dtype=torch.int32)
+    rows = x.storage.view(B, T, 576)
+    for b in range(B):
+        for j in range(nblk):
+            blk = int(perm[b * nblk + j])
+            table[b, j] = blk
+            n = min(bs, T - j * bs)
+            pool[blk * bs: blk * bs + n] = rows[b, j * bs: j * bs + n]
+    table = table.to(DEV)
+    paged = binding.make_cache(pool[:, :512], pool[:, 512:], block_table=table, block_size=bs)
+    for P in (1, 4):
+        a = binding.mla_decode_latent(d, contig, q_lat, x.q_pe, x.seq_lens, T, P)
+        c = binding.mla_decode_latent(d, paged, q_lat, x.q_pe, x.seq_lens, T, P)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1]), P
+
+
+def test_single_token_returns_that_row():
+    """With one cached token the softmax weight is exactly 1, so o_lat is that
+    token's latent row, bit for bit."""
+    announce("T=1 -> o_lat == c_0")
+    B, H = 4, 128
+    x = _inputs("v3_b32_s4096", batch=B, seq_len=1, heads=H)
+    q_lat = datagen.random_latent_queries(B, H, seed=6, device=DEV)
+    d = binding.dims(B, H, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+    o_lat, lse = binding.mla_decode_latent(d, cache, q_lat, x.q_pe, x.seq_lens, 1, 1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        row = x.kv_rows[b * x.seq_stride]
+        assert torch.equal(o_lat[b], row.unsqueeze(0).expand(H, 512)), b
+
+
+def test_zero_query_averages_rows():
+    """q = 0 gives a uniform softmax: o_lat is the mean latent row and
+    lse = ln T."""
+    announce("q=0 -> mean row, lse = ln T")
+    B, H, T = 2, 64, 500
+    x = _inputs("v3_b32_s4096", batch=B, seq_len=T, heads=H)
+    zq = torch.zeros((B, H, 512), dtype=torch.bfloat16, device=DEV)
+    zpe = torch.zeros((B, H, 64), dtype=torch.bfloat16, device=DEV)
+    d = binding.dims(B, H, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+    o_lat, lse = binding.mla_decode_latent(d, cache, zq, zpe, x.seq_lens, T, 1)
+    torch.cuda.synchronize()
+    c = f64(x.kv_rows).reshape(B, x.seq_stride, 512)[:, :T]
+    mean = c.mean(axis=1)
+    for b in range(B):
+        assert rel_err(f64(o_lat[b]), np.repeat(mean[b][None], H, 0)) <= TOL_BF16
+    assert np.max(np.abs(lse.cpu().numpy() - math.log(T))) <= 1e-5
+
+
+def test_deterministic_rerun():
+    """Two runs of the full step give byte-identical outputs."""
+    announce("determinism v3 B=32 S=4096")
+    x = _inputs("v3_b32_s4096")
+    d = binding.dims(x.batch, x.heads, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+    P = binding.mla_recommended_splits(d, x.max_seq_len, torch.cuda.get_device_properties(DEV).multi_processor_count)
+    step = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, DEV)
+    a = step(x.q_nope, x.q_pe, x.w_uk, x.w_uv).clone()
+    la = step.lse.clone()
+    b = step(x.q_nope, x.q_pe, x.w_uk, x.w_uv).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, step.lse)
+
+
+# ---------------------------------------------------------------------------
+# the full 4-call step on the workloads, at full size, in the bench launch
+# configuration (recommended number of splits)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("workload", ["v2lite_b1_s26", "v2lite_b64_s4096", "v3_b32_s4096", "v3_b128_paged"])
+def test_full_step_against_oracle(workload):
+    announce(f"full step {workload}")
+    x = _inputs(workload)
+    d = binding.dims(x.batch, x.heads, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
+                               block_size=x.block_size)
+    ncu = torch.cuda.get_device_properties(DEV).multi_processor_count
+    P = binding.mla_recommended_splits(d, x.max_seq_len, ncu)
+    step = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, DEV)
+    out = step(x.q_nope, x.q_pe, x.w_uk, x.w_uv)
+    torch.cuda.synchronize()
+    idx = sample_batch(x.batch)
+    ref = oracle.absorbed_decode(f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv),
+                                 seq_lens=x.seq_lens.cpu().numpy(), scale=x.scale, batch_indices=idx,
+                                 **cache_args(x))
+    got_out = f64(out)[idx]
+    e_out = rel_err(got_out, ref["out"])
+    e_lat = rel_err(f64(step.o_lat)[idx], ref["o_lat"])
+    e_q = rel_err(f64(step.q_lat)[idx], ref["q_lat"])
+    e_lse = float(np.max(np.abs(step.lse.cpu().numpy()[idx] - ref["lse"])))
+    print(f"  {workload} P={P} sampled {idx}: out {e_out:.2e} o_lat {e_lat:.2e} q_lat {e_q:.2e} lse {e_lse:.2e}")
+    assert np.isfinite(got_out).all()
+    assert max(e_out, e_lat, e_q, e_lse) <= TOL_BF16
+
+
+def test_v2lite_s26_against_naive_oracle():
+    """The 26-token V2-Lite-shaped step also matches the expanded (naive)
+    form of the oracle."""
+    announce("v2lite_b1_s26 vs naive oracle")
+    x = _inputs("v2lite_b1_s26")
+    d = binding.dims(x.batch, x.heads, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+    step = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, 1, DEV)
+    out = step(x.q_nope, x.q_pe, x.w_uk, x.w_uv)
+    torch.cuda.synchronize()
+    ref = oracle.naive_decode(f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv),
+                              seq_lens=x.seq_lens.cpu().numpy(), scale=x.scale, **cache_args(x))
+    assert rel_err(f64(out), ref) <= TOL_BF16
+
+
+def test_fp8_cache_not_built_yet_is_refused():
+    """The E4M3 cache path is declared but not built; the call must refuse
+    it cleanly rather than run."""
+    announce("fp8 refused")
+    x = _inputs("v3_b64_s32768_fp8", batch=2, seq_len=64, heads=128)
+    d = binding.dims(2, 128, x.scale)
+    cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, token_scale=x.token_scale)
+    q_lat = datagen.random_latent_queries(2, 128, seed=1, device=DEV)
+    with pytest.raises(binding.MlaError) as e:
+        binding.mla_decode_latent(d, cache, q_lat, torch.zeros((2, 128, 64), dtype=torch.bfloat16, device=DEV),
+                                  x.seq_lens, 64, 1)
+    assert e.value.status == 3
