@@ -1,0 +1,242 @@
+"""Benchmark of one absorbed-MLA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b32_s4096]
+
+A step is the whole decode path of one layer for one batch: mla_absorb_q,
+mla_decode_latent (split-KV), mla_combine_splits and mla_expand_v, on seeded
+synthetic inputs already resident in HBM.  Inputs are rotated over several
+replicas per step so the working set exceeds the 256 MB Infinity Cache and
+every step streams its latent cache from HBM.
+
+Prints one JSON line:
+  value           latent-KV GB/s over the whole step (cache bytes / step time)
+  roofline        the dominant kernel (mla_decode_latent): algorithmic cache
+                  bytes per launch / its mean duration from HIP events around
+                  each launch, against 8 TB/s
+  cpu_baseline    the float64 oracle on the host cores, on a bounded sample of
+                  the same workload, in the same unit
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), V3 H=128 B=32 S=4096"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_latent_v3_b32_s4096_hbm_counters.json")
+KERNEL_SOURCES = ["mla_absorbed_latent_absorb_amd/csrc/decode_latent.hip",
+                  "mla_absorbed_latent_absorb_amd/csrc/device_common.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def core_flops(B, H, lens_sum):
+    """Score (2*H*576) + latent P.V (2*H*512) multiply-adds per cached token."""
+    return 2 * H * (576 + 512) * lens_sum
+
+
+def proj_flops(B, H):
+    """absorb_q + expand_v: 2 * B * H * 128 * 512 each."""
+    return 2 * 2 * B * H * 128 * 512
+
+
+def traffic_from_counters(per_launch_algo_bytes):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when they are missing or the kernel source changed since."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, target_s=10.0):
+    """Time the float64 oracle (as it stands) on the host cores: absorbed
+    decode of the workload's sequences one at a time, cycling over the batch
+    until about target_s seconds of CPU work."""
+    import oracle
+    from tests.gpu_helpers import cache_args, f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - informational only
+        threads = os.cpu_count()
+    args = cache_args(x)
+    qn, qp, wuk, wuv = f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv)
+    lens = x.seq_lens.cpu().numpy()
+    per_tok = 1152 if x.workload.dtype == "bf16" else 580
+    n_seq, nbytes, t_total = 0, 0, 0.0
+    while t_total < target_s:
+        b = n_seq % x.batch
+        t0 = time.perf_counter()
+        oracle.absorbed_decode(qn, qp, wuk, wuv, seq_lens=lens, scale=x.scale, batch_indices=[b], **args)
+        t_total += time.perf_counter() - t0
+        n_seq += 1
+        nbytes += int(lens[b]) * per_tok
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} sequence decodes cycling over the {x.batch} sequences of {x.workload.name} "
+                      f"(absorbed form, float64 NumPy; {nbytes} cache bytes in {t_total:.2f} s; "
+                      f"{os.cpu_count()} host CPUs visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="v3_b32_s4096")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library recommendation")
+    ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough for > 512 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): this build has no "
+              "multi-GPU path; batch sharding across GPUs needs no exchange and is described in DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    binding.load()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = datagen.WORKLOADS[args.workload]
+    x0 = datagen.make_inputs(wl, device=dev)
+    cache_bytes = x0.cache_bytes()
+    R = args.replicas or max(2, math.ceil(512e6 / cache_bytes) + 1)
+    reps = [x0] + [datagen.make_inputs(wl, device=dev) for _ in range(R - 1)]
+    d = binding.dims(x0.batch, x0.heads, x0.scale)
+    P = args.splits or binding.mla_recommended_splits(d, x0.max_seq_len, props.multi_processor_count)
+    steps = []
+    for x in reps:
+        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
+                                   block_size=x.block_size, token_scale=x.token_scale)
+        steps.append((x, binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev)))
+
+    def run(i, ev=None):
+        x, st = steps[i % R]
+        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
+        if ev is not None:
+            ev[0].record()
+        st.attend(x.q_pe)
+        if ev is not None:
+            ev[1].record()
+        binding.mla_expand_v(d, st.o_lat, x.w_uv, out=st.out)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    # dominant kernel: HIP events around each decode launch (same stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs_dec = []
+    for i in range(args.steps):
+        x, st = steps[i % R]
+        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
+        a, b = evs[i]
+        a.record()
+        if P > 1:
+            binding.mla_decode_latent(d, st.cache, st.q_lat, x.q_pe, st.seq_lens, st.max_seq_len, P,
+                                      o_part=st.o_part, lse_part=st.lse_part)
+            b.record()
+            binding.mla_combine_splits(d, st.o_part, st.lse_part, o_lat=st.o_lat, lse=st.lse)
+        else:
+            binding.mla_decode_latent(d, st.cache, st.q_lat, x.q_pe, st.seq_lens, st.max_seq_len, 1,
+                                      o_lat=st.o_lat, lse=st.lse)
+            b.record()
+        binding.mla_expand_v(d, st.o_lat, x.w_uv, out=st.out)
+        evs_dec.append((a, b))
+    torch.cuda.synchronize()
+    t_dec = sum(a.elapsed_time(b) for a, b in evs_dec) / len(evs_dec) * 1e-3
+
+    # decode + combine (the attention part of the step)
+    evs_att = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(i, evs_att[i])
+    torch.cuda.synchronize()
+    t_att = sum(a.elapsed_time(b) for a, b in evs_att) / len(evs_att) * 1e-3
+
+    lens_sum = int(x0.seq_lens.to(torch.int64).sum().item())
+    flops_core = core_flops(x0.batch, x0.heads, lens_sum)
+    flops_step = flops_core + proj_flops(x0.batch, x0.heads)
+    gbs_step = cache_bytes / t_step / 1e9
+    gbs_dec = cache_bytes / t_dec / 1e9
+    gbs_att = cache_bytes / t_att / 1e9
+    traffic = traffic_from_counters(cache_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs_step, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp8_e4m3 cache / bf16 MFMA",
+        "data": "synthetic (seeded N(0,1) cache and queries, N(0,1/512) weights; no checkpoint)",
+        "config": {"workload": wl.name, "batch": x0.batch, "heads": x0.heads, "seq_len": x0.max_seq_len,
+                   "kv_lora_rank": 512, "qk_rope_head_dim": 64, "layout": wl.layout, "cache_dtype": wl.dtype,
+                   "num_splits": P, "input_replicas": R, "cache_bytes_per_step": cache_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs_dec, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_dec / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernel": "mla_decode_latent",
+        "decode_us": round(t_dec * 1e6, 3),
+        "decode_plus_combine_us": round(t_att * 1e6, 3),
+        "attention_gbs": round(gbs_att, 2),
+        "attention_hbm_frac": round(gbs_att / HBM_PEAK_GBS, 4),
+        "tflops_step": round(flops_step / t_step / 1e12, 3),
+        "tflops_decode": round(flops_core / t_dec / 1e12, 3),
+        "decode_mfma_frac": round(flops_core / t_dec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "tokens_per_s": round(x0.batch / t_step, 1),
+        "device": props.name,
+        "cus": props.multi_processor_count,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x0)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,7 +15,8 @@ Recipe (per workload): one ``torch.Generator`` on the target device, seeded
 with the workload's seed, draws in this order: sequence lengths (if they
 vary), the physical block permutation (if paged), q_nope, q_pe, W_UK, W_UV,
 then the cache rows: contiguous caches one [T_b, 576] draw per sequence,
-paged caches one [num_blocks, block_size, 576] draw in physical block order.  Draws are float32 N(0,1) scaled by the stated std, then rounded to
+paged caches one [num_blocks, block_size, 576] draw in physical block
+order.  Draws are float32 N(0,1) scaled by the stated std, then rounded to
 bfloat16 (round to nearest even).  For an E4M3 cache each token's 576 values
 x_t get the scale s_t = max|x_t| / 448 (float32) and are stored as the E4M3
 code of x_t / s_t (round to nearest even, clamped to +-448).
@@ -105,11 +106,11 @@ class DecodeInputs:
 
     @property
     def batch(self):
-        return self.workload.batch
+        return self.q_nope.shape[0]
 
     @property
     def heads(self):
-        return self.workload.heads
+        return self.q_nope.shape[1]
 
     def cache_bytes(self):
         """Bytes of cache rows the decode step reads (active tokens only)."""
