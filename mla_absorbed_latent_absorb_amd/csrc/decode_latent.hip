@@ -8,82 +8,81 @@
 // §6.1: absorbed decode is MQA with a 576-wide key whose first 512 elements
 // are also the value).
 //
-// Work decomposition (one workgroup per (sequence, split)):
-//   - the workgroup streams its token range in tiles of 32 cache rows
-//     (36,864 bytes) from HBM into LDS with 16-byte direct-to-LDS loads,
-//     each row read exactly once, through a ring of NBUF tile buffers
-//     (prefetch distance NBUF - 1 tiles);
-//   - each wave owns 16 heads.  Its 16 x 576 query block stays in registers
-//     as the B operand of the score product S^T[token][head] = K . Q^T
-//     (16x16x32 bf16 MFMA), so a lane holds the scores of one head and the
-//     softmax row reductions stay within a lane and across 4 lanes;
-//   - the probabilities go straight from the score accumulators to the B
-//     operand of O^T[c][head] += V^T . P^T, with V^T read from the same LDS
-//     tile by transposing LDS reads: both products run on MFMA and every
-//     head shares the one LDS copy of each tile;
-//   - the running max is only moved (and O rescaled) when it grows by more
-//     than 2^8 in the exp2 domain, so the rescale of the 128 accumulator
-//     registers is rare after the first tile.
+// Work decomposition: one workgroup per (sequence, split), NW = H/16 waves.
+//   - The workgroup streams its token range in tiles of 32 cache rows
+//     (36,864 bytes) from HBM into LDS with 16-byte direct-to-LDS loads; each
+//     row is read from HBM exactly once, through a ring of NBUF tile buffers
+//     (prefetch distance NBUF - 1 tiles).
+//   - Scores: wave w owns heads 16w .. 16w+15.  Its 16 x 576 query block stays
+//     in registers as the B operand of S^T[token][head] = K . Q^T
+//     (16x16x32 bf16 MFMA), so a lane holds scores of one head and the
+//     softmax row reductions stay within a lane plus two cross-lane steps.
+//   - P.V: the waves split the 512 latent columns instead of the heads: wave
+//     w accumulates O^T[c][head] for columns [w*512/NW, (w+1)*512/NW) and all
+//     H heads.  The bf16 probability fragments (already in the MFMA operand
+//     layout) are exchanged through LDS, so every V^T element of a tile is
+//     fetched with the (slow) transposing LDS read exactly once, and each V^T
+//     fragment feeds NW MFMAs.
+//   - The running max of a head moves (and O is rescaled by exp2 of the
+//     difference) only when it grows by more than 2^8 in the exp2 domain; the
+//     owner wave publishes the factor through LDS, so rescales are rare after
+//     the first tile.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "tile_layout.hpp"
 
 namespace mla {
-
-constexpr int kTile = 32;                      // cache rows per tile
-constexpr int kKvRow = kDc * 2;                // 1024-byte latent row in LDS
-constexpr int kPeRow = kDr * 2;                // 128-byte RoPE row in LDS
-constexpr int kPeRegion = kTile * kKvRow;      // RoPE rows follow the 32 latent rows
-constexpr int kTileBytes = kTile * (kKvRow + kPeRow);  // 36864
-constexpr int kTileDma = kTile + kTile * kPeRow / 1024;  // 36 wave-wide 1 KiB copies per tile
-constexpr float kRescaleLog2 = 8.0f;           // lazy-rescale threshold (exp2 domain)
-
-// LDS tile (per ring buffer):
-//   [0, 32 KiB)      latent rows: row r holds chunk c (16 bytes = 8 elements)
-//                    of token r at chunk slot c ^ kv_swizzle(r)
-//   [32, 36 KiB)     RoPE rows: row r holds chunk c of token r at slot
-//                    c ^ pe_swizzle(r)
-// A wave-wide 1 KiB copy fills one latent row (one token: scalar base
-// address) or eight RoPE rows.
 
 template <int NW, int NBUF, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_latent_kernel(DecodeArgs a) {
-  constexpr int LW = NW < 4 ? NW : 4;     // waves that issue the tile copies
-  constexpr int LPW = kTileDma / LW;      // copies per loading wave per tile
-  constexpr int KV_PW = kTile / LW;       // latent rows per loading wave
-  constexpr int PE_PW = (kTile / 8) / LW; // RoPE copies (8 rows each) per loading wave
-  static_assert(kTileDma % LW == 0 && kTile % LW == 0 && (kTile / 8) % LW == 0, "tile copies must split evenly");
-  __shared__ __attribute__((aligned(1024))) char smem[NBUF * kTileBytes];
+  constexpr int H = NW * 16;
+  // Tile copies are spread over all waves: each wave copies KV_PW latent rows;
+  // the 4 RoPE copies (8 rows each) go to waves 0..3 (or are shared evenly
+  // when there are fewer waves).
+  constexpr int KV_PW = kTile / NW;       // latent rows per wave
+  constexpr int PE_W = NW < 4 ? NW : 4;   // waves that copy RoPE rows
+  constexpr int PE_PW = 4 / PE_W;         // RoPE copies per such wave
+  constexpr int CB = 32 / NW;             // 16-column blocks of O owned by a wave
+  constexpr int C = 512 / NW;             // latent columns owned by a wave
+  static_assert(kTile % NW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
+  // LDS: tile ring, then the probability exchange (one 1 KiB fragment per
+  // wave), the per-head rescale factors / reciprocal sums, and the flags.
+  constexpr int kRing = NBUF * kTileBytes;
+  constexpr int kPOff = kRing;
+  constexpr int kAlphaOff = kPOff + NW * 1024;
+  constexpr int kFlagOff = kAlphaOff + H * 4;
+  constexpr int kSmem = kFlagOff + 64;
+  static_assert(NW * C * 64 <= kRing, "epilogue staging (16 rows x C fp32 per wave) must fit in the ring");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
-  const int hl = lane & 15;   // head within the wave's 16
+  const int hl = lane & 15;   // row/column within a 16-block
   const int g4 = lane >> 4;   // 16-lane group
-  const int b = blockIdx.x / a.num_splits;
-  const int split = blockIdx.x - b * a.num_splits;
-  const int h = w * 16 + hl;
+  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
+  const int b = item / a.num_splits;
+  const int split = item - b * a.num_splits;
+  const int h = w * 16 + hl;  // head whose scores this lane computes
 
   int T = a.seq_lens[b];
   T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
   const int t_begin = split * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
   const bool final_out = a.num_splits == 1;
-
-  float* part_row = nullptr;
-  uint16_t* final_row = nullptr;
-  if (final_out) {
-    final_row = a.o_lat + ((size_t)b * a.num_heads + h) * kDc;
-  } else {
-    part_row = a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads + h) * kDc;
-  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const int col0 = w * C;     // first latent column of this wave's P.V share
 
   if (t_begin >= t_end) {
     // No tokens in this range: zero weight (o = 0, lse = -inf).
-    for (int cb = 0; cb < 32; ++cb) {
+    for (int r = 0; r < 16; ++r) {
+      const size_t row = (size_t)(w * 16 + r);
       if (final_out) {
-        *reinterpret_cast<u32x2*>(final_row + cb * 16 + g4 * 4) = u32x2{0u, 0u};
+        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + row) * kDc + lane * 8) = u32x4{0u, 0u, 0u, 0u};
       } else {
-        *reinterpret_cast<f32x4*>(part_row + cb * 16 + g4 * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        float* dst = a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads + row) * kDc;
+        *reinterpret_cast<f32x4*>(dst + lane * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dst + 256 + lane * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     if (g4 == 0) {
@@ -109,64 +108,107 @@ void decode_latent_kernel(DecodeArgs a) {
     for (int s = 0; s < 18; ++s) asm volatile("" : : "v"(q[s]));
   }
 
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   const char* kv_base = uniform_ptr(a.kv);
   const char* pe_base = uniform_ptr(a.pe);
 
-  auto issue_tile = [&](int tile, int buf) {
-    if (w >= LW) return;
-    const int t0 = t_begin + tile * kTile;
-    const int last = min(kTile, t_end - t0) - 1;  // rows past the end re-read the last row
+  // Source of one tile (all wave-uniform): first cache slot, last valid row,
+  // LDS destination.  Rows past the end re-read the last valid row.
+  struct TileSrc {
     int64_t slot0;
+    int last;
+    uint32_t dst;
+  };
+  auto tile_src = [&](int tile, int buf) -> TileSrc {
+    const int t0 = t_begin + tile * kTile;
+    TileSrc ts;
+    ts.last = min(kTile, t_end - t0) - 1;
     if (PAGED) {
-      const int blk = a.block_table[(size_t)b * a.max_blocks + t0 / a.block_size];
-      slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
+      // Scalar load (constant address space): a vector load here would make
+      // the compiler wait for every tile copy in flight before using it.
+      const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+          reinterpret_cast<uintptr_t>(a.block_table));
+      const int blk = table[(size_t)b * a.max_blocks + t0 / a.block_size];
+      ts.slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
     } else {
-      slot0 = (int64_t)b * a.seq_stride + t0;
+      ts.slot0 = (int64_t)b * a.seq_stride + t0;
     }
-    const uint32_t dst = lds0 + buf * kTileBytes;
+    ts.dst = lds0 + buf * kTileBytes;
+    return ts;
+  };
+  // Per-lane offsets come from the lane id (mbcnt) of the current iteration
+  // rather than being kept live across the loop: a spilled value's scratch
+  // reload would wait for every tile copy in flight (vmcnt counts in issue
+  // order).  ln16 = 16 * lane.
+  auto copy_kv = [&](const TileSrc& ts, int r, uint32_t ln16) {  // latent row r
+    const int64_t slot = ts.slot0 + min(r, ts.last);
+    const uint32_t voff = ln16 ^ (kv_swizzle(r) << 4);
+    dma16(uniform_ptr(kv_base + slot * a.kv_sb), voff, ts.dst + r * kKvRow);
+  };
+  auto copy_pe = [&](const TileSrc& ts, int i, uint32_t ln16) {  // RoPE rows 8i .. 8i+7
+    const uint32_t r = 8 * i + (ln16 >> 7);
+    const uint32_t c = ((ln16 >> 4) & 7u) ^ pe_swizzle(r);
+    const uint32_t voff = (uint32_t)min((int)r, ts.last) * (uint32_t)a.pe_sb + (c << 4);
+    dma16(uniform_ptr(pe_base + ts.slot0 * a.pe_sb), voff, ts.dst + kPeRegion + i * 1024);
+  };
+  // Copy k of this wave: latent row w*KV_PW + k, then (waves < PE_W) RoPE
+  // copy w*PE_PW + k - KV_PW.
+  const bool pe_wave = w < PE_W;
+  const int n_copy = KV_PW + (pe_wave ? PE_PW : 0);
+  auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
+    if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
+    else copy_pe(ts, w * PE_PW + (k - KV_PW), ln16);
+  };
+  auto issue_tile = [&](int tile, int buf) {
+    const TileSrc ts = tile_src(tile, buf);
+    const uint32_t ln16 = lane_id() << 4;
 #pragma unroll
-    for (int k = 0; k < KV_PW; ++k) {
-      const int r = w * KV_PW + k;
-      const int64_t slot = slot0 + min(r, last);
-      const uint32_t voff = ((uint32_t)lane ^ kv_swizzle(r)) << 4;
-      dma16(uniform_ptr(kv_base + slot * a.kv_sb), voff, dst + r * kKvRow);
-    }
+    for (int k = 0; k < KV_PW; ++k) copy_kv(ts, w * KV_PW + k, ln16);
+    if (pe_wave) {
 #pragma unroll
-    for (int k = 0; k < PE_PW; ++k) {
-      const int i = w * PE_PW + k;
-      const uint32_t r = 8 * i + (lane >> 3);
-      const uint32_t c = ((uint32_t)lane & 7u) ^ pe_swizzle(r);
-      const uint32_t voff = (uint32_t)min((int)r, last) * (uint32_t)a.pe_sb + (c << 4);
-      dma16(uniform_ptr(pe_base + slot0 * a.pe_sb), voff, dst + kPeRegion + i * 1024);
+      for (int k = 0; k < PE_PW; ++k) copy_pe(ts, w * PE_PW + k, ln16);
     }
   };
 
-  // ---- per-lane LDS offsets (swizzled) ----
-  // score K fragment: token row hl (and 16 + hl), element block d = 32 s + 8 g4
-  const uint32_t kx = kv_swizzle(hl);
-  uint32_t k_off[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) k_off[m] = hl * kKvRow + (((4u * m + g4) ^ kx) << 4);
-  const uint32_t p_off0 = kPeRegion + hl * kPeRow + (((uint32_t)g4 ^ pe_swizzle(hl)) << 4);
-  const uint32_t p_off1 = kPeRegion + hl * kPeRow + (((uint32_t)(4 + g4) ^ pe_swizzle(hl)) << 4);
-  // P.V fragment: rows 4 g4 + hl/4 (and +16), columns 16 cb + 4 (hl%4) .. +3
-  const uint32_t vr = 4 * g4 + (hl >> 2);
-  const uint32_t vx = kv_swizzle(vr);
-  const uint32_t vsel = (hl & 3) >> 1;
-  uint32_t v_off[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) v_off[m] = vr * kKvRow + (((2u * m + vsel) ^ vx) << 4) + ((hl & 1) << 3);
+  // ---- per-lane LDS addresses inside a tile (swizzled) ----
+  // The swizzles XOR only the 16-byte chunk index and tile buffers are 1 KiB
+  // aligned, so every fragment address is a per-lane base XOR a step constant
+  // plus an immediate offset: one VALU op per read instead of recomputing the
+  // swizzle.
+  //   score K fragment of step s: token row l%16 (and 16 + l%16), elements
+  //   32 s + 8 (l/16) .. +7, i.e. chunk 4 s + l/16 of the latent row (s < 16)
+  //   or chunk 4 (s-16) + l/16 of the RoPE row.  With s = 4 m + s4 the latent
+  //   chunk is 16 m + ((l/16 ^ swz) ^ 4 s4).
+  auto k_base = [&](uint32_t l) -> uint32_t {
+    const uint32_t r = l & 15u;
+    return r * kKvRow + (((l >> 4) ^ kv_swizzle(r)) << 4);
+  };
+  auto pe_lane_base = [&](uint32_t l) -> uint32_t {
+    const uint32_t r = l & 15u;
+    return kPeRegion + r * kPeRow + (((l >> 4) ^ pe_swizzle(r)) << 4);
+  };
+  //   V^T fragment of column block cb of the wave: rows 4 (l/16) + (l%16)/4
+  //   (and +16), columns col0 + 16 cb + 4 (l%4) .. +3 (transposing read: lane
+  //   l%16 receives column col0 + 16 cb + l%16).  col0 / 16 is a multiple of
+  //   CB, so the chunk 2 (col0/16 + cb) + (l%4)/2 is (2 col0/16 + (l%4)/2) XOR 2 cb.
+  auto v_base = [&](uint32_t l) -> uint32_t {
+    const uint32_t r = 4 * (l >> 4) + ((l & 15u) >> 2);
+    return r * kKvRow + ((((uint32_t)(2 * (col0 >> 4)) | ((l & 3u) >> 1)) ^ kv_swizzle(r)) << 4) + ((l & 1u) << 3);
+  };
+  static_assert(kTileBytes % 1024 == 0, "tile buffers must stay 1 KiB aligned");
 
-  f32x4 o[32];
+  f32x4 o[CB][NW];   // o[cb][n][j] = O^T[col0 + 16 cb + 4 g4 + j][16 n + hl]
 #pragma unroll
-  for (int cb = 0; cb < 32; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference max of raw scores q.k (unscaled)
-  float l_sum = 0.f;        // this lane's share of sum_t exp2((s - m_ref) * c)
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int n = 0; n < NW; ++n) o[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // reference max of raw scores q.k of head h (owner)
+  float l_sum = 0.f;        // this lane's share of sum_t exp2((s - m_ref) * c) (owner)
   const float c2 = a.scale_log2;
 
-  // ---- prologue ----
+  if (w == 0 && lane == 0) lds_write_u32x2(lds0 + kFlagOff, u32x2{0u, 0u});  // published by the first barrier
+
+  // ---- prologue: tiles 0 .. NBUF-2 in flight ----
   if (NBUF == 1) {
     issue_tile(0, 0);
   } else {
@@ -175,30 +217,43 @@ void decode_latent_kernel(DecodeArgs a) {
       if (i < n_tiles) issue_tile(i, i);
   }
 
+  // Copies a wave has in flight per tile: KV_PW, plus PE_PW for waves < PE_W.
+  // With a ring of several tiles the next tile's copies are spread over the
+  // score loop (one every kCopyStride steps) so the address unit drains them
+  // while the MFMAs run instead of stalling the waves at the issue.
+  constexpr int kCopyStride = 18 / (KV_PW + PE_PW) > 0 ? 18 / (KV_PW + PE_PW) : 1;
+  static_assert(NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18, "copies must fit in the score loop");
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = NBUF == 1 ? 0 : it % NBUF;
-    if (NBUF > 1) {
-      const int nxt = it + NBUF - 1;
-      if (nxt < n_tiles) issue_tile(nxt, nxt % NBUF);
+    {
+      // wait for this wave's copies of tile it (later tiles may stay in flight)
+      const int later = NBUF > 1 ? min(NBUF - 2, n_tiles - 1 - it) : 0;
+      if (later <= 0) {
+        wait_vmcnt<0>();
+      } else if (later == 1) {
+        if (pe_wave) wait_vmcnt<KV_PW + PE_PW>(); else wait_vmcnt<KV_PW>();
+      } else {
+        if (pe_wave) wait_vmcnt<(NBUF > 3 ? 2 * (KV_PW + PE_PW) : 0)>(); else wait_vmcnt<(NBUF > 3 ? 2 * KV_PW : 0)>();
+      }
     }
-    if (w < LW) {
-      // copies of later tiles still allowed in flight
-      const int later = NBUF > 1 ? min(NBUF - 1, n_tiles - 1 - it) : 0;
-      if (later <= 0) wait_vmcnt<0>();
-      else if (later == 1) wait_vmcnt<(NBUF > 1 ? LPW : 0)>();
-      else if (later == 2) wait_vmcnt<(NBUF > 2 ? 2 * LPW : 0)>();
-      else wait_vmcnt<(NBUF > 3 ? 3 * LPW : 0)>();
-    }
+    // Tile it is visible to all waves, and every wave has finished iteration
+    // it-1, so the buffer of tile it-1 can be refilled.
     barrier();
+    const int nxt = it + NBUF - 1;
+    const bool copy_next = NBUF > 1 && nxt < n_tiles;
+    const TileSrc nts = tile_src(copy_next ? nxt : it, NBUF > 1 ? nxt % NBUF : 0);
     __builtin_amdgcn_sched_barrier(0);
 
     const uint32_t tb = lds0 + buf * kTileBytes;
+    const uint32_t ln = lane_id();
+    const uint32_t ln16 = ln << 4;
+    const uint32_t kb0 = tb + k_base(ln);
+    const uint32_t pb0 = tb + pe_lane_base(ln);
 
     // ---- scores: S^T[token][head] for tokens 0..15 (s0) and 16..31 (s1) ----
-    // K fragments are read two steps ahead of their MFMAs.
     auto k_addr = [&](int s) -> uint32_t {
-      if (s < 16) return tb + k_off[s & 3] + (uint32_t)(s >> 2) * 256u;
-      return tb + (s == 16 ? p_off0 : p_off1);
+      if (s < 16) return (kb0 ^ ((uint32_t)(s & 3) << 6)) + 256u * (uint32_t)(s >> 2);
+      return pb0 ^ ((uint32_t)(s - 16) << 6);
     };
     auto k_hi = [&](int s) -> uint32_t { return s < 16 ? 16u * kKvRow : 16u * kPeRow; };
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -210,13 +265,34 @@ void decode_latent_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < 18; ++s) {
       if (s + 2 < 18) {
-        ka[(s + 2) % 3] = lds_read_b128(k_addr(s + 2));
-        kb[(s + 2) % 3] = lds_read_b128(k_addr(s + 2) + k_hi(s + 2));
+        const uint32_t ad = k_addr(s + 2);
+        ka[(s + 2) % 3] = lds_read_b128(ad);
+        kb[(s + 2) % 3] = lds_read_b128(ad + k_hi(s + 2));
+      }
+      if (NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
+        if (copy_next && s / kCopyStride < n_copy) issue_copy(nts, s / kCopyStride, ln16);
       }
       s0 = mfma16(ka[s % 3], q[s], s0);
       s1 = mfma16(kb[s % 3], q[s], s1);
       __builtin_amdgcn_sched_barrier(0);
     }
+
+    // V^T fragment of the wave's column block cb (independent of the scores,
+    // so the first reads are issued before the softmax to hide their latency)
+    const uint32_t vb0 = tb + v_base(ln);
+    auto va_load = [&](int cb) -> bf16x8 {
+      const uint32_t off = vb0 ^ ((uint32_t)cb << 5);
+      const bf16x4 lo = lds_read_tr16(off);                // tokens 4 g4 + 0..3
+      const bf16x4 hi = lds_read_tr16(off + 16 * kKvRow);  // tokens 16 + 4 g4 + 0..3
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // Many heads (NW > CB): all CB fragments stay in registers and the NW
+    // probability fragments stream.  Few heads: the other way round.
+    constexpr bool kKeepV = NW > CB;
+    constexpr int kVPre = kKeepV ? CB : (CB < 2 ? CB : 2);
+    bf16x8 va[kKeepV ? CB : 3];
+#pragma unroll
+    for (int cb = 0; cb < kVPre; ++cb) va[cb] = va_load(cb);
 
     // ---- mask the ragged tail ----
     const int t0 = t_begin + it * kTile;
@@ -229,18 +305,17 @@ void decode_latent_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- online softmax (one head per lane; 4 lanes share a head) ----
+    // ---- online softmax of the wave's own heads ----
     float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                      fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float m_new = fmaxf(m_ref, mx);
     const bool grow = (m_new - m_ref) * c2 > kRescaleLog2;
-    if (__ballot(grow) != 0) {
-      const float alpha = fast_exp2((m_ref - m_new) * c2);
+    const bool any_grow = __ballot(grow) != 0;
+    float alpha = 1.0f;
+    if (any_grow) {
+      alpha = fast_exp2((m_ref - m_new) * c2);
       l_sum *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb) o[cb] *= alpha;
       m_ref = m_new;
     }
     const float mb = m_ref * c2;
@@ -251,50 +326,116 @@ void decode_latent_kernel(DecodeArgs a) {
       p[4 + j] = fast_exp2(fmaf(s1[j], c2, -mb));
     }
     l_sum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    // B operand of P.V: element i <-> token i<4 ? 4 g4 + i : 16 + 4 g4 + (i-4)
+    // B operand of P.V for head 16 w + hl: element i <-> token
+    // i<4 ? 4 g4 + i : 16 + 4 g4 + (i-4)
     const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+    lds_write_u32x4(lds0 + kPOff + w * 1024 + lane * 16, pk);
+    if (g4 == 0) lds_write_f32(lds0 + kAlphaOff + h * 4, alpha);
+    if (lane == 0) lds_write_u8(lds0 + kFlagOff + w, any_grow ? 1u : 0u);
+    barrier();  // probabilities and rescale factors of every head are published
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- O^T[c][head] += V^T . P^T over the 32 tokens ----
-    auto v_addr = [&](int cb) -> uint32_t { return tb + v_off[cb & 7] + (uint32_t)(cb >> 3) * 256u; };
-    bf16x4 vl[3], vh[3];
-    vl[0] = lds_read_tr16(v_addr(0));
-    vh[0] = lds_read_tr16(v_addr(0) + 16 * kKvRow);
-    vl[1] = lds_read_tr16(v_addr(1));
-    vh[1] = lds_read_tr16(v_addr(1) + 16 * kKvRow);
+    // ---- rescale (rare after the first tile) ----
+    const u32x2 fl = lds_read_u32x2(lds0 + kFlagOff);  // one byte per wave
+    if ((fl[0] | fl[1]) != 0) {
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      if (cb + 2 < 32) {
-        vl[(cb + 2) % 3] = lds_read_tr16(v_addr(cb + 2));                // tokens 4 g4 + 0..3
-        vh[(cb + 2) % 3] = lds_read_tr16(v_addr(cb + 2) + 16 * kKvRow);  // tokens 16 + 4 g4 + 0..3
+      for (int n = 0; n < NW; ++n) {
+        const float al = lds_read_f32(lds0 + kAlphaOff + (16 * n + hl) * 4);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][n] *= al;
       }
-      const bf16x8 va = __builtin_shufflevector(vl[cb % 3], vh[cb % 3], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[cb] = mfma16(va, pb, o[cb]);
-      __builtin_amdgcn_sched_barrier(0);
     }
 
-    barrier();  // every wave is done with this buffer
-    if (NBUF == 1 && it + 1 < n_tiles) issue_tile(it + 1, 0);
+    // ---- O^T[c][head] += V^T . P^T for the wave's columns, all heads ----
+    auto p_load = [&](int n) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, lds_read_u32x4(lds0 + kPOff + n * 1024 + lane * 16));
+    };
+    if constexpr (kKeepV) {
+      bf16x8 pf[2];
+      pf[0] = p_load(0);
+#pragma unroll
+      for (int n = 0; n < NW; ++n) {
+        if (n + 1 < NW) pf[(n + 1) & 1] = p_load(n + 1);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[cb][n] = mfma16(va[cb], pf[n & 1], o[cb][n]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      bf16x8 pf[NW];
+#pragma unroll
+      for (int n = 0; n < NW; ++n) pf[n] = p_load(n);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        if (cb + 2 < CB) va[(cb + 2) % 3] = va_load(cb + 2);
+#pragma unroll
+        for (int n = 0; n < NW; ++n) o[cb][n] = mfma16(va[cb % 3], pf[n], o[cb][n]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    if (NBUF == 1) {
+      barrier();  // the single buffer is free
+      if (it + 1 < n_tiles) issue_tile(it + 1, 0);
+    }
   }
 
   // ---- finalize ----
-  float l_tot = l_sum + __shfl_xor(l_sum, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const float inv = 1.0f / l_tot;
+  const float l_tot = sum_xor32(sum_xor16(l_sum));
   const float lse_val = m_ref * a.scale + __logf(l_tot);
+  if (g4 == 0) {
+    lds_write_f32(lds0 + kAlphaOff + h * 4, 1.0f / l_tot);
+    if (final_out) a.lse[(size_t)b * a.num_heads + h] = lse_val;
+    else a.lse_part[((size_t)b * a.num_splits + split) * a.num_heads + h] = lse_val;
+  }
+  barrier();
+  float inv[NW];
+#pragma unroll
+  for (int n = 0; n < NW; ++n) inv[n] = lds_read_f32(lds0 + kAlphaOff + (16 * n + hl) * 4);
+
+  // Each wave holds its C columns for all H heads.  Per 16-head block, stage
+  // the block in a private LDS region of the (idle) tile ring, chunk slots
+  // XOR-swizzled by row, and store whole row segments of C columns.
+  const uint32_t stage = lds0 + (uint32_t)w * (uint32_t)(C * 64);
   if (final_out) {
+    constexpr int RC = C / 8;                  // 16-byte chunks per bf16 row
+    constexpr uint32_t SWZ = RC >= 16 ? 15u : (uint32_t)(RC - 1);
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      const u32x2 v = {pack_bf16x2(o[cb][0] * inv, o[cb][1] * inv), pack_bf16x2(o[cb][2] * inv, o[cb][3] * inv)};
-      *reinterpret_cast<u32x2*>(final_row + cb * 16 + g4 * 4) = v;
+    for (int n = 0; n < NW; ++n) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        // columns 16 cb + 4 g4 .. +3 -> 8 bytes at chunk 2 cb + g4/2, half g4 % 2
+        const u32x2 v = {pack_bf16x2(o[cb][n][0] * inv[n], o[cb][n][1] * inv[n]),
+                         pack_bf16x2(o[cb][n][2] * inv[n], o[cb][n][3] * inv[n])};
+        const uint32_t chunk = ((uint32_t)(2 * cb + (g4 >> 1))) ^ ((uint32_t)hl & SWZ);
+        lds_write_b64(stage + hl * (uint32_t)(2 * C) + (chunk << 4) + ((g4 & 1) << 3), v);
+      }
+#pragma unroll
+      for (int k = 0; k < (16 * RC) / 64; ++k) {
+        const uint32_t L = (uint32_t)(64 * k + lane);
+        const uint32_t row = L / RC, ch = L % RC;
+        const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
+        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + 16 * n + row) * kDc + col0 + ch * 8) = v;
+      }
     }
-    if (g4 == 0) a.lse[(size_t)b * a.num_heads + h] = lse_val;
   } else {
+    constexpr int RC = C / 4;                  // 16-byte chunks per fp32 row
+    float* part = a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads) * kDc;
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) *reinterpret_cast<f32x4*>(part_row + cb * 16 + g4 * 4) = o[cb] * inv;
-    if (g4 == 0) a.lse_part[((size_t)b * a.num_splits + split) * a.num_heads + h] = lse_val;
+    for (int n = 0; n < NW; ++n) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t chunk = ((uint32_t)(4 * cb + g4)) ^ (uint32_t)hl;
+        lds_write_f32x4(stage + hl * (uint32_t)(4 * C) + (chunk << 4), o[cb][n] * inv[n]);
+      }
+#pragma unroll
+      for (int k = 0; k < (16 * RC) / 64; ++k) {
+        const uint32_t L = (uint32_t)(64 * k + lane);
+        const uint32_t row = L / RC, ch = L % RC;
+        const f32x4 v = lds_read_f32x4(stage + row * (uint32_t)(4 * C) + ((ch ^ (row & 15u)) << 4));
+        *reinterpret_cast<f32x4*>(part + (size_t)(16 * n + row) * kDc + col0 + ch * 4) = v;
+      }
+    }
   }
 }
 

@@ -90,12 +90,93 @@ __device__ __forceinline__ uint32_t kv_swizzle(uint32_t row) {
 // even rows): the XOR value is a bijection of (row / 2) % 8.
 __device__ __forceinline__ uint32_t pe_swizzle(uint32_t row) { return (row >> 1) & 7u; }
 
+__device__ __forceinline__ void lds_write_b64(uint32_t byte_off, u32x2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ void lds_write_f32x4(uint32_t byte_off, f32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) f32x4*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ void lds_write_u32x4(uint32_t byte_off, u32x4 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ void lds_write_f32(uint32_t byte_off, float v) {
+  *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ void lds_write_u32(uint32_t byte_off, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ float lds_read_f32(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)byte_off);
+}
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((uintptr_t)byte_off);
+}
+__device__ __forceinline__ u32x4 lds_read_u32x4(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((uintptr_t)byte_off);
+}
+__device__ __forceinline__ f32x4 lds_read_f32x4(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>((uintptr_t)byte_off);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by id.  This maps the
+// launch index so that consecutive work items (e.g. the splits of one
+// sequence, which read the same query block) run on the same XCD and share
+// its L2: XCD x receives the contiguous item range of its share of the grid.
+__device__ __forceinline__ int xcd_grouped_index(int id, int grid) {
+  constexpr int kXcd = 8;
+  const int per = grid / kXcd, rem = grid % kXcd;
+  const int x = id % kXcd, k = id / kXcd;
+  const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return start + k;
+}
+
+// Cross-lane reductions between lanes l and l^16 / l^32 with the gfx950
+// permlane swaps (VALU, no LDS round trip).  Each swap returns the pair
+// {x[l], x[l^k]} in some order, so a commutative op of the two halves is the
+// pairwise reduction.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void lds_write_u8(uint32_t byte_off, uint32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) uint8_t*>((uintptr_t)byte_off) = (uint8_t)v;
+}
+__device__ __forceinline__ void lds_write_u32x2(uint32_t byte_off, u32x2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2*>((uintptr_t)byte_off) = v;
+}
+__device__ __forceinline__ u32x2 lds_read_u32x2(uint32_t byte_off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>((uintptr_t)byte_off);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo;
   __bf16 b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Lane index recomputed at the point of use (v_mbcnt over a full mask).  It is
+// opaque to the compiler on purpose: values derived from it are then computed
+// where they are needed instead of being hoisted out of loops, kept live, and
+// spilled under register pressure.
+__device__ __forceinline__ uint32_t lane_id() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
 }
 
 __device__ __forceinline__ int wave_id() {
