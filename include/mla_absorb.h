@@ -163,7 +163,7 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  *                chunk = 32 * ceil(ceil(max_seq_len / P) / 32).
  *   P == 1: writes o_lat (device bf16 [B, H, 512]) and lse (device fp32 [B, H]);
  *           o_part / lse_part must be NULL.
- *   P  > 1: writes o_part (device fp32 [B, P, H, 512], each split normalised
+ *   P  > 1: writes o_part (device bf16 [B, P, H, 512], each split normalised
  *           by its own softmax sum) and lse_part (device fp32 [B, P, H]); an
  *           empty split gets o = 0 and lse = -inf.  o_lat / lse must be NULL;
  *           merge with mla_combine_splits.
@@ -171,18 +171,19 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  */
 mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
                              const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,
-                             int32_t num_splits, float *o_part, float *lse_part, void *o_lat,
+                             int32_t num_splits, void *o_part, float *lse_part, void *o_lat,
                              float *lse, void *stream);
 
 /*
  * Split-KV merge: LSE = ln sum_i exp(lse_part[b,i,h]),
  * o_lat[b,h] = sum_i exp(lse_part[b,i,h] - LSE) * o_part[b,i,h]; splits with
  * lse = -inf carry no weight.
- *   o_part device fp32 [B, P, H, 512], lse_part device fp32 [B, P, H]
+ *   o_part device bf16 [B, P, H, 512], lse_part device fp32 [B, P, H]
+ *   (weights and sums in fp32)
  *   o_lat  device bf16 [B, H, 512] (output), lse device fp32 [B, H] (output,
  *          may be NULL)
  */
-mla_status mla_combine_splits(const mla_dims *dims, const float *o_part, const float *lse_part,
+mla_status mla_combine_splits(const mla_dims *dims, const void *o_part, const float *lse_part,
                               int32_t num_splits, void *o_lat, float *lse, void *stream);
 
 /*

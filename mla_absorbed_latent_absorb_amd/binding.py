@@ -211,10 +211,10 @@ def mla_decode_latent(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_splits=1
         _expect(lse, "lse", torch.float32, (B, H), dev)
     else:
         if o_part is None:
-            o_part = torch.empty((B, num_splits, H, d.kv_lora_rank), dtype=torch.float32, device=dev)
+            o_part = torch.empty((B, num_splits, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
         if lse_part is None:
             lse_part = torch.empty((B, num_splits, H), dtype=torch.float32, device=dev)
-        _expect(o_part, "o_part", torch.float32, (B, num_splits, H, d.kv_lora_rank), dev)
+        _expect(o_part, "o_part", torch.bfloat16, (B, num_splits, H, d.kv_lora_rank), dev)
         _expect(lse_part, "lse_part", torch.float32, (B, num_splits, H), dev)
     _check(load().mla_decode_latent(ctypes.byref(d), ctypes.byref(cache), _ptr(q_lat), _ptr(q_pe), _ptr(seq_lens),
                                     int(max_seq_len), int(num_splits),
@@ -230,7 +230,7 @@ def mla_combine_splits(d, o_part, lse_part, o_lat=None, lse=None, stream=None):
     B, H = d.batch, d.num_heads
     P = o_part.shape[1]
     dev = o_part.device
-    _expect(o_part, "o_part", torch.float32, (B, P, H, d.kv_lora_rank))
+    _expect(o_part, "o_part", torch.bfloat16, (B, P, H, d.kv_lora_rank))
     _expect(lse_part, "lse_part", torch.float32, (B, P, H), dev)
     if o_lat is None:
         o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
@@ -269,7 +269,7 @@ class DecodeStep:
         self.lse = torch.empty((B, H), dtype=f32, device=device)
         self.out = torch.empty((B, H, d.v_head_dim), dtype=bf, device=device)
         if self.num_splits > 1:
-            self.o_part = torch.empty((B, self.num_splits, H, d.kv_lora_rank), dtype=f32, device=device)
+            self.o_part = torch.empty((B, self.num_splits, H, d.kv_lora_rank), dtype=bf, device=device)
             self.lse_part = torch.empty((B, self.num_splits, H), dtype=f32, device=device)
         else:
             self.o_part = self.lse_part = None

@@ -33,19 +33,24 @@
 
 namespace mla {
 
-template <int NW, int NBUF, bool PAGED>
+template <int NW, int NBUF, bool PAGED, bool COPY_AT_BARRIER = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_latent_kernel(DecodeArgs a) {
   constexpr int H = NW * 16;
-  // Tile copies are spread over all waves: each wave copies KV_PW latent rows;
-  // the 4 RoPE copies (8 rows each) go to waves 0..3 (or are shared evenly
-  // when there are fewer waves).
-  constexpr int KV_PW = kTile / NW;       // latent rows per wave
-  constexpr int PE_W = NW < 4 ? NW : 4;   // waves that copy RoPE rows
+  // Tile copies: CW copy waves each copy KV_PW latent rows; the 4 RoPE copies
+  // (8 rows each) go to copy waves 0..3 (or are shared evenly among fewer).
+  // COPY_AT_BARRIER: only waves 0 .. NW/2-1 copy, all at once just before the
+  // mid-tile barrier, where they otherwise wait for the other half (the
+  // lower-numbered waves win the SIMD arbitration and finish their scores
+  // first); a copy that stalls at issue then delays no MFMA work.
+  static_assert(!COPY_AT_BARRIER || (NBUF > 1 && NW >= 4), "copy at the barrier needs a ring and 4+ waves");
+  constexpr int CW = COPY_AT_BARRIER ? NW / 2 : NW;  // waves that copy
+  constexpr int KV_PW = kTile / CW;       // latent rows per copy wave
+  constexpr int PE_W = CW < 4 ? CW : 4;   // waves that copy RoPE rows
   constexpr int PE_PW = 4 / PE_W;         // RoPE copies per such wave
   constexpr int CB = 32 / NW;             // 16-column blocks of O owned by a wave
   constexpr int C = 512 / NW;             // latent columns owned by a wave
-  static_assert(kTile % NW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
+  static_assert(kTile % CW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
   // LDS: tile ring, then the probability exchange (one 1 KiB fragment per
   // wave), the per-head rescale factors / reciprocal sums, and the flags.
   constexpr int kRing = NBUF * kTileBytes;
@@ -53,7 +58,7 @@ void decode_latent_kernel(DecodeArgs a) {
   constexpr int kAlphaOff = kPOff + NW * 1024;
   constexpr int kFlagOff = kAlphaOff + H * 4;
   constexpr int kSmem = kFlagOff + 64;
-  static_assert(NW * C * 64 <= kRing, "epilogue staging (16 rows x C fp32 per wave) must fit in the ring");
+  static_assert(NW * C * 32 <= kRing, "epilogue staging (16 rows x C bf16 per wave) must fit in the ring");
   __shared__ __attribute__((aligned(1024))) char smem[kSmem];
 
   const int lane = threadIdx.x & 63;
@@ -77,13 +82,9 @@ void decode_latent_kernel(DecodeArgs a) {
     // No tokens in this range: zero weight (o = 0, lse = -inf).
     for (int r = 0; r < 16; ++r) {
       const size_t row = (size_t)(w * 16 + r);
-      if (final_out) {
-        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + row) * kDc + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-      } else {
-        float* dst = a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads + row) * kDc;
-        *reinterpret_cast<f32x4*>(dst + lane * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(dst + 256 + lane * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      uint16_t* dst = final_out ? a.o_lat + ((size_t)b * a.num_heads + row) * kDc
+                                : a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads + row) * kDc;
+      *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
     }
     if (g4 == 0) {
       if (final_out) a.lse[(size_t)b * a.num_heads + h] = -INFINITY;
@@ -153,13 +154,15 @@ void decode_latent_kernel(DecodeArgs a) {
   };
   // Copy k of this wave: latent row w*KV_PW + k, then (waves < PE_W) RoPE
   // copy w*PE_PW + k - KV_PW.
+  const bool copy_wave = w < CW;
   const bool pe_wave = w < PE_W;
-  const int n_copy = KV_PW + (pe_wave ? PE_PW : 0);
+  const int n_copy = copy_wave ? KV_PW + (pe_wave ? PE_PW : 0) : 0;
   auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
     if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
     else copy_pe(ts, w * PE_PW + (k - KV_PW), ln16);
   };
   auto issue_tile = [&](int tile, int buf) {
+    if (!copy_wave) return;
     const TileSrc ts = tile_src(tile, buf);
     const uint32_t ln16 = lane_id() << 4;
 #pragma unroll
@@ -269,7 +272,7 @@ void decode_latent_kernel(DecodeArgs a) {
         ka[(s + 2) % 3] = lds_read_b128(ad);
         kb[(s + 2) % 3] = lds_read_b128(ad + k_hi(s + 2));
       }
-      if (NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
+      if (!COPY_AT_BARRIER && NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
         if (copy_next && s / kCopyStride < n_copy) issue_copy(nts, s / kCopyStride, ln16);
       }
       s0 = mfma16(ka[s % 3], q[s], s0);
@@ -333,6 +336,15 @@ void decode_latent_kernel(DecodeArgs a) {
     lds_write_u32x4(lds0 + kPOff + w * 1024 + lane * 16, pk);
     if (g4 == 0) lds_write_f32(lds0 + kAlphaOff + h * 4, alpha);
     if (lane == 0) lds_write_u8(lds0 + kFlagOff + w, any_grow ? 1u : 0u);
+    if (COPY_AT_BARRIER && copy_next && copy_wave) {
+      const uint32_t ln16c = lane_id() << 4;
+#pragma unroll
+      for (int k = 0; k < KV_PW; ++k) copy_kv(nts, w * KV_PW + k, ln16c);
+      if (pe_wave) {
+#pragma unroll
+        for (int k = 0; k < PE_PW; ++k) copy_pe(nts, w * PE_PW + k, ln16c);
+      }
+    }
     barrier();  // probabilities and rescale factors of every head are published
     __builtin_amdgcn_sched_barrier(0);
 
@@ -394,47 +406,30 @@ void decode_latent_kernel(DecodeArgs a) {
   for (int n = 0; n < NW; ++n) inv[n] = lds_read_f32(lds0 + kAlphaOff + (16 * n + hl) * 4);
 
   // Each wave holds its C columns for all H heads.  Per 16-head block, stage
-  // the block in a private LDS region of the (idle) tile ring, chunk slots
-  // XOR-swizzled by row, and store whole row segments of C columns.
-  const uint32_t stage = lds0 + (uint32_t)w * (uint32_t)(C * 64);
-  if (final_out) {
-    constexpr int RC = C / 8;                  // 16-byte chunks per bf16 row
-    constexpr uint32_t SWZ = RC >= 16 ? 15u : (uint32_t)(RC - 1);
+  // the bf16 rows in a private LDS region of the (idle) tile ring, chunk slots
+  // XOR-swizzled by row, and store whole row segments of C columns: to o_lat
+  // (one split) or to the split's bf16 partial rows.
+  uint16_t* const out_rows = final_out ? a.o_lat + (size_t)b * a.num_heads * kDc
+                                       : a.o_part + ((size_t)b * a.num_splits + split) * a.num_heads * kDc;
+  const uint32_t stage = lds0 + (uint32_t)w * (uint32_t)(C * 32);
+  constexpr int RC = C / 8;                  // 16-byte chunks per bf16 row
+  constexpr uint32_t SWZ = RC >= 16 ? 15u : (uint32_t)(RC - 1);
 #pragma unroll
-    for (int n = 0; n < NW; ++n) {
+  for (int n = 0; n < NW; ++n) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        // columns 16 cb + 4 g4 .. +3 -> 8 bytes at chunk 2 cb + g4/2, half g4 % 2
-        const u32x2 v = {pack_bf16x2(o[cb][n][0] * inv[n], o[cb][n][1] * inv[n]),
-                         pack_bf16x2(o[cb][n][2] * inv[n], o[cb][n][3] * inv[n])};
-        const uint32_t chunk = ((uint32_t)(2 * cb + (g4 >> 1))) ^ ((uint32_t)hl & SWZ);
-        lds_write_b64(stage + hl * (uint32_t)(2 * C) + (chunk << 4) + ((g4 & 1) << 3), v);
-      }
-#pragma unroll
-      for (int k = 0; k < (16 * RC) / 64; ++k) {
-        const uint32_t L = (uint32_t)(64 * k + lane);
-        const uint32_t row = L / RC, ch = L % RC;
-        const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
-        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + 16 * n + row) * kDc + col0 + ch * 8) = v;
-      }
+    for (int cb = 0; cb < CB; ++cb) {
+      // columns 16 cb + 4 g4 .. +3 -> 8 bytes at chunk 2 cb + g4/2, half g4 % 2
+      const u32x2 v = {pack_bf16x2(o[cb][n][0] * inv[n], o[cb][n][1] * inv[n]),
+                       pack_bf16x2(o[cb][n][2] * inv[n], o[cb][n][3] * inv[n])};
+      const uint32_t chunk = ((uint32_t)(2 * cb + (g4 >> 1))) ^ ((uint32_t)hl & SWZ);
+      lds_write_b64(stage + hl * (uint32_t)(2 * C) + (chunk << 4) + ((g4 & 1) << 3), v);
     }
-  } else {
-    constexpr int RC = C / 4;                  // 16-byte chunks per fp32 row
-    float* part = a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads) * kDc;
 #pragma unroll
-    for (int n = 0; n < NW; ++n) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t chunk = ((uint32_t)(4 * cb + g4)) ^ (uint32_t)hl;
-        lds_write_f32x4(stage + hl * (uint32_t)(4 * C) + (chunk << 4), o[cb][n] * inv[n]);
-      }
-#pragma unroll
-      for (int k = 0; k < (16 * RC) / 64; ++k) {
-        const uint32_t L = (uint32_t)(64 * k + lane);
-        const uint32_t row = L / RC, ch = L % RC;
-        const f32x4 v = lds_read_f32x4(stage + row * (uint32_t)(4 * C) + ((ch ^ (row & 15u)) << 4));
-        *reinterpret_cast<f32x4*>(part + (size_t)(16 * n + row) * kDc + col0 + ch * 4) = v;
-      }
+    for (int k = 0; k < (16 * RC) / 64; ++k) {
+      const uint32_t L = (uint32_t)(64 * k + lane);
+      const uint32_t row = L / RC, ch = L % RC;
+      const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
+      *reinterpret_cast<u32x4*>(out_rows + (size_t)(16 * n + row) * kDc + col0 + ch * 8) = v;
     }
   }
 }

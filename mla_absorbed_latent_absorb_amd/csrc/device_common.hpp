@@ -45,14 +45,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t byte_off) {
 
 // Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4, scalar
 // base + 32-bit per-lane offset).  Lane i reads sbase + voff and writes bytes
-// [lds_base + 16*i, +16).  lds_base and sbase must be wave-uniform.  It is
-// issued through inline asm so the compiler does not add a conservative
+// [lds_base + 16*i, +16).  lds_base and sbase must be wave-uniform (lds_base is
+// moved to a scalar register here even where the compiler cannot prove it).
+// It is issued through inline asm so the compiler does not add a conservative
 // vmcnt(0) before every later LDS read; completion is tracked explicitly with
 // wait_vmcnt() followed by a workgroup barrier.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds_base), "v"(voff), "s"(sbase)
+               : "s"(m0), "v"(voff), "s"(sbase)
                : "memory");
 }
 

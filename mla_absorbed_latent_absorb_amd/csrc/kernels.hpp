@@ -25,7 +25,7 @@ struct DecodeArgs {
   int32_t max_seq_len;
   float scale;                // softmax scale
   float scale_log2;           // softmax scale * log2(e)
-  float* o_part;              // [B, P, H, 512] fp32 (P > 1)
+  uint16_t* o_part;           // [B, P, H, 512] bf16 (P > 1)
   float* lse_part;            // [B, P, H] fp32 (P > 1)
   uint16_t* o_lat;            // [B, H, 512] bf16 (P == 1)
   float* lse;                 // [B, H] fp32 (P == 1)
@@ -40,7 +40,7 @@ struct ProjArgs {
 };
 
 struct CombineArgs {
-  const float* o_part;   // [B, P, H, 512]
+  const uint16_t* o_part; // [B, P, H, 512] bf16
   const float* lse_part; // [B, P, H]
   uint16_t* o_lat;       // [B, H, 512]
   float* lse;            // [B, H] or null

@@ -150,7 +150,7 @@ mla_status mla_expand_v(const mla_dims* dims, const void* o_lat, const void* w_u
   return launch_result(mla::launch_expand_v(a, static_cast<hipStream_t>(stream)), where);
 }
 
-mla_status mla_combine_splits(const mla_dims* dims, const float* o_part, const float* lse_part, int32_t num_splits,
+mla_status mla_combine_splits(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,
                               void* o_lat, float* lse, void* stream) {
   const char* where = "mla_combine_splits";
   mla_status st = check_dims(dims, where);
@@ -161,13 +161,13 @@ mla_status mla_combine_splits(const mla_dims* dims, const float* o_part, const f
   REQUIRE_PTR(o_lat, "o_lat", where);
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
     return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
-  mla::CombineArgs a{o_part, lse_part, static_cast<uint16_t*>(o_lat), lse, dims->batch, dims->num_heads,
+  mla::CombineArgs a{static_cast<const uint16_t*>(o_part), lse_part, static_cast<uint16_t*>(o_lat), lse, dims->batch, dims->num_heads,
                      num_splits};
   return launch_result(mla::launch_combine(a, static_cast<hipStream_t>(stream)), where);
 }
 
 mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
-                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, float* o_part,
+                             const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_part,
                              float* lse_part, void* o_lat, float* lse, void* stream) {
   const char* where = "mla_decode_latent";
   mla_status st = check_dims(dims, where);
@@ -236,7 +236,7 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   a.max_seq_len = max_seq_len;
   a.scale = dims->softmax_scale;
   a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
-  a.o_part = o_part;
+  a.o_part = static_cast<uint16_t*>(o_part);
   a.lse_part = lse_part;
   a.o_lat = static_cast<uint16_t*>(o_lat);
   a.lse = lse;

@@ -257,7 +257,7 @@ def random_latent_queries(batch, heads, seed, device="cpu"):
 
 def random_partials(batch, splits, heads, seed, device="cpu", empty_fraction=0.25):
     """Split-KV partial results for testing the combine step in isolation:
-    o_part [B, P, H, 512] float32 ~ N(0,1), lse_part [B, P, H] float32
+    o_part [B, P, H, 512] bfloat16 ~ N(0,1), lse_part [B, P, H] float32
     ~ N(0, 4) with about `empty_fraction` of the (b, p) slots set to -inf
     (an empty token range); slot p = 0 is never empty."""
     dev = torch.device(device)
@@ -270,4 +270,4 @@ def random_partials(batch, splits, heads, seed, device="cpu", empty_fraction=0.2
     empty[:, 0] = False
     lse = torch.where(empty.unsqueeze(-1), torch.full_like(lse, -math.inf), lse)
     o = torch.where(empty.unsqueeze(-1).unsqueeze(-1), torch.zeros_like(o), o)
-    return o, lse
+    return o.to(torch.bfloat16), lse

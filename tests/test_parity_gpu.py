@@ -33,7 +33,7 @@ def _inputs(workload, **kw):
 # mla_absorb_q / mla_expand_v
 # ---------------------------------------------------------------------------
 
-PROJ_CASES = [(1, 16), (5, 16), (64, 16), (3, 32), (17, 64), (32, 128), (128, 128)]
+PROJ_CASES = [(1, 16), (5, 16), (64, 16), (3, 32), (17, 64), (32, 128), (128, 128), (130, 64), (200, 16)]
 
 
 @pytest.mark.parametrize("B,H", PROJ_CASES)
@@ -129,7 +129,7 @@ def test_decode_latent_splits_and_combine(workload, H, B, T, P):
     args = cache_args(x)
     lens = x.seq_lens.cpu().numpy()
     q64, qpe64 = f64(q_lat), f64(x.q_pe)
-    o_part_h, lse_part_h = o_part.cpu().numpy(), lse_part.cpu().numpy()
+    o_part_h, lse_part_h = f64(o_part), lse_part.cpu().numpy()
     for b in range(B):
         slots = oracle.token_slots(b, int(lens[b]), args["seq_stride"], args["block_table"], args["block_size"])
         c, k_r = oracle.load_rows(args["kv_codes"], args["pe_codes"], slots, args["dtype"], args["token_scale"])
