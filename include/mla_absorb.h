@@ -93,7 +93,8 @@ typedef struct mla_dims {
  *     slot = block_table[b * max_blocks_per_seq + t / block_size]
  *              * block_size + t % block_size                      (paged)
  * Its 512 latent elements start at kv + slot * kv_stride and its 64 RoPE-key
- * elements at pe + slot * pe_stride (strides in elements).  A fused
+ * elements at pe + slot * pe_stride (strides in elements; multiples of 16
+ * bytes: 8 bf16 or 16 E4M3 elements, else MLA_ERR_BUFFER).  A fused
  * [.., 576] row layout is kv = base, pe = base + 512, both strides 576.
  * The RoPE half holds keys that are already rotated.
  *
@@ -167,7 +168,11 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  *           by its own softmax sum) and lse_part (device fp32 [B, P, H]); an
  *           empty split gets o = 0 and lse = -inf.  o_lat / lse must be NULL;
  *           merge with mla_combine_splits.
- * fp8 caches are not built yet (MLA_ERR_UNSUPPORTED).
+ * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): each tile of cached rows
+ * is decoded (value = e4m3(code) * token_scale[slot], in fp32) and rounded to
+ * bf16 before the same bf16 matrix products as a bf16 cache; the queries stay
+ * bf16.  token_scale must then be non-NULL (4-byte aligned), else
+ * MLA_ERR_NULL; a bf16 cache must pass token_scale = NULL (MLA_ERR_BUFFER).
  */
 mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
                              const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,

@@ -33,27 +33,32 @@
 
 namespace mla {
 
-template <int NW, int NBUF, bool PAGED, bool COPY_AT_BARRIER = false>
+template <int NW, int NBUF, bool PAGED, bool FP8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_latent_kernel(DecodeArgs a) {
   constexpr int H = NW * 16;
-  // Tile copies: CW copy waves each copy KV_PW latent rows; the 4 RoPE copies
-  // (8 rows each) go to copy waves 0..3 (or are shared evenly among fewer).
-  // COPY_AT_BARRIER: only waves 0 .. NW/2-1 copy, all at once just before the
-  // mid-tile barrier, where they otherwise wait for the other half (the
-  // lower-numbered waves win the SIMD arbitration and finish their scores
-  // first); a copy that stalls at issue then delays no MFMA work.
-  static_assert(!COPY_AT_BARRIER || (NBUF > 1 && NW >= 4), "copy at the barrier needs a ring and 4+ waves");
-  constexpr int CW = COPY_AT_BARRIER ? NW / 2 : NW;  // waves that copy
-  constexpr int KV_PW = kTile / CW;       // latent rows per copy wave
-  constexpr int PE_W = CW < 4 ? CW : 4;   // waves that copy RoPE rows
+  // bf16 tile copies: each wave copies KV_PW latent rows; the 4 RoPE copies
+  // (8 rows each) go to waves 0..3 (or are shared evenly among fewer).
+  constexpr int KV_PW = kTile / NW;       // latent rows per wave
+  constexpr int PE_W = NW < 4 ? NW : 4;   // waves that copy RoPE rows
   constexpr int PE_PW = 4 / PE_W;         // RoPE copies per such wave
   constexpr int CB = 32 / NW;             // 16-column blocks of O owned by a wave
   constexpr int C = 512 / NW;             // latent columns owned by a wave
-  static_assert(kTile % CW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
-  // LDS: tile ring, then the probability exchange (one 1 KiB fragment per
-  // wave), the per-head rescale factors / reciprocal sums, and the flags.
-  constexpr int kRing = NBUF * kTileBytes;
+  static_assert(kTile % NW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
+  // E4M3 tiles (FP8): the raw tile (latent rows, RoPE rows, per-token scales)
+  // streams into a ring of raw buffers and is expanded once per tile into a
+  // single bf16 tile in the layout the bf16 path reads.  Copies per wave and
+  // tile: KV8 latent copies (2 rows each) plus E8 extras (RoPE halves, the
+  // scales, or a dummy copy so that every wave issues the same number).
+  constexpr int KV8 = 16 / NW;
+  constexpr int E8 = (3 + NW - 1) / NW;
+  constexpr int kCopies8 = KV8 + E8;
+  static_assert(!FP8 || NBUF > 1, "the E4M3 path uses a ring of raw tiles");
+  // LDS: tile ring (bf16 tiles, or raw tiles plus one bf16 tile), then the
+  // probability exchange (one 1 KiB fragment per wave), the per-head rescale
+  // factors / reciprocal sums, and the flags.
+  constexpr int kBf16Off = FP8 ? ((NBUF * kRawTileBytes + 1023) / 1024) * 1024 : 0;
+  constexpr int kRing = kBf16Off + (FP8 ? kTileBytes : NBUF * kTileBytes);
   constexpr int kPOff = kRing;
   constexpr int kAlphaOff = kPOff + NW * 1024;
   constexpr int kFlagOff = kAlphaOff + H * 4;
@@ -134,7 +139,7 @@ void decode_latent_kernel(DecodeArgs a) {
     } else {
       ts.slot0 = (int64_t)b * a.seq_stride + t0;
     }
-    ts.dst = lds0 + buf * kTileBytes;
+    ts.dst = lds0 + buf * (FP8 ? kRawTileBytes : kTileBytes);
     return ts;
   };
   // Per-lane offsets come from the lane id (mbcnt) of the current iteration
@@ -154,22 +159,89 @@ void decode_latent_kernel(DecodeArgs a) {
   };
   // Copy k of this wave: latent row w*KV_PW + k, then (waves < PE_W) RoPE
   // copy w*PE_PW + k - KV_PW.
-  const bool copy_wave = w < CW;
   const bool pe_wave = w < PE_W;
-  const int n_copy = copy_wave ? KV_PW + (pe_wave ? PE_PW : 0) : 0;
+  const int n_copy = KV_PW + (pe_wave ? PE_PW : 0);
   auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
     if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
     else copy_pe(ts, w * PE_PW + (k - KV_PW), ln16);
   };
+
+  // E4M3 raw tile: latent row r at r*512, RoPE row r at kRawPeOff + r*64,
+  // scale of row r at kRawScaleOff + 4r.  Rows past the end re-read the last
+  // valid row (also for the scales, so no read leaves the sequence).
+  // ln = lane id.
+  auto copy8_kv = [&](const TileSrc& ts, int k, uint32_t ln) {  // latent rows 2k, 2k+1
+    const uint32_t r = (uint32_t)min(2 * k + (int)(ln >> 5), ts.last);
+    const uint32_t voff = r * (uint32_t)a.kv_sb + ((ln & 31u) << 4);
+    dma16(uniform_ptr(kv_base + ts.slot0 * a.kv_sb), voff, ts.dst + k * 1024);
+  };
+  auto copy8_pe = [&](const TileSrc& ts, int k, uint32_t ln) {  // RoPE rows 16k .. 16k+15
+    const uint32_t r = (uint32_t)min(16 * k + (int)(ln >> 2), ts.last);
+    const uint32_t voff = r * (uint32_t)a.pe_sb + ((ln & 3u) << 4);
+    dma16(uniform_ptr(pe_base + ts.slot0 * a.pe_sb), voff, ts.dst + kRawPeOff + k * 1024);
+  };
+  auto copy8_scale = [&](const TileSrc& ts, uint32_t ln, uint32_t dst_off) {  // 4 B per lane, row (l%32)
+    const uint32_t r = (uint32_t)min((int)(ln & 31u), ts.last);
+    dma4(uniform_ptr(reinterpret_cast<const char*>(a.token_scale + ts.slot0)), r * 4u, ts.dst + dst_off);
+  };
+  auto issue_copy8 = [&](const TileSrc& ts, int k, uint32_t ln) {
+    if (k < KV8) {
+      copy8_kv(ts, w * KV8 + k, ln);
+    } else {
+      const int e = w * E8 + (k - KV8);
+      if (e < 2) copy8_pe(ts, e, ln);
+      else copy8_scale(ts, ln, e == 2 ? kRawScaleOff : kRawDummyOff);
+    }
+  };
+
   auto issue_tile = [&](int tile, int buf) {
-    if (!copy_wave) return;
     const TileSrc ts = tile_src(tile, buf);
+    if (FP8) {
+      const uint32_t ln = lane_id();
+#pragma unroll
+      for (int k = 0; k < kCopies8; ++k) issue_copy8(ts, k, ln);
+      return;
+    }
     const uint32_t ln16 = lane_id() << 4;
 #pragma unroll
     for (int k = 0; k < KV_PW; ++k) copy_kv(ts, w * KV_PW + k, ln16);
     if (pe_wave) {
 #pragma unroll
       for (int k = 0; k < PE_PW; ++k) copy_pe(ts, w * PE_PW + k, ln16);
+    }
+  };
+
+  // Expand raw tile `buf` into the bf16 tile: 32 rows x 72 chunks of 8
+  // elements (64 latent + 8 RoPE), each value decoded (OCP E4M3) and
+  // multiplied by its token's scale, then rounded to bf16 into the swizzled
+  // bf16 layout.
+  auto expand_tile = [&](int buf) {
+    const uint32_t raw = lds0 + buf * kRawTileBytes;
+    const uint32_t bt = lds0 + kBf16Off;
+    const uint32_t ln = lane_id();
+#pragma unroll
+    for (int k0 = 0; k0 < 32 * 72; k0 += 64 * NW) {
+      const uint32_t k = (uint32_t)(k0 + 64 * w) + ln;
+      if (k < 32 * 72) {
+        const uint32_t r = k / 72u, c = k - r * 72u;
+        uint32_t src, dst;
+        if (c < 64u) {
+          src = raw + r * 512u + c * 8u;
+          dst = bt + r * kKvRow + ((c ^ kv_swizzle(r)) << 4);
+        } else {
+          src = raw + kRawPeOff + r * 64u + (c - 64u) * 8u;
+          dst = bt + kPeRegion + r * kPeRow + (((c - 64u) ^ pe_swizzle(r)) << 4);
+        }
+        const u32x2 v = lds_read_u32x2(src);
+        const float sc = lds_read_f32(raw + kRawScaleOff + r * 4u);
+        u32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
+          out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
+        }
+        lds_write_u32x4(dst, out);
+      }
     }
   };
 
@@ -225,18 +297,24 @@ void decode_latent_kernel(DecodeArgs a) {
   // score loop (one every kCopyStride steps) so the address unit drains them
   // while the MFMAs run instead of stalling the waves at the issue.
   constexpr int kCopyStride = 18 / (KV_PW + PE_PW) > 0 ? 18 / (KV_PW + PE_PW) : 1;
-  static_assert(NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18, "copies must fit in the score loop");
+  static_assert(FP8 || NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18, "copies must fit in the score loop");
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = NBUF == 1 ? 0 : it % NBUF;
     {
       // wait for this wave's copies of tile it (later tiles may stay in flight)
       const int later = NBUF > 1 ? min(NBUF - 2, n_tiles - 1 - it) : 0;
-      if (later <= 0) {
-        wait_vmcnt<0>();
-      } else if (later == 1) {
-        if (pe_wave) wait_vmcnt<KV_PW + PE_PW>(); else wait_vmcnt<KV_PW>();
+      if constexpr (FP8) {
+        if (later <= 0) wait_vmcnt<0>();
+        else if (later == 1) wait_vmcnt<kCopies8>();
+        else wait_vmcnt<(NBUF > 3 ? 2 * kCopies8 : 0)>();
       } else {
-        if (pe_wave) wait_vmcnt<(NBUF > 3 ? 2 * (KV_PW + PE_PW) : 0)>(); else wait_vmcnt<(NBUF > 3 ? 2 * KV_PW : 0)>();
+        if (later <= 0) {
+          wait_vmcnt<0>();
+        } else if (later == 1) {
+          if (pe_wave) wait_vmcnt<KV_PW + PE_PW>(); else wait_vmcnt<KV_PW>();
+        } else {
+          if (pe_wave) wait_vmcnt<(NBUF > 3 ? 2 * (KV_PW + PE_PW) : 0)>(); else wait_vmcnt<(NBUF > 3 ? 2 * KV_PW : 0)>();
+        }
       }
     }
     // Tile it is visible to all waves, and every wave has finished iteration
@@ -246,8 +324,21 @@ void decode_latent_kernel(DecodeArgs a) {
     const bool copy_next = NBUF > 1 && nxt < n_tiles;
     const TileSrc nts = tile_src(copy_next ? nxt : it, NBUF > 1 ? nxt % NBUF : 0);
     __builtin_amdgcn_sched_barrier(0);
+    if (FP8) {
+      // the raw tile of iteration it-1 was expanded then: refill its buffer,
+      // and expand tile it into the bf16 tile (free: every wave has finished
+      // iteration it-1)
+      if (copy_next) {
+        const uint32_t ln = lane_id();
+#pragma unroll
+        for (int k = 0; k < kCopies8; ++k) issue_copy8(nts, k, ln);
+      }
+      expand_tile(buf);
+      barrier();  // the bf16 tile is complete
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
-    const uint32_t tb = lds0 + buf * kTileBytes;
+    const uint32_t tb = lds0 + (FP8 ? kBf16Off : buf * kTileBytes);
     const uint32_t ln = lane_id();
     const uint32_t ln16 = ln << 4;
     const uint32_t kb0 = tb + k_base(ln);
@@ -272,7 +363,7 @@ void decode_latent_kernel(DecodeArgs a) {
         ka[(s + 2) % 3] = lds_read_b128(ad);
         kb[(s + 2) % 3] = lds_read_b128(ad + k_hi(s + 2));
       }
-      if (!COPY_AT_BARRIER && NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
+      if (!FP8 && NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
         if (copy_next && s / kCopyStride < n_copy) issue_copy(nts, s / kCopyStride, ln16);
       }
       s0 = mfma16(ka[s % 3], q[s], s0);
@@ -336,15 +427,6 @@ void decode_latent_kernel(DecodeArgs a) {
     lds_write_u32x4(lds0 + kPOff + w * 1024 + lane * 16, pk);
     if (g4 == 0) lds_write_f32(lds0 + kAlphaOff + h * 4, alpha);
     if (lane == 0) lds_write_u8(lds0 + kFlagOff + w, any_grow ? 1u : 0u);
-    if (COPY_AT_BARRIER && copy_next && copy_wave) {
-      const uint32_t ln16c = lane_id() << 4;
-#pragma unroll
-      for (int k = 0; k < KV_PW; ++k) copy_kv(nts, w * KV_PW + k, ln16c);
-      if (pe_wave) {
-#pragma unroll
-        for (int k = 0; k < PE_PW; ++k) copy_pe(nts, w * PE_PW + k, ln16c);
-      }
-    }
     barrier();  // probabilities and rescale factors of every head are published
     __builtin_amdgcn_sched_barrier(0);
 
@@ -434,23 +516,32 @@ void decode_latent_kernel(DecodeArgs a) {
   }
 }
 
-template <int NW, int NBUF>
+template <int NW, int NBUF, bool FP8>
 static hipError_t launch_nw(const DecodeArgs& a, int grid, hipStream_t stream) {
   if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((decode_latent_kernel<NW, NBUF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_latent_kernel<NW, NBUF, true, FP8>), dim3(grid), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_latent_kernel<NW, NBUF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_latent_kernel<NW, NBUF, false, FP8>), dim3(grid), dim3(NW * 64), 0, stream, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
   const int grid = a.batch * a.num_splits;
+  if (a.fp8) {
+    switch (a.num_heads) {
+      case 16: return launch_nw<1, 4, true>(a, grid, stream);
+      case 32: return launch_nw<2, 4, true>(a, grid, stream);
+      case 64: return launch_nw<4, 4, true>(a, grid, stream);
+      case 128: return launch_nw<8, 4, true>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.num_heads) {
-    case 16: return launch_nw<1, 1>(a, grid, stream);
-    case 32: return launch_nw<2, 1>(a, grid, stream);
-    case 64: return launch_nw<4, 2>(a, grid, stream);
-    case 128: return launch_nw<8, 4>(a, grid, stream);
+    case 16: return launch_nw<1, 1, false>(a, grid, stream);
+    case 32: return launch_nw<2, 1, false>(a, grid, stream);
+    case 64: return launch_nw<4, 2, false>(a, grid, stream);
+    case 128: return launch_nw<8, 4, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,6 +58,23 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory");
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane i writes
+// [lds_base + 4*i, +4).
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+// Two OCP E4M3 (e4m3fn) codes, bytes 2*HI and 2*HI+1 of a 32-bit word, to
+// fp32 (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+}
+
 // Make a pointer that is uniform in value also uniform in register class.
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

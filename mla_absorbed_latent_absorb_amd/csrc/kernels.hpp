@@ -17,6 +17,8 @@ struct DecodeArgs {
   const int32_t* block_table; // paged: [B, max_blocks]; null = contiguous
   int32_t block_size;
   int32_t max_blocks;
+  const float* token_scale;   // E4M3 cache: one fp32 scale per slot (else null)
+  int32_t fp8;                // cache holds OCP E4M3 codes
   const int32_t* seq_lens;    // [B]
   int32_t batch;
   int32_t num_heads;

@@ -173,20 +173,30 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   mla_status st = check_dims(dims, where);
   if (st != MLA_OK) return st;
   if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
-  if (cache->dtype == MLA_DTYPE_FP8_E4M3)
-    return fail(MLA_ERR_UNSUPPORTED, "fp8 cache not built yet (mla_cache.dtype, %s)", where);
-  if (cache->dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  if (cache->dtype != MLA_DTYPE_BF16 && cache->dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  // 16-byte copies: row strides must be multiples of 16 bytes
+  const int64_t stride_align = fp8 ? 16 : 8;
   REQUIRE_PTR(cache->kv, "mla_cache.kv", where);
   REQUIRE_PTR(cache->pe, "mla_cache.pe", where);
   REQUIRE_PTR(q_lat, "q_lat", where);
   REQUIRE_PTR(q_pe, "q_pe", where);
   if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
-  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % 8 != 0)
-    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of 8 elements (%s)",
-                (long long)cache->kv_stride, dims->kv_lora_rank, where);
-  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % 8 != 0)
-    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of 8 elements (%s)",
-                (long long)cache->pe_stride, dims->qk_rope_head_dim, where);
+  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->kv_stride, dims->kv_lora_rank, (long long)stride_align, where);
+  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->pe_stride, dims->qk_rope_head_dim, (long long)stride_align, where);
+  if (fp8) {
+    if (cache->token_scale == nullptr)
+      return fail(MLA_ERR_NULL, "mla_cache.token_scale is NULL (E4M3 cache needs one fp32 scale per slot, %s)", where);
+    if (reinterpret_cast<uintptr_t>(cache->token_scale) % 4 != 0)
+      return fail(MLA_ERR_ALIGN, "mla_cache.token_scale is not 4-byte aligned (%s)", where);
+  } else if (cache->token_scale != nullptr) {
+    return fail(MLA_ERR_BUFFER, "mla_cache.token_scale must be NULL for a bf16 cache (%s)", where);
+  }
   if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
   if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
   if ((int64_t)dims->batch * num_splits > (int64_t)1 << 30)
@@ -222,8 +232,10 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.kv = static_cast<const char*>(cache->kv);
   a.pe = static_cast<const char*>(cache->pe);
-  a.kv_sb = cache->kv_stride * 2;
-  a.pe_sb = cache->pe_stride * 2;
+  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
+  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
+  a.token_scale = cache->token_scale;
+  a.fp8 = fp8 ? 1 : 0;
   a.seq_stride = cache->seq_stride;
   a.block_table = cache->block_table;
   a.block_size = cache->block_size;

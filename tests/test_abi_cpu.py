@@ -101,7 +101,12 @@ def test_decode_latent_validation(lib):
         return binding.MlaCache(**c)
 
     assert _decode(lib, d, None) == 1
-    assert _decode(lib, d, cache(dtype=1)) == 3 and "fp8" in lib.mla_last_error().decode()
+    # E4M3 cache: needs the per-slot scales and 16-byte row strides; bf16 takes no scales
+    assert _decode(lib, d, cache(dtype=1)) == 1 and "token_scale" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(dtype=1, token_scale=4098)) == 6 and "token_scale" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(dtype=1, token_scale=4096, kv_stride=520)) == 5
+    assert _decode(lib, d, cache(token_scale=4096)) == 5 and "token_scale" in lib.mla_last_error().decode()
+    assert _decode(lib, d, cache(dtype=2)) == 3 and "dtype" in lib.mla_last_error().decode()
     assert _decode(lib, d, cache(kv=None)) == 1
     assert _decode(lib, d, cache(kv=1032)) == 6
     assert _decode(lib, d, cache(kv_stride=500)) == 5 and "kv_stride" in lib.mla_last_error().decode()
