@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), V3 H=128 B=32 S=4096"
+METRIC_OTHER = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), {}"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_latent_v3_b32_s4096_hbm_counters.json")
 KERNEL_SOURCES = ["mla_absorbed_latent_absorb_amd/csrc/decode_latent.hip",
                   "mla_absorbed_latent_absorb_amd/csrc/tile_layout.hpp",
@@ -97,6 +98,75 @@ def cpu_baseline(x, target_s=10.0):
                       f"{os.cpu_count()} host CPUs visible)"}
 
 
+COPY_ELEMS = 1 << 28          # float32 elements of the calibration copy (1 GiB each way)
+PMC_COMMANDS = [
+    "export TMPDIR=/tmp",
+    "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $PWD/gpurun_out/pmc_fetch -o run --output-format csv "
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline",
+    "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $PWD/gpurun_out/pmc_write -o run --output-format csv "
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline",
+    "python bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
+    "gpurun_out/pmc_write/run_counter_collection.csv",
+]
+
+
+def _counter_means(path, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3
+    counter_collection.csv (FETCH_SIZE / WRITE_SIZE are KiB per dispatch)."""
+    import csv
+    acc = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            k = row["Kernel_Name"]
+            n, t = acc.get(k, (0, 0.0))
+            acc[k] = (n + 1, t + float(row["Counter_Value"]))
+    return {k: (t / n, n) for k, (n, t) in acc.items()}
+
+
+def _pick(means, pattern):
+    hits = [(k, v) for k, v in means.items() if pattern in k]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one kernel matching {pattern!r} in the counter file, found {len(hits)}")
+    return hits[0]
+
+
+def summarize_counters(args, fetch_csv, write_csv):
+    """HBM bytes per decode launch = counter KiB x 1024, each counter scaled by
+    (known bytes / counter reading) of the calibration copy kernel."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    name, (dec_f, n_f) = _pick(fetch, "decode_latent_kernel")
+    _, (dec_w, n_w) = _pick(write, "decode_latent_kernel")
+    _, (cp_f, _) = _pick(fetch, "neg_kernel")
+    _, (cp_w, _) = _pick(write, "neg_kernel")
+    copy_kib = COPY_ELEMS * 4 / 1024
+    rs, ws = copy_kib / cp_f, copy_kib / cp_w
+    rd, wr = dec_f * rs * 1024, dec_w * ws * 1024
+    out = {
+        "kernel": name,
+        "workload": args.workload,
+        "kernel_source_hash": kernel_source_hash(),
+        "decode_fetch_kib_per_launch": round(dec_f, 1),
+        "decode_write_kib_per_launch": round(dec_w, 1),
+        "launches": [n_f, n_w],
+        "copy_fetch_kib": round(cp_f, 1),
+        "copy_write_kib": round(cp_w, 1),
+        "copy_known_kib": copy_kib,
+        "read_scale": round(rs, 4),
+        "write_scale": round(ws, 4),
+        "hbm_read_bytes_per_launch": int(rd),
+        "hbm_write_bytes_per_launch": int(wr),
+        "hbm_bytes_per_launch": int(rd + wr),
+        "commands": PMC_COMMANDS,
+    }
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,8 +177,16 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+                    help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
+                         "for the HBM byte counters")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM byte counter file from two rocprofv3 --pmc runs of "
+                         "'bench.py --copy-calibration' (FETCH_SIZE, then WRITE_SIZE) and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args, *args.summarize_counters)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -126,10 +204,10 @@ def main():
     binding.load()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.empty(COPY_ELEMS, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)  # one elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
 
@@ -205,7 +283,7 @@ def main():
     traffic = traffic_from_counters(cache_bytes)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "v3_b32_s4096" else METRIC_OTHER.format(wl.description),
         "value": round(gbs_step, 2),
         "unit": "GB/s",
         "n_gpus": 1,
