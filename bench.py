@@ -34,6 +34,7 @@ METRIC = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), V3 H=128 B=32 S=4096
 METRIC_OTHER = "MLA decode latent-KV GB/s + TFLOP/s (% roofline), {}"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_latent_v3_b32_s4096_hbm_counters.json")
 KERNEL_SOURCES = ["mla_absorbed_latent_absorb_amd/csrc/decode_latent.hip",
+                  "mla_absorbed_latent_absorb_amd/csrc/decode_latent_wide.hip",
                   "mla_absorbed_latent_absorb_amd/csrc/tile_layout.hpp",
                   "mla_absorbed_latent_absorb_amd/csrc/device_common.hpp"]
 

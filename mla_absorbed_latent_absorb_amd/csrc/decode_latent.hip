@@ -538,10 +538,10 @@ hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
     }
   }
   switch (a.num_heads) {
+    case 128: return launch_decode_latent_wide(a, stream);
     case 16: return launch_nw<1, 1, false>(a, grid, stream);
     case 32: return launch_nw<2, 1, false>(a, grid, stream);
     case 64: return launch_nw<4, 2, false>(a, grid, stream);
-    case 128: return launch_nw<8, 4, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,614 @@
+// Latent attention of absorbed-MLA decode on gfx950 for 128 heads: 32-head
+// waves, one wave per SIMD, with the P.V product of one cache tile woven into
+// the score MFMAs of the next.
+//
+// Same computation as decode_latent.hip ("DeepSeek MLA 吸收式缓存：真实权重执行与
+// FlashMLA 架构边界" §2.2-§2.4, §6.1: every head scores the shared 576-wide
+// cache rows, online softmax, o[h] = sum_t p c_t over the 512 latent
+// columns), with a different work split and schedule.
+//
+// One workgroup per (sequence, split), 4 waves, one per SIMD, each with the
+// SIMD's whole register file (256 VGPRs + 256 AGPRs).
+//   - Tiles of 32 cache rows stream from HBM into LDS with 16-byte
+//     direct-to-LDS copies: the 32 latent rows (32 KiB) into a ring of NBUF
+//     buffers, the 32 RoPE rows (4 KiB) into a ring of NBUF - 1 buffers (a
+//     tile's RoPE rows are dead once it is scored, one step before its latent
+//     rows, which P.V still reads).
+//   - The query block reaches the registers through LDS: whole 1 KiB rows are
+//     copied direct-to-LDS (coalesced), then read back in the MFMA operand
+//     layout.  Loaded straight into that layout, every load instruction would
+//     touch 16 rows, which the address path serves at a fraction of the rate.
+//   - Scores: wave w owns heads 32w .. 32w+31.  Per 32-wide k-step it runs
+//     four independent 16x16x32 MFMAs (2 token halves x 2 head halves) with
+//     its 32 x 576 query block in VGPRs as the B operand: every K fragment
+//     read from LDS feeds 32 heads, half the LDS traffic of 16-head waves.
+//   - P.V: wave w accumulates O^T[c][head] for latent columns [128w, 128w+128)
+//     and all 128 heads in 32x32x16 tiles: 256 accumulators in AGPRs.  The
+//     bf16 probabilities of every head go through LDS in the B-operand layout.
+//   - Schedule: iteration k runs, in one instruction stream, the 72 score
+//     MFMAs of tile k+1 and the 32 P.V MFMAs of tile k (independent work, so
+//     the LDS latency of either is covered by the other's matrix work), then
+//     the online softmax of tile k+1, whose probabilities, rescale factors and
+//     flags go to the other half of double-buffered LDS slots.  One workgroup
+//     barrier per tile.
+//   - The running max of a head moves only when it grows by more than
+//     2^kRescaleLog2 in the exp2 domain, so O is rarely rescaled.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "tile_layout.hpp"
+
+namespace mla {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Both MFMA kinds are issued as inline asm so the register classes are ours:
+// the P.V accumulators live in AGPRs ("a"), the query block, score
+// accumulators and fragments in VGPRs.  (With builtins the compiler gives
+// every MFMA accumulator of the function the same class and runs out of
+// registers.)  The hazards the compiler would cover are then ours:
+//   - a chain's first MFMA takes a literal 0 accumulator, later ones
+//     accumulate into exactly the same registers (forwarded by the matrix
+//     core);
+//   - MFMA inputs come from LDS reads, covered by the compiler's lgkmcnt waits
+//     on asm operands, and are overwritten only by later LDS reads, which
+//     return after the MFMA has read them;
+//   - VALU reads of a result wait 24 cycles after the last MFMA (drain_v /
+//     acc_fence_read); VALU writes of an accumulator precede its next MFMA by
+//     8 cycles (acc_fence_write).
+
+// 16x16x32 bf16, accumulator in VGPRs.  Lane l holds A[l%16][8*(l/16) .. +7],
+// B[8*(l/16) .. +7][l%16], D[4*(l/16) + j][l%16].
+__device__ __forceinline__ f32x4 mfma16_v_first(bf16x8 a, bf16x8 b) {
+  f32x4 d;
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ f32x4 mfma16_v(bf16x8 a, bf16x8 b, f32x4 c) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  return c;
+}
+// 32x32x16 bf16, accumulator in AGPRs.  Lane l holds A[l%32][8*(l/32) .. +7],
+// B[8*(l/32) .. +7][l%32], D[8*(j/4) + 4*(l/32) + j%4][l%32] for j = 0..15.
+__device__ __forceinline__ void mfma32_a(bf16x8 a, bf16x8 b, f32x16& c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Ordering points (volatile asm keeps its order; each names one value so the
+// compiler's own reads / copies of it stay after / before).  The first of a
+// run carries the wait states.
+__device__ __forceinline__ void drain_v(f32x4& c, bool first) {
+  if (first) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+  else asm volatile("" : "+v"(c));
+}
+__device__ __forceinline__ void acc_fence_read(f32x16& c, bool first) {
+  if (first) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+  else asm volatile("" : "+a"(c));
+}
+__device__ __forceinline__ void acc_fence_write(f32x16& c, bool last) {
+  if (last) asm volatile("s_nop 7" : "+a"(c));
+  else asm volatile("" : "+a"(c));
+}
+
+}  // namespace
+
+template <int NBUF, bool PAGED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_latent_wide_kernel(DecodeArgs a) {
+  static_assert(NBUF >= 3, "a tile's latent rows stay live for two iterations");
+  constexpr int NW = 4;                   // waves: one per SIMD
+  constexpr int H = NW * 32;              // heads
+  constexpr int NT = NW;                  // 32-head tiles (all heads)
+  constexpr int C = 512 / NW;             // latent columns owned by a wave in P.V
+  constexpr int CT = C / 32;              // their 32-column tiles
+  constexpr int KV_PW = kTile / NW;       // latent rows copied per wave and tile
+  constexpr int PE_PW = 4 / NW;           // RoPE copies (8 rows each) per wave
+  constexpr int kCopies = KV_PW + PE_PW;  // copies per wave and tile
+  constexpr int NPE = NBUF - 1;           // RoPE ring length
+  constexpr int kLatBytes = kTile * kKvRow;
+  constexpr int kPeBytes = kTile * kPeRow;
+  constexpr int kPeRing = 0;                    // RoPE ring, then the latent ring
+  constexpr int kLatRing = kPeRing + NPE * kPeBytes;
+  constexpr int kPBuf = NW * 2048;              // one tile's probabilities, [head tile][k-step] 1 KiB
+  constexpr int kPOff = kLatRing + NBUF * kLatBytes;
+  constexpr int kAlphaOff = kPOff + 2 * kPBuf;  // [2][H] rescale factors, then 1/l
+  constexpr int kFlagOff = kAlphaOff + 2 * H * 4;  // [2][8] byte per wave: its softmax rescaled
+  constexpr int kSmem = kFlagOff + 64;
+  static_assert(kSmem <= 160 * 1024, "LDS budget");
+  // query staging (prologue only): per wave 16 latent rows (16 KiB) + 16
+  // RoPE rows (2 KiB), from latent buffer 2 on (latent buffers 2 .. 3 and
+  // the probability slots, all unused until tile 2 is issued)
+  constexpr int kQStage = kLatRing + 2 * kLatBytes;
+  constexpr int kQWave = 16 * 1024 + 2048;
+  static_assert(NBUF == 4 && kQStage + NW * kQWave <= kAlphaOff, "query staging must fit before the factors");
+  static_assert(NW * 32 * C * 2 <= kPOff, "epilogue staging must fit in the rings");
+  static_assert(kLatBytes % 1024 == 0 && kPeBytes % 1024 == 0 && kLatRing % 1024 == 0 && kPOff % 1024 == 0,
+                "buffers must stay 1 KiB aligned");
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  // score / softmax layout (16x16 tiles): head 32w + 16 hh + h16, tokens
+  // 16 th + 4 q4 + j
+  const int h16 = lane & 15;
+  const int q4 = lane >> 4;
+  // P.V / output layout (32x32 tiles): head 32 n + h32, columns 8 (j/4) + 4 g2 + j%4
+  const int h32 = lane & 31;
+  const int g2 = lane >> 5;
+  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
+  const int b = item / a.num_splits;
+  const int split = item - b * a.num_splits;
+  const int col0 = w * C;  // first latent column of the wave's P.V share
+
+  int T = a.seq_lens[b];
+  T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
+  const int t_begin = split * a.chunk;
+  const int t_end = min(T, t_begin + a.chunk);
+  const bool final_out = a.num_splits == 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  uint16_t* const out_rows = final_out ? a.o_lat + (size_t)b * a.num_heads * kDc
+                                       : a.o_part + ((size_t)b * a.num_splits + split) * a.num_heads * kDc;
+  float* const lse_out = final_out ? a.lse + (size_t)b * a.num_heads
+                                   : a.lse_part + ((size_t)b * a.num_splits + split) * a.num_heads;
+
+  if (t_begin >= t_end) {
+    // No tokens in this range: zero weight (o = 0, lse = -inf).
+    for (int r = 0; r < 32; ++r)
+      *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * w + r) * kDc + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+    if (g2 == 0) lse_out[32 * w + h32] = -INFINITY;
+    return;
+  }
+
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  const char* kv_base = uniform_ptr(a.kv);
+  const char* pe_base = uniform_ptr(a.pe);
+
+  // ---- tile copies (HBM -> LDS, 16 B per lane, rows swizzled by chunk) ----
+  struct TileSrc {
+    int64_t slot0;    // cache slot of the tile's first token
+    int last;         // last valid row (rows past it re-read it)
+    uint32_t lat;     // LDS latent buffer
+    uint32_t pe;      // LDS RoPE buffer
+  };
+  auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NBUF) * kLatBytes; };
+  auto pe_buf = [&](int tile) -> uint32_t { return lds0 + kPeRing + (uint32_t)(tile % NPE) * kPeBytes; };
+  auto tile_src = [&](int tile) -> TileSrc {
+    const int t0 = t_begin + tile * kTile;
+    TileSrc ts;
+    ts.last = min(kTile, t_end - t0) - 1;
+    if (PAGED) {
+      // scalar load: a vector load would make the compiler wait for every
+      // tile copy in flight before using it
+      const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+          reinterpret_cast<uintptr_t>(a.block_table));
+      const int blk = table[(size_t)b * a.max_blocks + t0 / a.block_size];
+      ts.slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
+    } else {
+      ts.slot0 = (int64_t)b * a.seq_stride + t0;
+    }
+    ts.lat = lat_buf(tile);
+    ts.pe = pe_buf(tile);
+    return ts;
+  };
+  // ln16 = 16 * lane from the lane id of the current step (not kept live: a
+  // spilled value's scratch reload would wait for every copy in flight).
+  auto copy_kv = [&](const TileSrc& ts, int r, uint32_t ln16) {  // latent row r
+    const int64_t slot = ts.slot0 + min(r, ts.last);
+    dma16(uniform_ptr(kv_base + slot * a.kv_sb), ln16 ^ (kv_swizzle(r) << 4), ts.lat + r * kKvRow);
+  };
+  auto copy_pe = [&](const TileSrc& ts, int i, uint32_t ln16) {  // RoPE rows 8i .. 8i+7
+    const uint32_t r = 8 * i + (ln16 >> 7);
+    const uint32_t c = ((ln16 >> 4) & 7u) ^ pe_swizzle(r);
+    const uint32_t voff = (uint32_t)min((int)r, ts.last) * (uint32_t)a.pe_sb + (c << 4);
+    dma16(uniform_ptr(pe_base + ts.slot0 * a.pe_sb), voff, ts.pe + i * 1024);
+  };
+  auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
+    if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
+    else copy_pe(ts, w * PE_PW + (k - KV_PW), ln16);
+  };
+  auto issue_tile = [&](int tile) {
+    const TileSrc ts = tile_src(tile);
+    const uint32_t ln16 = lane_id() << 4;
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) issue_copy(ts, k, ln16);
+  };
+
+  // ---- prologue ----
+  // Copies in issue order: tile 0, query half 0 (heads 32w .. 32w+15), tile
+  // 1, query half 1; each query half is read back as soon as it has landed,
+  // and tile 2 goes into the staging area once every wave is done with it.
+  const uint32_t qstage = lds0 + kQStage + (uint32_t)w * kQWave;
+  // Query half hh: latent row of head j (0..15) at qstage + 1024 j with
+  // chunk c at slot c ^ j; RoPE rows of heads 8i .. 8i+7 at qstage + 16 KiB +
+  // 1024 i, head j's chunk k at slot 8 (j % 8) + (k ^ ((j / 2) % 8)).  Both
+  // make the 16 rows that one fragment read touches land in 16 bank slots.
+  auto stage_q = [&](int hh) {
+    const size_t head0 = (size_t)b * a.num_heads + 32 * w + 16 * hh;
+    const uint32_t ln = lane_id();
+    const char* ql = uniform_ptr(reinterpret_cast<const char*>(a.q_lat + head0 * kDc));
+    const char* qr = uniform_ptr(reinterpret_cast<const char*>(a.q_pe + head0 * kDr));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dma16(ql + j * (kDc * 2), (ln ^ (uint32_t)j) << 4, qstage + j * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t j = 8 * i + (ln >> 3);
+      dma16(qr, j * (kDr * 2) + (((ln & 7u) ^ ((j >> 1) & 7u)) << 4), qstage + 16384 + i * 1024);
+    }
+  };
+  // q[s][hh]: head 32w + 16 hh + h16, elements 32 s + 8 q4 .. +7 (s < 16
+  // latent, s = 16, 17 RoPE): the B operand of the score MFMAs
+  bf16x8 q[18][2];
+  auto read_q = [&](int hh) {
+    const uint32_t ln = lane_id();
+    const uint32_t j = ln & 15u, qq = ln >> 4;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) q[s][hh] = lds_read_b128(qstage + j * 1024 + (((4 * s + qq) ^ j) << 4));
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      q[16 + s][hh] = lds_read_b128(qstage + 16384 + (j >> 3) * 1024 + ((j & 7u) * 8 + ((4 * s + qq) ^ ((j >> 1) & 7u))) * 16);
+    // the reads are complete before the staging area is overwritten
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  issue_tile(0);
+  stage_q(0);
+  if (n_tiles > 1) {
+    issue_tile(1);
+    wait_vmcnt<kCopies>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  read_q(0);
+  stage_q(1);
+  wait_vmcnt<0>();
+  read_q(1);
+  barrier();  // every wave has read its query block: the staging area is free
+  if (NBUF > 3 && n_tiles > 2) issue_tile(2);
+
+  // ---- per-lane LDS addresses inside a tile ----
+  // The swizzles XOR only the 16-byte chunk index and buffers are 1 KiB
+  // aligned, so each fragment address is a per-lane base XOR a step constant
+  // plus an immediate offset.
+  //   K fragment of score step s, token half th: row 16 th + l%16, latent
+  //   chunk 4 s + l/16 = 16 m + ((l/16 ^ swz) ^ 4 s4) for s = 4 m + s4 < 16;
+  //   steps 16, 17: RoPE chunk 4 (s-16) + l/16.  Row r + 16 has the swizzle of r.
+  auto k_addr_fn = [&](uint32_t kb0, uint32_t pb0, int s) -> uint32_t {
+    if (s < 16) return (kb0 ^ ((uint32_t)(s & 3) << 6)) + 256u * (uint32_t)(s >> 2);
+    return pb0 ^ ((uint32_t)(s - 16) << 6);
+  };
+  auto k_hi = [&](int s) -> uint32_t { return s < 16 ? 16u * kKvRow : 16u * kPeRow; };
+  //   V^T fragment (column tile ct, k-step kk): the 16-lane group l/16 reads
+  //   rows 16 kk + 8 (l/32) + (l%16)/4 (and + 4), columns col0 + 32 ct +
+  //   16 ((l/16) % 2) + 4 (l%4) .. +3; lane l receives column col0 + 32 ct +
+  //   l%32 of those 4 rows (transposing read).  The chunk is
+  //   (col0/8 + 2 ((l/16)%2) + (l%4)/2) XOR 4 ct, col0/8 a multiple of 16.
+  auto v_base = [&](uint32_t l, uint32_t roff) -> uint32_t {
+    const uint32_t r = 8 * (l >> 5) + ((l & 15u) >> 2) + roff;
+    const uint32_t chunk = (uint32_t)(col0 >> 3) | (((l >> 4) & 1u) << 1) | ((l & 3u) >> 1);
+    return r * kKvRow + ((chunk ^ kv_swizzle(r)) << 4) + ((l & 1u) << 3);
+  };
+
+  f32x16 o[CT][NT];  // o[ct][n][j] = O^T[col0 + 32 ct + 8 (j/4) + 4 g2 + j%4][32 n + h32]
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[ct][n][j] = 0.f;
+      acc_fence_write(o[ct][n], ct == CT - 1 && n == NT - 1);
+    }
+  // softmax state of the lane's two heads 32w + 16 hh + h16 (the four lanes
+  // with the same h16 hold the same reference max)
+  float m_ref[2] = {-INFINITY, -INFINITY};  // reference max of the raw scores q.k
+  float l_sum[2] = {0.f, 0.f};              // this lane's share of sum_t exp2((s - m_ref) c2)
+  const float c2 = a.scale_log2;
+
+  // Wait for this wave's copies of tile k, leaving at most `younger_max`
+  // younger tiles in flight.
+  auto wait_tile = [&](int k, int younger_max) {
+    const int later = min(younger_max, n_tiles - 1 - k);
+    if (later <= 0) wait_vmcnt<0>();
+    else if (later == 1) wait_vmcnt<kCopies>();
+    else wait_vmcnt<(NBUF > 3 ? 2 * kCopies : 0)>();
+  };
+  static_assert(kCopies <= 9, "one copy every other score step");
+
+  typedef f32x4 Scores[2][2];  // [token half th][head half hh]
+
+  // P.V operands, kept across iterations (see `iteration`): probability
+  // fragments of the four head tiles, V^T fragments of three column tiles.
+  bf16x8 pf[NT], va[3];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) pf[n] = bf16x8{};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) va[i] = bf16x8{};
+  // P.V MFMA m: k-step m / 16, column tile (m / 4) % 4, head tile m % 4
+  auto pv_mfma = [&](int m) {
+    const int vi = m >> 2, ct = vi & 3, n = m & 3;
+    mfma32_a(va[vi % 3], pf[n], o[ct][n]);
+  };
+
+  // One iteration of the pipeline as a single instruction stream:
+  //   - 18 score steps: the four score MFMAs of k-step s of tile tq (into sc),
+  //     then (DO_PV) P.V MFMA m = s - 1 of tile tv, then the K reads of step
+  //     s + 2, the operand reads of later P.V MFMAs, and on odd steps one of
+  //     this wave's copies of tile `nts` (after the MFMAs, so a copy waiting
+  //     for the address unit overlaps matrix work);
+  //   - 8 softmax stages for the scores just computed, behind the P.V MFMAs
+  //     m = 17 .. 27, so part of the VALU work runs in the matrix core's
+  //     shadow.  The probabilities, rescale factors and flags go to slot ps;
+  //     the running max and sum change only if commit;
+  //   - P.V MFMAs 28 .. 31 are issued at the start of the next iteration (or
+  //     after the loop), where they cover the latency of its first LDS reads.
+  //     Their operands stay in pf / va, which live across iterations and start
+  //     as zeros, so the deferred MFMAs of the first iteration add zeros.
+  //   P.V MFMA m: k-step kk = m / 16 (tokens 16 kk .. +15), column tile
+  //   ct = (m / 4) % 4, head tile n = m % 4, with the probabilities of slot
+  //   pb.  The V^T fragment of (kk, ct) is read two column tiles ahead; the
+  //   four probability fragments of k-step 0 are replaced by those of k-step
+  //   1 right after their last use (m = 12 .. 15).
+  //   Before the steps (DO_PV and rescale_check), after the deferred MFMAs of
+  //   tile tv - 1: O *= alpha of slot pb if any wave's softmax of tile tv moved
+  //   its reference max.
+  auto iteration = [&](auto pv_tag, int tq, Scores& sc, int tv, int pb, int ps, bool rescale_check,
+                       bool commit, bool copy_next, const TileSrc& nts) {
+    constexpr bool DO_PV = decltype(pv_tag)::value;
+    const uint32_t ln = lane_id();
+    const uint32_t ln16 = ln << 4;
+    const uint32_t r16 = ln & 15u;
+    uint32_t flags = 0u;
+    if (DO_PV && rescale_check) flags = lds_read_u32(lds0 + kFlagOff + pb * 8);  // one byte per wave
+    const uint32_t kb0 = lat_buf(tq) + r16 * kKvRow + (((ln >> 4) ^ kv_swizzle(r16)) << 4);
+    const uint32_t pb0 = pe_buf(tq) + r16 * kPeRow + (((ln >> 4) ^ pe_swizzle(r16)) << 4);
+    uint32_t va0 = 0, va4 = 0;
+    const uint32_t pbase = lds0 + kPOff + (uint32_t)pb * kPBuf + ln16;
+    if (DO_PV) {
+      const uint32_t tb = lat_buf(tv);
+      va0 = tb + v_base(ln, 0);
+      va4 = tb + v_base(ln, 4);
+    }
+    auto va_load = [&](int vi) -> bf16x8 {  // vi = 4 kk + ct
+      const int ct = vi & 3, kk = vi >> 2;
+      const uint32_t x = (uint32_t)ct << 6;
+      const bf16x4 lo = lds_read_tr16((va0 ^ x) + (uint32_t)kk * 16u * kKvRow);
+      const bf16x4 hi = lds_read_tr16((va4 ^ x) + (uint32_t)kk * 16u * kKvRow);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto pf_load = [&](int n, int kk) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, lds_read_u32x4(pbase + (uint32_t)(n * 2 + kk) * 1024u));
+    };
+    constexpr int D = 2;  // score steps of K fragments in flight
+    bf16x8 kf[D + 1][2];
+#pragma unroll
+    for (int st = 0; st < D; ++st) {
+      const uint32_t ad = k_addr_fn(kb0, pb0, st);
+      kf[st][0] = lds_read_b128(ad);
+      kf[st][1] = lds_read_b128(ad + k_hi(st));
+    }
+    if (DO_PV) {
+#pragma unroll
+      for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the previous tile
+#pragma unroll
+      for (int n = 0; n < NT; ++n) pf[n] = pf_load(n, 0);
+      va[0] = va_load(0);
+      va[1] = va_load(1);
+      if (flags != 0u) {  // rare after the first tile
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float al = lds_read_f32(lds0 + kAlphaOff + (uint32_t)pb * (H * 4) + (32 * n + h32) * 4);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            acc_fence_read(o[ct][n], n == 0 && ct == 0);
+            o[ct][n] *= al;
+            acc_fence_write(o[ct][n], n == NT - 1 && ct == CT - 1);
+          }
+        }
+      }
+    }
+    // P.V MFMA m (m < 28) and the operand reads that follow it
+    auto pv = [&](int m) {
+      if (!DO_PV || m >= 28) return;
+      pv_mfma(m);
+      const int vi = m >> 2, n = m & 3;
+      if ((m & 3) == 0 && vi + 2 < 8) va[(vi + 2) % 3] = va_load(vi + 2);
+      if (m >= 12 && m < 16) pf[n] = pf_load(n, 1);
+    };
+
+#pragma unroll
+    for (int st = 0; st < 18; ++st) {
+#pragma unroll
+      for (int th = 0; th < 2; ++th)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          sc[th][hh] = st == 0 ? mfma16_v_first(kf[0][th], q[0][hh])
+                               : mfma16_v(kf[st % (D + 1)][th], q[st][hh], sc[th][hh]);
+      if (st >= 1) pv(st - 1);
+      if (st + D < 18) {
+        const uint32_t ad = k_addr_fn(kb0, pb0, st + D);
+        kf[(st + D) % (D + 1)][0] = lds_read_b128(ad);
+        kf[(st + D) % (D + 1)][1] = lds_read_b128(ad + k_hi(st + D));
+      }
+      if ((st & 1) == 1 && (st >> 1) < kCopies) {
+        if (copy_next) issue_copy(nts, st >> 1, ln16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- online softmax of tile tq, woven with P.V MFMAs 17 .. 31 ----
+    Scores& sp = sc;
+    const int nvalid = min(kTile, t_end - (t_begin + tq * kTile));
+    float mx[2], m_new[2], alpha[2], mb[2];
+    bool any_grow = false;
+#pragma unroll
+    for (int stage = 0; stage < 8; ++stage) {
+      pv(17 + 2 * stage);
+      pv(18 + 2 * stage);
+      if (stage == 0) {
+        drain_v(sp[0][0], true);
+        drain_v(sp[0][1], false);
+        drain_v(sp[1][0], false);
+        drain_v(sp[1][1], false);
+        if (nvalid < kTile) {  // ragged tail: tokens 16 th + 4 q4 + j at or past nvalid
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (16 * th + 4 * q4 + j >= nvalid) sp[th][hh][j] = -INFINITY;
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          mx[hh] = fmaxf(fmaxf(fmaxf(sp[0][hh][0], sp[0][hh][1]), fmaxf(sp[0][hh][2], sp[0][hh][3])),
+                         fmaxf(fmaxf(sp[1][hh][0], sp[1][hh][1]), fmaxf(sp[1][hh][2], sp[1][hh][3])));
+      } else if (stage == 1) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) mx[hh] = max_xor32(max_xor16(mx[hh]));
+      } else if (stage == 2) {
+        bool grow = false;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          m_new[hh] = fmaxf(m_ref[hh], mx[hh]);
+          grow = grow || (m_new[hh] - m_ref[hh]) * c2 > kRescaleLog2;
+        }
+        any_grow = __ballot(grow) != 0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float ex = fast_exp2((m_ref[hh] - m_new[hh]) * c2);
+          alpha[hh] = any_grow ? ex : 1.0f;
+          const float m_use = any_grow ? m_new[hh] : m_ref[hh];
+          mb[hh] = m_use * c2;
+          if (commit) m_ref[hh] = m_use;
+        }
+      } else if (stage == 3 || stage == 4) {
+        const int th = stage - 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sp[th][hh][j] = fast_exp2(fmaf(sp[th][hh][j], c2, -mb[hh]));
+      } else if (stage == 5) {
+        // B operand of P.V (k-step th of head tile w): lane h' + 32 g' holds
+        // tokens 16 th + 8 g' + i; this lane's 4 tokens 16 th + 4 q4 + j are
+        // elements 4 (q4 % 2) + j of lane (16 hh + h16) + 32 (q4 / 2)
+        const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u;
+#pragma unroll
+        for (int th = 0; th < 2; ++th)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x2 pk = {pack_bf16x2(sp[th][hh][0], sp[th][hh][1]), pack_bf16x2(sp[th][hh][2], sp[th][hh][3])};
+            const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
+            lds_write_b64(pw + (uint32_t)th * 1024u + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
+          }
+      } else if (stage == 6) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float psum = ((sp[0][hh][0] + sp[0][hh][1]) + (sp[0][hh][2] + sp[0][hh][3])) +
+                             ((sp[1][hh][0] + sp[1][hh][1]) + (sp[1][hh][2] + sp[1][hh][3]));
+          const float nl = fmaf(l_sum[hh], alpha[hh], psum);
+          if (commit) l_sum[hh] = nl;
+        }
+        if (q4 == 0) {
+          const uint32_t ab = lds0 + kAlphaOff + (uint32_t)ps * (H * 4);
+          lds_write_f32(ab + (32 * w + h16) * 4, alpha[0]);
+          lds_write_f32(ab + (32 * w + 16 + h16) * 4, alpha[1]);
+        }
+        if (lane == 0) lds_write_u8(lds0 + kFlagOff + ps * 8 + w, any_grow ? 1u : 0u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Pipeline.  Before the loop: scores and softmax of tile 0 (slot 0).
+  // Iteration k, after barrier A (tile k+1 landed; every wave's probabilities
+  // of tile k are in slot k%2; every wave is done with iteration k-1, so the
+  // latent buffer of tile k-1 and the RoPE buffer of tile k are free and the
+  // copies of tile k + NBUF - 1 go there): the P.V of tile k woven with the
+  // scores and softmax of tile k+1 into slot (k+1)%2 (whose previous
+  // contents, tile k-1's, were consumed in iteration k-1).  The last tile has
+  // no successor: its own rows are scored again and that softmax is not
+  // committed (one code path keeps the registers allocated once).
+  const TileSrc no_copy = {0, 0, 0u, 0u};
+  Scores sc;
+  wait_tile(0, NBUF - 2);
+  barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, false, no_copy);
+  for (int it = 0; it < n_tiles; ++it) {
+    const bool has_next = it + 1 < n_tiles;
+    if (has_next) wait_tile(it + 1, NBUF - 3);
+    barrier();  // barrier A
+    __builtin_amdgcn_sched_barrier(0);
+    const int nxt = it + NBUF - 1;
+    const bool copy_next = nxt < n_tiles;
+    const TileSrc nts = tile_src(copy_next ? nxt : it);
+    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next,
+              copy_next, nts);
+  }
+#pragma unroll
+  for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the last tile
+
+  // ---- finalize: normalise by the per-head sum and store ----
+  float l_tot[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) l_tot[hh] = sum_xor32(sum_xor16(l_sum[hh]));
+  barrier();  // every wave is done with the tiles and the rescale factors
+  if (q4 == 0) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int hd = 32 * w + 16 * hh + h16;
+      lds_write_f32(lds0 + kAlphaOff + hd * 4, 1.0f / l_tot[hh]);
+      lse_out[hd] = m_ref[hh] * a.scale + __logf(l_tot[hh]);
+    }
+  }
+  barrier();
+  float inv[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) inv[n] = lds_read_f32(lds0 + kAlphaOff + (32 * n + h32) * 4);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc_fence_read(o[ct][n], ct == 0 && n == 0);
+
+  // Per 32-head tile, stage the wave's C columns of the 32 rows in a private
+  // region of the latent ring (16-byte chunk slots XOR-swizzled by row) and
+  // store whole row segments.
+  constexpr int RC = C / 8;                 // 16-byte chunks per bf16 row segment
+  constexpr uint32_t SWZ = RC >= 16 ? 15u : (uint32_t)(RC - 1);
+  const uint32_t stage = lds0 + (uint32_t)w * (uint32_t)(32 * C * 2);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // columns 32 ct + 8 jj + 4 g2 .. +3 of head row h32: 8 bytes at chunk
+        // 4 ct + jj, half g2
+        const u32x2 v = {pack_bf16x2(o[ct][n][4 * jj + 0] * inv[n], o[ct][n][4 * jj + 1] * inv[n]),
+                         pack_bf16x2(o[ct][n][4 * jj + 2] * inv[n], o[ct][n][4 * jj + 3] * inv[n])};
+        const uint32_t chunk = ((uint32_t)(4 * ct + jj)) ^ ((uint32_t)h32 & SWZ);
+        lds_write_b64(stage + (uint32_t)h32 * (uint32_t)(2 * C) + (chunk << 4) + ((uint32_t)g2 << 3), v);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < (32 * RC) / 64; ++k) {
+      const uint32_t L = (uint32_t)(64 * k + lane);
+      const uint32_t row = L / RC, ch = L % RC;
+      const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
+      *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v;
+    }
+  }
+}
+
+hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_heads != 128 || a.fp8) return hipErrorInvalidValue;
+  const int grid = a.batch * a.num_splits;
+  if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -52,6 +52,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
+// 128 heads, bf16 cache: 32-head waves with P.V woven into the next tile's scores.
+hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
