@@ -92,6 +92,15 @@ __device__ __forceinline__ void acc_fence_write(f32x16& c, bool last) {
   else asm volatile("" : "+a"(c));
 }
 
+// XOR swizzle of the 16-byte chunk index of latent row r in an LDS tile.
+// Chosen by measurement (rocprofv3 SQ_LDS_BANK_CONFLICT on this kernel's two
+// read patterns, over 34 candidate swizzles): the score K fragment read (16
+// consecutive rows, one chunk each, 1 KiB apart) is free of bank conflicts,
+// and the transposing V^T read (4 consecutive rows x 4 adjacent chunks) costs
+// 2 extra cycles per instruction.  No candidate made both free; the K reads
+// are twice as many.  A bijection of r % 16 that touches the chunk bits only.
+__device__ __forceinline__ uint32_t lat_swizzle(uint32_t r) { return ((r & 1u) << 3) | ((r >> 1) & 7u); }
+
 }  // namespace
 
 template <int NBUF, bool PAGED>
@@ -167,7 +176,8 @@ void decode_latent_wide_kernel(DecodeArgs a) {
 
   // ---- tile copies (HBM -> LDS, 16 B per lane, rows swizzled by chunk) ----
   struct TileSrc {
-    int64_t slot0;    // cache slot of the tile's first token
+    const char* kv0;  // latent row of the tile's first token (rows of a tile share a page)
+    const char* pe0;  // its RoPE row
     int last;         // last valid row (rows past it re-read it)
     uint32_t lat;     // LDS latent buffer
     uint32_t pe;      // LDS RoPE buffer
@@ -178,31 +188,36 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     const int t0 = t_begin + tile * kTile;
     TileSrc ts;
     ts.last = min(kTile, t_end - t0) - 1;
+    int64_t slot0;
     if (PAGED) {
       // scalar load: a vector load would make the compiler wait for every
       // tile copy in flight before using it
       const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
           reinterpret_cast<uintptr_t>(a.block_table));
       const int blk = table[(size_t)b * a.max_blocks + t0 / a.block_size];
-      ts.slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
+      slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
     } else {
-      ts.slot0 = (int64_t)b * a.seq_stride + t0;
+      slot0 = (int64_t)b * a.seq_stride + t0;
     }
+    ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
+    ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
     ts.lat = lat_buf(tile);
     ts.pe = pe_buf(tile);
     return ts;
   };
   // ln16 = 16 * lane from the lane id of the current step (not kept live: a
   // spilled value's scratch reload would wait for every copy in flight).
+  // Row offsets inside a tile fit 32 bits (token strides are below 2^24 bytes).
+  const uint32_t kv_sb32 = (uint32_t)a.kv_sb, pe_sb32 = (uint32_t)a.pe_sb;
   auto copy_kv = [&](const TileSrc& ts, int r, uint32_t ln16) {  // latent row r
-    const int64_t slot = ts.slot0 + min(r, ts.last);
-    dma16(uniform_ptr(kv_base + slot * a.kv_sb), ln16 ^ (kv_swizzle(r) << 4), ts.lat + r * kKvRow);
+    const uint32_t roff = (uint32_t)min(r, ts.last) * kv_sb32;
+    dma16(ts.kv0 + roff, ln16 ^ (lat_swizzle(r) << 4), ts.lat + r * kKvRow);
   };
   auto copy_pe = [&](const TileSrc& ts, int i, uint32_t ln16) {  // RoPE rows 8i .. 8i+7
     const uint32_t r = 8 * i + (ln16 >> 7);
     const uint32_t c = ((ln16 >> 4) & 7u) ^ pe_swizzle(r);
-    const uint32_t voff = (uint32_t)min((int)r, ts.last) * (uint32_t)a.pe_sb + (c << 4);
-    dma16(uniform_ptr(pe_base + ts.slot0 * a.pe_sb), voff, ts.pe + i * 1024);
+    const uint32_t voff = (uint32_t)min((int)r, ts.last) * pe_sb32 + (c << 4);
+    dma16(ts.pe0, voff, ts.pe + i * 1024);
   };
   auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
     if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
@@ -286,7 +301,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   auto v_base = [&](uint32_t l, uint32_t roff) -> uint32_t {
     const uint32_t r = 8 * (l >> 5) + ((l & 15u) >> 2) + roff;
     const uint32_t chunk = (uint32_t)(col0 >> 3) | (((l >> 4) & 1u) << 1) | ((l & 3u) >> 1);
-    return r * kKvRow + ((chunk ^ kv_swizzle(r)) << 4) + ((l & 1u) << 3);
+    return r * kKvRow + ((chunk ^ lat_swizzle(r)) << 4) + ((l & 1u) << 3);
   };
 
   f32x16 o[CT][NT];  // o[ct][n][j] = O^T[col0 + 32 ct + 8 (j/4) + 4 g2 + j%4][32 n + h32]
@@ -329,37 +344,40 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     mfma32_a(va[vi % 3], pf[n], o[ct][n]);
   };
 
-  // One iteration of the pipeline as a single instruction stream:
-  //   - 18 score steps: the four score MFMAs of k-step s of tile tq (into sc),
-  //     then (DO_PV) P.V MFMA m = s - 1 of tile tv, then the K reads of step
-  //     s + 2, the operand reads of later P.V MFMAs, and on odd steps one of
-  //     this wave's copies of tile `nts` (after the MFMAs, so a copy waiting
-  //     for the address unit overlaps matrix work);
-  //   - 8 softmax stages for the scores just computed, behind the P.V MFMAs
-  //     m = 17 .. 27, so part of the VALU work runs in the matrix core's
-  //     shadow.  The probabilities, rescale factors and flags go to slot ps;
-  //     the running max and sum change only if commit;
+  // One iteration of the pipeline as a single instruction stream.  A wave
+  // issues in order and an MFMA holds the issue until the matrix core takes
+  // it, so other work overlaps the matrix core only when it sits between two
+  // MFMAs: the stream alternates single MFMAs with single other operations
+  // (sched_barrier keeps the source order).
+  //   - Score phase, 18 steps: the four score MFMAs of k-step s of tile tq
+  //     (into sc), separated by the two K reads of step s + 2 and two more
+  //     slots: on odd steps one of this wave's copies of tile `nts`; in the
+  //     first steps the operand reads of the first P.V MFMAs of tile tv.
+  //   - P.V phase: P.V MFMAs m = 0 .. 27 of tile tv with the probabilities of
+  //     slot pb, each followed by the operand reads it makes due and one chunk
+  //     of the online softmax of the scores just computed.  The softmax writes
+  //     the probabilities, rescale factors and flags of slot ps; the running
+  //     max and sum change only if commit.
   //   - P.V MFMAs 28 .. 31 are issued at the start of the next iteration (or
   //     after the loop), where they cover the latency of its first LDS reads.
   //     Their operands stay in pf / va, which live across iterations and start
   //     as zeros, so the deferred MFMAs of the first iteration add zeros.
   //   P.V MFMA m: k-step kk = m / 16 (tokens 16 kk .. +15), column tile
-  //   ct = (m / 4) % 4, head tile n = m % 4, with the probabilities of slot
-  //   pb.  The V^T fragment of (kk, ct) is read two column tiles ahead; the
-  //   four probability fragments of k-step 0 are replaced by those of k-step
-  //   1 right after their last use (m = 12 .. 15).
-  //   Before the steps (DO_PV and rescale_check), after the deferred MFMAs of
-  //   tile tv - 1: O *= alpha of slot pb if any wave's softmax of tile tv moved
-  //   its reference max.
+  //   ct = (m / 4) % 4, head tile n = m % 4.  The V^T fragment of (kk, ct) is
+  //   read two column tiles ahead; the four probability fragments of k-step 0
+  //   are replaced by those of k-step 1 right after their last use.
+  //   After the deferred MFMAs of tile tv - 1 (DO_PV and rescale_check):
+  //   O *= alpha of slot pb if any wave's softmax of tile tv moved its
+  //   reference max.
   auto iteration = [&](auto pv_tag, int tq, Scores& sc, int tv, int pb, int ps, bool rescale_check,
                        bool commit, bool copy_next, const TileSrc& nts) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
     const uint32_t ln = lane_id();
     const uint32_t ln16 = ln << 4;
     const uint32_t r16 = ln & 15u;
-    uint32_t flags = 0u;
-    if (DO_PV && rescale_check) flags = lds_read_u32(lds0 + kFlagOff + pb * 8);  // one byte per wave
-    const uint32_t kb0 = lat_buf(tq) + r16 * kKvRow + (((ln >> 4) ^ kv_swizzle(r16)) << 4);
+    // one byte per wave; read now, tested after the deferred MFMAs
+    const uint32_t flags = DO_PV ? lds_read_u32(lds0 + kFlagOff + pb * 8) : 0u;
+    const uint32_t kb0 = lat_buf(tq) + r16 * kKvRow + (((ln >> 4) ^ lat_swizzle(r16)) << 4);
     const uint32_t pb0 = pe_buf(tq) + r16 * kPeRow + (((ln >> 4) ^ pe_swizzle(r16)) << 4);
     uint32_t va0 = 0, va4 = 0;
     const uint32_t pbase = lds0 + kPOff + (uint32_t)pb * kPBuf + ln16;
@@ -386,14 +404,14 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       kf[st][0] = lds_read_b128(ad);
       kf[st][1] = lds_read_b128(ad + k_hi(st));
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (DO_PV) {
 #pragma unroll
-      for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the previous tile
-#pragma unroll
-      for (int n = 0; n < NT; ++n) pf[n] = pf_load(n, 0);
-      va[0] = va_load(0);
-      va[1] = va_load(1);
-      if (flags != 0u) {  // rare after the first tile
+      for (int m = 28; m < 32; ++m) {  // deferred from the previous tile
+        pv_mfma(m);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (rescale_check && flags != 0u) {  // rare after the first tile
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const float al = lds_read_f32(lds0 + kAlphaOff + (uint32_t)pb * (H * 4) + (32 * n + h32) * 4);
@@ -406,45 +424,45 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         }
       }
     }
-    // P.V MFMA m (m < 28) and the operand reads that follow it
-    auto pv = [&](int m) {
-      if (!DO_PV || m >= 28) return;
-      pv_mfma(m);
-      const int vi = m >> 2, n = m & 3;
-      if ((m & 3) == 0 && vi + 2 < 8) va[(vi + 2) % 3] = va_load(vi + 2);
-      if (m >= 12 && m < 16) pf[n] = pf_load(n, 1);
-    };
+    __builtin_amdgcn_sched_barrier(0);
 
+    // ---- score phase ----
+    // slot work of step st (two slots per step): this wave's copy i in the
+    // first slot of step 2i + 1, P.V operand preloads in steps 0 .. 3
+    auto slot = [&](int st, int k) {
+      if ((st & 1) == 1 && k == 0 && (st >> 1) < kCopies && copy_next) issue_copy(nts, st >> 1, ln16);
+      if (DO_PV) {
+        if (k == 0 && st < 2) pf[2 * st] = pf_load(2 * st, 0);
+        else if (k == 1 && st < 2) pf[2 * st + 1] = pf_load(2 * st + 1, 0);
+        else if (k == 1 && st == 2) va[0] = va_load(0);
+        else if (k == 1 && st == 3) va[1] = va_load(1);
+      }
+    };
 #pragma unroll
     for (int st = 0; st < 18; ++st) {
+      const uint32_t ad = st + D < 18 ? k_addr_fn(kb0, pb0, st + D) : 0u;
 #pragma unroll
-      for (int th = 0; th < 2; ++th)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          sc[th][hh] = st == 0 ? mfma16_v_first(kf[0][th], q[0][hh])
-                               : mfma16_v(kf[st % (D + 1)][th], q[st][hh], sc[th][hh]);
-      if (st >= 1) pv(st - 1);
-      if (st + D < 18) {
-        const uint32_t ad = k_addr_fn(kb0, pb0, st + D);
-        kf[(st + D) % (D + 1)][0] = lds_read_b128(ad);
-        kf[(st + D) % (D + 1)][1] = lds_read_b128(ad + k_hi(st + D));
+      for (int e = 0; e < 4; ++e) {
+        const int th = e >> 1, hh = e & 1;
+        sc[th][hh] = st == 0 ? mfma16_v_first(kf[0][th], q[0][hh])
+                             : mfma16_v(kf[st % (D + 1)][th], q[st][hh], sc[th][hh]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (e < 2) {
+          if (st + D < 18) kf[(st + D) % (D + 1)][e] = lds_read_b128(ad + (e ? k_hi(st + D) : 0u));
+        } else {
+          slot(st, e - 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if ((st & 1) == 1 && (st >> 1) < kCopies) {
-        if (copy_next) issue_copy(nts, st >> 1, ln16);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- online softmax of tile tq, woven with P.V MFMAs 17 .. 31 ----
+    // ---- P.V phase with the online softmax of tile tq ----
     Scores& sp = sc;
     const int nvalid = min(kTile, t_end - (t_begin + tq * kTile));
-    float mx[2], m_new[2], alpha[2], mb[2];
+    float mx[2], alpha[2], mb[2];
     bool any_grow = false;
-#pragma unroll
-    for (int stage = 0; stage < 8; ++stage) {
-      pv(17 + 2 * stage);
-      pv(18 + 2 * stage);
-      if (stage == 0) {
+    auto softmax_chunk = [&](int c) {
+      if (c == 0) {
         drain_v(sp[0][0], true);
         drain_v(sp[0][1], false);
         drain_v(sp[1][0], false);
@@ -458,15 +476,19 @@ void decode_latent_wide_kernel(DecodeArgs a) {
               for (int j = 0; j < 4; ++j)
                 if (16 * th + 4 * q4 + j >= nvalid) sp[th][hh][j] = -INFINITY;
         }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          mx[hh] = fmaxf(fmaxf(fmaxf(sp[0][hh][0], sp[0][hh][1]), fmaxf(sp[0][hh][2], sp[0][hh][3])),
-                         fmaxf(fmaxf(sp[1][hh][0], sp[1][hh][1]), fmaxf(sp[1][hh][2], sp[1][hh][3])));
-      } else if (stage == 1) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) mx[hh] = max_xor32(max_xor16(mx[hh]));
-      } else if (stage == 2) {
+      } else if (c == 1 || c == 2) {
+        const int hh = c - 1;
+        mx[hh] = fmaxf(fmaxf(fmaxf(sp[0][hh][0], sp[0][hh][1]), fmaxf(sp[0][hh][2], sp[0][hh][3])),
+                       fmaxf(fmaxf(sp[1][hh][0], sp[1][hh][1]), fmaxf(sp[1][hh][2], sp[1][hh][3])));
+      } else if (c == 3) {
+        mx[0] = max_xor16(mx[0]);
+        mx[1] = max_xor16(mx[1]);
+      } else if (c == 4) {
+        mx[0] = max_xor32(mx[0]);
+        mx[1] = max_xor32(mx[1]);
+      } else if (c == 5) {
         bool grow = false;
+        float m_new[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           m_new[hh] = fmaxf(m_ref[hh], mx[hh]);
@@ -481,33 +503,32 @@ void decode_latent_wide_kernel(DecodeArgs a) {
           mb[hh] = m_use * c2;
           if (commit) m_ref[hh] = m_use;
         }
-      } else if (stage == 3 || stage == 4) {
-        const int th = stage - 3;
+      } else if (c >= 6 && c < 14) {
+        // two of the lane's 16 probabilities per chunk
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sp[th][hh][j] = fast_exp2(fmaf(sp[th][hh][j], c2, -mb[hh]));
-      } else if (stage == 5) {
+        for (int x = 0; x < 2; ++x) {
+          const int e = 2 * (c - 6) + x, th = e >> 3, hh = (e >> 2) & 1, j = e & 3;
+          sp[th][hh][j] = fast_exp2(fmaf(sp[th][hh][j], c2, -mb[hh]));
+        }
+      } else if (c == 14 || c == 15) {
         // B operand of P.V (k-step th of head tile w): lane h' + 32 g' holds
         // tokens 16 th + 8 g' + i; this lane's 4 tokens 16 th + 4 q4 + j are
         // elements 4 (q4 % 2) + j of lane (16 hh + h16) + 32 (q4 / 2)
-        const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u;
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x2 pk = {pack_bf16x2(sp[th][hh][0], sp[th][hh][1]), pack_bf16x2(sp[th][hh][2], sp[th][hh][3])};
-            const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
-            lds_write_b64(pw + (uint32_t)th * 1024u + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
-          }
-      } else if (stage == 6) {
+        const int th = c - 14;
+        const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u + (uint32_t)th * 1024u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const float psum = ((sp[0][hh][0] + sp[0][hh][1]) + (sp[0][hh][2] + sp[0][hh][3])) +
-                             ((sp[1][hh][0] + sp[1][hh][1]) + (sp[1][hh][2] + sp[1][hh][3]));
-          const float nl = fmaf(l_sum[hh], alpha[hh], psum);
-          if (commit) l_sum[hh] = nl;
+          const u32x2 pk = {pack_bf16x2(sp[th][hh][0], sp[th][hh][1]), pack_bf16x2(sp[th][hh][2], sp[th][hh][3])};
+          const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
+          lds_write_b64(pw + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
         }
+      } else if (c == 16 || c == 17) {
+        const int hh = c - 16;
+        const float psum = ((sp[0][hh][0] + sp[0][hh][1]) + (sp[0][hh][2] + sp[0][hh][3])) +
+                           ((sp[1][hh][0] + sp[1][hh][1]) + (sp[1][hh][2] + sp[1][hh][3]));
+        const float nl = fmaf(l_sum[hh], alpha[hh], psum);
+        if (commit) l_sum[hh] = nl;
+      } else if (c == 18) {
         if (q4 == 0) {
           const uint32_t ab = lds0 + kAlphaOff + (uint32_t)ps * (H * 4);
           lds_write_f32(ab + (32 * w + h16) * 4, alpha[0]);
@@ -515,6 +536,17 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         }
         if (lane == 0) lds_write_u8(lds0 + kFlagOff + ps * 8 + w, any_grow ? 1u : 0u);
       }
+    };
+#pragma unroll
+    for (int m = 0; m < 28; ++m) {
+      if (DO_PV) {
+        pv_mfma(m);
+        __builtin_amdgcn_sched_barrier(0);
+        const int vi = m >> 2, n = m & 3;
+        if ((m & 3) == 0 && vi + 2 < 8) va[(vi + 2) % 3] = va_load(vi + 2);
+        if (m >= 12 && m < 16) pf[n] = pf_load(n, 1);
+      }
+      softmax_chunk(m);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -528,7 +560,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // contents, tile k-1's, were consumed in iteration k-1).  The last tile has
   // no successor: its own rows are scored again and that softmax is not
   // committed (one code path keeps the registers allocated once).
-  const TileSrc no_copy = {0, 0, 0u, 0u};
+  const TileSrc no_copy = {nullptr, nullptr, 0, 0u, 0u};
   Scores sc;
   wait_tile(0, NBUF - 2);
   barrier();

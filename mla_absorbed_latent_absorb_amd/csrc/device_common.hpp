@@ -49,10 +49,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t byte_off) {
 // moved to a scalar register here even where the compiler cannot prove it).
 // It is issued through inline asm so the compiler does not add a conservative
 // vmcnt(0) before every later LDS read; completion is tracked explicitly with
-// wait_vmcnt() followed by a workgroup barrier.
+// wait_vmcnt() followed by a workgroup barrier.  An SALU write of M0 needs one
+// wait state before a load with LDS = 1 reads it (s_nop 0).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(sbase)
                : "memory");
@@ -62,7 +63,7 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 // [lds_base + 4*i, +4).
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(m0), "v"(voff), "s"(sbase)
                : "memory");

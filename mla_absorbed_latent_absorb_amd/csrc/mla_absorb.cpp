@@ -189,6 +189,10 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % stride_align != 0)
     return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of %lld elements (%s)",
                 (long long)cache->pe_stride, dims->qk_rope_head_dim, (long long)stride_align, where);
+  // the kernels address the rows of one 32-token tile with 32-bit offsets
+  if (cache->kv_stride > (int64_t)1 << 23 || cache->pe_stride > (int64_t)1 << 23)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld / pe_stride %lld above %lld elements (%s)",
+                (long long)cache->kv_stride, (long long)cache->pe_stride, (long long)1 << 23, where);
   if (fp8) {
     if (cache->token_scale == nullptr)
       return fail(MLA_ERR_NULL, "mla_cache.token_scale is NULL (E4M3 cache needs one fp32 scale per slot, %s)", where);
