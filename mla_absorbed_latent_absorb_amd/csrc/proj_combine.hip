@@ -6,164 +6,215 @@
 // combine : LSE = ln sum_i exp(lse_i); o = sum_i exp(lse_i - LSE) o_i
 //
 // Both projections are per-head batched GEMMs that are bound by reading the
-// weights once (16 MiB each for 128 heads).  They are computed transposed,
-// D^T[column][batch] = W^T . X^T with 16x16x32 bf16 MFMAs, so a lane ends up
-// with four consecutive output columns of one batch row (one 8-byte store),
-// and every load a workgroup needs is issued before its first use.
+// weights once (16 MiB each for 128 heads); two workgroups per head, every
+// operand copied into LDS as whole rows, 16x16x32 bf16 MFMAs.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace mla {
 
 // ---------------------------------------------------------------------------
-// absorb_q: workgroup = (head h, 64 output columns c); wave w owns columns
-// 16 w .. 16 w + 15 of the block (the 16 rows of its D^T tiles).
-//   A[c][d] = W_UK[h][d][c]: the [128 d][64 c] slab is staged in LDS and read
-//             transposed with ds_read_b64_tr_b16 (lane l: column l%16, 8 rows).
-//   B[d][b] = q_nope[b][h][d]: 16-byte contiguous loads from global.
+// Shared layout: every operand reaches LDS through 16-byte direct-to-LDS
+// copies of whole rows (coalesced), the 16-byte chunks of row r stored at slot
+// chunk ^ swz(r) so that the fragment reads (16 rows, one chunk each) spread
+// over the banks.  Batch rows are processed in chunks of kProjRows; rows past
+// the batch re-read the last row and are not stored.
 // ---------------------------------------------------------------------------
-constexpr int kAbsorbBatchBlocks = 4;  // batch blocks of 16 whose query fragments are loaded together
+constexpr int kProjRows = 32;  // batch rows per chunk
+
+// ---------------------------------------------------------------------------
+// absorb_q: workgroup = (head h, column half ch): q_lat[b][h][256 ch + c].
+//   LDS: W_UK[h][d][256 ch .. +256] as 128 rows of 512 B (chunk ^ 2d % 32),
+//        q_nope[b][h][:] as 32 rows of 256 B (chunk ^ b % 16), and the output
+//        chunk as 32 rows of 512 B (chunk ^ b % 32) for row-wise stores.
+//   D^T[c][b] = W^T . Q^T on 16x16x32 MFMAs; wave w owns columns 64 w .. +63:
+//   A[c][d] via transposing reads of the W rows, B[d][b] from the query rows.
+// ---------------------------------------------------------------------------
+constexpr int kAbsCols = 256;                      // output columns per workgroup
+constexpr int kAbsW = kDn * kAbsCols * 2;          // 64 KiB W slab
+constexpr int kAbsQ = kProjRows * kDn * 2;         // 8 KiB query rows
+constexpr int kAbsOut = kProjRows * kAbsCols * 2;  // 16 KiB output staging
 
 __global__ __launch_bounds__(256) void absorb_q_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kDn * 64];  // 16 KiB
-  // the 8 column blocks of a head run on one XCD (shared L2 for its rows)
+  __shared__ __attribute__((aligned(1024))) char smem[kAbsW + kAbsQ + kAbsOut];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t wl = lds0, ql = lds0 + kAbsW, ol = lds0 + kAbsW + kAbsQ;
+  // both halves of a head run on one XCD (its query rows are fetched once)
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int h = item >> 3;
-  const int cblk = item & 7;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int nl = lane & 15, g = lane >> 4;
+  const int h = item >> 1, ch = item & 1;
+  const int w = wave_id();
+  const int nl = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const size_t qrow_bytes = (size_t)a.num_heads * kDn * 2;  // stride of q_nope rows
 
-  // slab rows: thread t copies 16-byte pieces k*256 + t (row piece/8, chunk piece%8)
-  const uint16_t* wsrc = a.w + (size_t)h * kDn * kDc + cblk * 64;
-  u32x4 wreg[4];
+  // W slab: copy k (16 per wave) = rows 2k, 2k+1 (lane l: row 2k + l/32, slot l % 32)
+  {
+    const uint32_t ln = lane_id();
+    const char* wsrc = reinterpret_cast<const char*>(a.w + (size_t)h * kDn * kDc + ch * kAbsCols);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = k * 256 + t;
-    wreg[k] = *reinterpret_cast<const u32x4*>(wsrc + (size_t)(idx >> 3) * kDc + (idx & 7) * 8);
+    for (int i = 0; i < 16; ++i) {
+      const int k = 16 * w + i;
+      const uint32_t row = 2 * k + (ln >> 5);
+      const uint32_t src = (ln & 31u) ^ ((2u * row) & 30u);
+      dma16(uniform_ptr(wsrc + (size_t)(2 * k) * (kDc * 2)), (ln >> 5) * (kDc * 2) + src * 16, wl + k * 1024);
+    }
   }
-  // query fragments of the first batch blocks, in flight with the slab
-  auto load_q = [&](int mb, bf16x8 (&qf)[4]) {
-    const int brow = mb * 16 + nl;
-    if (brow < a.batch) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(a.x + ((size_t)brow * a.num_heads + h) * kDn + 8 * g);
+  // query rows b0 .. b0+31: copy k (2 per wave) = rows 4k .. 4k+3 (lane l:
+  // row 4k + l/16, slot l % 16); rows past the batch re-read the last one
+  auto stage_q = [&](int b0) {
+    const uint32_t ln = lane_id();
+    const char* qbase = reinterpret_cast<const char*>(a.x + (size_t)h * kDn);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qf[s] = src[4 * s];
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int i = 0; i < 2; ++i) {
+      const int k = 2 * w + i;
+      const int r0 = min(b0 + 4 * k, a.batch - 1);
+      const uint32_t row = 4 * k + (ln >> 4);
+      const int br = min(b0 + (int)row, a.batch - 1);
+      const uint32_t src = (ln & 15u) ^ (row & 15u);
+      dma16(uniform_ptr(qbase + (size_t)r0 * qrow_bytes), (uint32_t)(br - r0) * (uint32_t)qrow_bytes + src * 16,
+            ql + k * 1024);
     }
   };
-  const int nblk = (a.batch + 15) / 16;
-  bf16x8 qf[kAbsorbBatchBlocks][4];
-#pragma unroll
-  for (int i = 0; i < kAbsorbBatchBlocks; ++i)
-    if (i < nblk) load_q(i, qf[i]);
+  stage_q(0);
+  wait_vmcnt<0>();
+  barrier();
 
+  // A fragments (column tile ct = 64 w + 16 ct, k-step s): lane (nl, g) gets
+  // W[32 s + 8 g + i][c = 64 w + 16 ct + nl], two transposing reads of 4 rows
+  bf16x8 af[4][4];
+  {
+    const uint32_t ln = lane_id();
+    const uint32_t lnl = ln & 15u, lg = ln >> 4;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = k * 256 + t;
-    *reinterpret_cast<u32x4*>(wt + (idx >> 3) * 64 + (idx & 7) * 8) = wreg[k];
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const uint32_t colb = (uint32_t)(64 * w + 16 * ct) * 2 + (lnl & 3u) * 8;  // byte in the 512 B row
+        bf16x4 half[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t row = 32 * s + 8 * lg + 4 * e + (lnl >> 2);
+          const uint32_t chunk = (colb >> 4) ^ ((2u * row) & 30u);
+          half[e] = lds_read_tr16(wl + row * 512 + (chunk << 4) + (colb & 15u));
+        }
+        af[ct][s] = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      }
   }
-  __syncthreads();
 
-  // A fragments for the 4 k-steps of 32 (d = 32 s + 8 g + i), column 16 w + nl
-  const uint32_t wbase = (uint32_t)(uintptr_t)wt;
-  bf16x8 af[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t row = 32 * s + 8 * g + (nl >> 2);
-    const uint32_t off = wbase + row * 128 + (16 * w + 4 * (nl & 3)) * 2;
-    const bf16x4 lo = lds_read_tr16(off);
-    const bf16x4 hi = lds_read_tr16(off + 4 * 128);
-    af[s] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  }
-
-  // D^T[c = 16 w + 4 g + j][b = 16 mb + nl]: four consecutive columns per lane
-  const int c0 = cblk * 64 + 16 * w + 4 * g;
-  auto emit = [&](int mb, const bf16x8 (&q)[4]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma16(af[s], q[s], acc);
-    const int bo = mb * 16 + nl;
-    if (bo < a.batch) {
-      const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-      *reinterpret_cast<u32x2*>(a.y + ((size_t)bo * a.num_heads + h) * kDc + c0) = v;
+  for (int b0 = 0; b0 < a.batch; b0 += kProjRows) {
+    if (b0 > 0) {
+      stage_q(b0);
+      wait_vmcnt<0>();
+      barrier();
     }
-  };
 #pragma unroll
-  for (int i = 0; i < kAbsorbBatchBlocks; ++i)
-    if (i < nblk) emit(i, qf[i]);
-  for (int mb = kAbsorbBatchBlocks; mb < nblk; ++mb) {
-    bf16x8 q[4];
-    load_q(mb, q);
-    emit(mb, q);
+    for (int mb = 0; mb < 2; ++mb) {
+      // B fragments: Q[b = 16 mb + nl][d = 32 s + 8 g .. +7]
+      bf16x8 bq[4];
+      const uint32_t brow = 16 * mb + nl;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bq[s] = lds_read_b128(ql + brow * 256 + (((uint32_t)(4 * s + g) ^ (brow & 15u)) << 4));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16(af[ct][s], bq[s], acc);
+        // D^T[c = 64 w + 16 ct + 4 g + j][b = 16 mb + nl] -> staging row b, 8 bytes
+        const uint32_t c = 64 * w + 16 * ct + 4 * g;
+        const uint32_t chunk = (c >> 3) ^ (brow & 31u);
+        const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        lds_write_b64(ol + brow * 512 + (chunk << 4) + (c & 7u) * 2, v);
+      }
+    }
+    barrier();
+    // 32 rows x 32 chunks of 16 B -> q_lat rows (512 contiguous bytes per row)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t idx = (uint32_t)(k * 256) + threadIdx.x;
+      const uint32_t row = idx >> 5, chunk = idx & 31u;
+      const int b = b0 + (int)row;
+      const u32x4 v = lds_read_u32x4(ol + row * 512 + ((chunk ^ (row & 31u)) << 4));
+      if (b < a.batch)
+        *reinterpret_cast<u32x4*>(a.y + ((size_t)b * a.num_heads + h) * kDc + ch * kAbsCols + chunk * 8) = v;
+    }
+    barrier();  // the query rows and the staging area are reused
   }
 }
 
 // ---------------------------------------------------------------------------
-// expand_v: workgroup = (head h, 16 output columns j); wave w reduces the
-// latent range c in [128 w, 128 w + 128) for every batch block, and the four
-// partial D^T tiles are summed through LDS.
-//   A[j][c] = W_UV[h][j][c], B[c][b] = o_lat[b][h][c]: both contiguous rows.
+// expand_v: workgroup = (head h, row half jh): out[b][h][64 jh + j].
+//   LDS: W_UV[h][64 jh .. +64][:] as 64 rows of 1 KiB (chunk ^ j % 16) and
+//        o_lat[b][h][:] as 32 rows of 1 KiB (chunk ^ b % 16).
+//   D[j][b] = W . O^T on 16x16x32 MFMAs over the 512 latent columns; wave w
+//   owns rows 16 w .. +15 of the half.
 // ---------------------------------------------------------------------------
-// NB = batch blocks per pass (at most 8: partials in LDS 32 KiB); sized to the
-// batch so small batches do not reserve registers for unused blocks.
-template <int NB>
-__global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) f32x4 red[4][NB][64];
-  // the 8 row blocks of a head run on one XCD, which then fetches the head's
-  // o_lat rows into its L2 once
-  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int h = item >> 3;
-  const int jblk = item & 7;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int cbase = 128 * w + 8 * g;
+constexpr int kExpRows = 64;                       // output rows (j) per workgroup
+constexpr int kExpW = kExpRows * kDc * 2;          // 64 KiB
+constexpr int kExpO = kProjRows * kDc * 2;         // 32 KiB
 
-  bf16x8 af[4];
+__global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kExpW + kExpO];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t wl = lds0, ol = lds0 + kExpW;
+  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
+  const int h = item >> 1, jh = item & 1;
+  const int w = wave_id();
+  const int nl = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const size_t orow_bytes = (size_t)a.num_heads * kDc * 2;
+
+  // W rows 64 jh .. +63 (contiguous 64 KiB): copy k (16 per wave) = row k
   {
-    const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * kDv + jblk * 16 + nl) * kDc + cbase);
+    const uint32_t ln = lane_id();
+    const char* wsrc = reinterpret_cast<const char*>(a.w + ((size_t)h * kDv + kExpRows * jh) * kDc);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) af[s] = wrow[4 * s];
+    for (int i = 0; i < 16; ++i) {
+      const int k = 16 * w + i;
+      dma16(uniform_ptr(wsrc + (size_t)k * (kDc * 2)), (ln ^ (uint32_t)(k & 15)) * 16, wl + k * 1024);
+    }
   }
-  const int nblk = (a.batch + 15) / 16;
-  for (int mb0 = 0; mb0 < nblk; mb0 += NB) {
-    bf16x8 bq[NB][4];
+  // o_lat rows b0 .. b0+31: copy k (8 per wave) = row k
+  auto stage_o = [&](int b0) {
+    const uint32_t ln = lane_id();
+    const char* obase = reinterpret_cast<const char*>(a.x + (size_t)h * kDc);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int brow = (mb0 + i) * 16 + nl;
-      if (mb0 + i < nblk && brow < a.batch) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(a.x + ((size_t)brow * a.num_heads + h) * kDc + cbase);
+    for (int i = 0; i < 8; ++i) {
+      const int k = 8 * w + i;
+      const int br = min(b0 + k, a.batch - 1);
+      dma16(uniform_ptr(obase + (size_t)br * orow_bytes), (ln ^ (uint32_t)(k & 15)) * 16, ol + k * 1024);
+    }
+  };
+  stage_o(0);
+  wait_vmcnt<0>();
+  barrier();
+
+  const uint32_t jrow = 16 * w + nl;  // A row of this lane
+  for (int b0 = 0; b0 < a.batch; b0 += kProjRows) {
+    if (b0 > 0) {
+      stage_o(b0);
+      wait_vmcnt<0>();
+      barrier();
+    }
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[i][s] = src[4 * s];
-      } else {
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t chunk = (uint32_t)(4 * s + g);
+      const bf16x8 aw = lds_read_b128(wl + jrow * 1024 + ((chunk ^ (jrow & 15u)) << 4));
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bq[i][s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint32_t brow = 16 * mb + nl;
+        const bf16x8 bo = lds_read_b128(ol + brow * 1024 + ((chunk ^ (brow & 15u)) << 4));
+        acc[mb] = mfma16(aw, bo, acc[mb]);
       }
     }
+    // D[j = 16 w + 4 g + r][b = 16 mb + nl]: four consecutive output columns
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (mb0 + i < nblk) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16(af[s], bq[i][s], acc);
-        red[w][i][lane] = acc;
+    for (int mb = 0; mb < 2; ++mb) {
+      const int b = b0 + 16 * mb + nl;
+      if (b < a.batch) {
+        const u32x2 v = {pack_bf16x2(acc[mb][0], acc[mb][1]), pack_bf16x2(acc[mb][2], acc[mb][3])};
+        *reinterpret_cast<u32x2*>(a.y + ((size_t)b * a.num_heads + h) * kDv + kExpRows * jh + 16 * w + 4 * g) = v;
       }
     }
-    __syncthreads();
-    // wave w finishes batch blocks i = w, w + 4: D^T[j = 4 g + r][b = 16 mb + nl]
-    for (int i = w; i < NB && mb0 + i < nblk; i += 4) {
-      const f32x4 acc = (red[0][i][lane] + red[1][i][lane]) + (red[2][i][lane] + red[3][i][lane]);
-      const int bo = (mb0 + i) * 16 + nl;
-      if (bo < a.batch) {
-        const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        *reinterpret_cast<u32x2*>(a.y + ((size_t)bo * a.num_heads + h) * kDv + jblk * 16 + 4 * g) = v;
-      }
-    }
-    __syncthreads();
+    barrier();  // the o_lat rows are reused
   }
 }
 
@@ -231,17 +282,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(a.num_heads * 8), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(a.num_heads * (kDc / kAbsCols)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream) {
-  const int nblk = (a.batch + 15) / 16;
-  const dim3 grid(a.num_heads * 8), block(256);
-  if (nblk <= 1) hipLaunchKernelGGL(expand_v_kernel<1>, grid, block, 0, stream, a);
-  else if (nblk <= 2) hipLaunchKernelGGL(expand_v_kernel<2>, grid, block, 0, stream, a);
-  else if (nblk <= 4) hipLaunchKernelGGL(expand_v_kernel<4>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(expand_v_kernel<8>, grid, block, 0, stream, a);
+  hipLaunchKernelGGL(expand_v_kernel, dim3(a.num_heads * (kDv / kExpRows)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
