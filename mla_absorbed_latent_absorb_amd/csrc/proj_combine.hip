@@ -220,9 +220,10 @@ __global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
 
 // ---------------------------------------------------------------------------
 // combine: one wave per (sequence, head); lane l handles latent columns
-// 8 l .. 8 l + 7 of the bf16 partial rows.  The split weights are formed once
-// per wave (lane i holds split i) and broadcast; all partial rows of a group
-// of 8 splits are loaded before they are accumulated.
+// 8 l .. 8 l + 7 of the bf16 partial rows.  The rows of the first 8 splits
+// and the split lse values are all requested before any of them is used (one
+// memory round trip); lane i holds split i's lse and weight, broadcast with
+// shuffles.  Splits past the first 8 (P > 8) are read in further groups of 8.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // Sequences map to XCDs the way the decode kernel's splits do, so a
@@ -234,50 +235,70 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = threadIdx.x & 63;
   const int P = a.num_splits;
   const float* lse_row = a.lse_part + (size_t)b * P * a.num_heads + h;
+  const uint16_t* prow = a.o_part + ((size_t)b * P * a.num_heads + h) * kDc + lane * 8;
+  const size_t split_stride = (size_t)a.num_heads * kDc;
 
-  float m = -INFINITY;
-  for (int i = lane; i < P; i += 64) m = fmaxf(m, lse_row[(size_t)i * a.num_heads]);
+  // issue: lse of split `lane` (lanes < P, up to 64) and the first 8 rows
+  const float li0 = lane < P ? lse_row[(size_t)lane * a.num_heads] : -INFINITY;
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < P) v[j] = *reinterpret_cast<const u32x4*>(prow + (size_t)j * split_stride);
+
+  float m = li0;
+  for (int i = 64 + lane; i < P; i += 64) m = fmaxf(m, lse_row[(size_t)i * a.num_heads]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
-  if (m != -INFINITY) {
-    const uint16_t* prow = a.o_part + ((size_t)b * P * a.num_heads + h) * kDc + lane * 8;
-    for (int i0 = 0; i0 < P; i0 += 64) {
-      // weight of split i0 + lane (0 for empty splits and lanes past P)
-      const float li = i0 + lane < P ? lse_row[(size_t)(i0 + lane) * a.num_heads] : -INFINITY;
-      const float wl = li == -INFINITY ? 0.f : __expf(li - m);
-      float ws = wl;
+  auto accumulate = [&](int i0, float wl, int n) {
 #pragma unroll
-      for (int k = 32; k >= 1; k >>= 1) ws += __shfl_xor(ws, k);
-      tot += ws;
-      const int n = min(64, P - i0);
-      for (int j0 = 0; j0 < n; j0 += 8) {
-        u32x4 v[8];
+    for (int j = 0; j < 8; ++j) {
+      if (j < n) {
+        const float wi = __shfl(wl, j);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j0 + j < n) v[j] = *reinterpret_cast<const u32x4*>(prow + (size_t)(i0 + j0 + j) * a.num_heads * kDc);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j0 + j < n) {
-            const float wi = __shfl(wl, j0 + j);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              acc0[2 * e] += wi * __uint_as_float(v[j][e] << 16);
-              acc0[2 * e + 1] += wi * __uint_as_float(v[j][e] & 0xffff0000u);
-              acc1[2 * e] += wi * __uint_as_float(v[j][2 + e] << 16);
-              acc1[2 * e + 1] += wi * __uint_as_float(v[j][2 + e] & 0xffff0000u);
-            }
-          }
+        for (int e = 0; e < 2; ++e) {
+          acc0[2 * e] += wi * __uint_as_float(v[j][e] << 16);
+          acc0[2 * e + 1] += wi * __uint_as_float(v[j][e] & 0xffff0000u);
+          acc1[2 * e] += wi * __uint_as_float(v[j][2 + e] << 16);
+          acc1[2 * e + 1] += wi * __uint_as_float(v[j][2 + e] & 0xffff0000u);
         }
       }
     }
+    (void)i0;
+  };
+  if (m != -INFINITY) {
+    // weight of split lane (0 for empty splits and lanes past P)
+    const float w0 = li0 == -INFINITY ? 0.f : __expf(li0 - m);
+    float ws = w0;
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) ws += __shfl_xor(ws, k);
+    tot = ws;
+    accumulate(0, w0, min(P, 8));
+    for (int i0 = 8; i0 < P; i0 += 8) {
+      const int n = min(8, P - i0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < n) v[j] = *reinterpret_cast<const u32x4*>(prow + (size_t)(i0 + j) * split_stride);
+      // weights of splits i0 .. i0+7 on lanes 0..7 (the lse of splits >= 64 re-read here)
+      const int si = i0 + (lane & 7);
+      const float li = si < P ? lse_row[(size_t)si * a.num_heads] : -INFINITY;
+      const float wl = li == -INFINITY ? 0.f : __expf(li - m);
+      if (i0 >= 64) {
+        // splits 64.. were not in the lane-wise total above
+        float wsum = lane < 8 && si < P ? wl : 0.f;
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1) wsum += __shfl_xor(wsum, k);
+        tot += wsum;
+      }
+      accumulate(i0, wl, n);
+    }
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-  const u32x4 v = {pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
+  const u32x4 o = {pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
                    pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
-  *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + h) * kDc + lane * 8) = v;
+  *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + h) * kDc + lane * 8) = o;
   if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.num_heads + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
 }
 

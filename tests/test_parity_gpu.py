@@ -167,7 +167,7 @@ def test_decode_latent_splits_and_combine(workload, H, B, T, P):
     assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= TOL_BF16
 
 
-@pytest.mark.parametrize("B,P,H", [(2, 3, 16), (4, 8, 128), (1, 1, 64), (3, 16, 32)])
+@pytest.mark.parametrize("B,P,H", [(2, 3, 16), (4, 8, 128), (1, 1, 64), (3, 16, 32), (2, 9, 16), (2, 70, 16), (1, 130, 32)])
 def test_combine_random_partials(B, P, H):
     announce(f"combine random partials B={B} P={P} H={H}")
     o_part, lse_part = datagen.random_partials(B, P, H, seed=31 + P, device=DEV)
