@@ -138,8 +138,8 @@ def summarize_counters(args, fetch_csv, write_csv):
     (known bytes / counter reading) of the calibration copy kernel."""
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
-    name, (dec_f, n_f) = _pick(fetch, "decode_latent_kernel")
-    _, (dec_w, n_w) = _pick(write, "decode_latent_kernel")
+    name, (dec_f, n_f) = _pick(fetch, "decode_latent")
+    _, (dec_w, n_w) = _pick(write, "decode_latent")
     _, (cp_f, _) = _pick(fetch, "neg_kernel")
     _, (cp_w, _) = _pick(write, "neg_kernel")
     copy_kib = COPY_ELEMS * 4 / 1024
