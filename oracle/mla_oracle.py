@@ -265,6 +265,95 @@ def naive_attention(q_nope, q_pe, c, k_r, w_uk, w_uv, scale):
 
 
 # ---------------------------------------------------------------------------
+# Encoding into the stored formats (used by the cache append)
+# ---------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x):
+    """float32 values -> bfloat16 bit patterns, rounded to nearest, ties to
+    the even pattern (finite inputs).
+
+    The bfloat16 values are the float32 values whose low 16 bits are zero; x
+    lies between the two bracketing ones, lo = x with the low bits cleared and
+    lo + one bf16 step, and the nearer one is taken (the even one on a tie).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lo = u & np.uint64(0xFFFF0000)
+    rem = u & np.uint64(0xFFFF)
+    half = np.uint64(0x8000)
+    up = (rem > half) | ((rem == half) & (((lo >> np.uint64(16)) & np.uint64(1)) == np.uint64(1)))
+    return ((lo >> np.uint64(16)) + up.astype(np.uint64)).astype(np.uint16)
+
+
+def e4m3fn_encode(x):
+    """Values within [-448, 448] -> OCP E4M3 codes: the nearest finite E4M3
+    value, ties to the even code (even mantissa), sign from the sign bit.
+
+    Written as a search over the 127 non-negative finite codes, which are
+    increasing in value (e4m3fn_to_f64 gives the grid).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > 448.0) or np.any(np.isnan(x)):
+        raise ValueError("e4m3fn_encode expects finite values within [-448, 448]")
+    grid = e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))  # codes 0 .. 126
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)  # first grid value >= a
+    lo = np.clip(hi - 1, 0, len(grid) - 1)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def e4m3_quantize_token(v32):
+    """One token's float32 values [..., n] -> (codes uint8, scale float32) with
+    one scale per token: scale = max|v| / 448 in float32 (at least the
+    smallest normal float32), code = E4M3(v / scale), the division in float32.
+
+    This is the per-token reading of the fp8 cache record: all 576 values of
+    a token share one fp32 scale ([G5SPEC] use case 1, 576 bytes per token).
+    """
+    v32 = np.asarray(v32, dtype=np.float32)
+    amax = np.max(np.abs(v32), axis=-1)
+    scale = np.maximum(amax / np.float32(448.0), np.finfo(np.float32).tiny).astype(np.float32)
+    q = np.clip((v32 / scale[..., None]).astype(np.float32), np.float32(-448.0), np.float32(448.0))
+    return e4m3fn_encode(q), scale
+
+
+def cache_append_rows(kv_in_bits, positions, dtype, rope_base=10000.0, d_c=512, d_r=64):
+    """Expected cache contents for appending new tokens.
+
+    kv_in_bits [B, n, >= d_c + d_r] bfloat16 bits: each row is a token's
+    fused projection output, d_c latent values then d_r RoPE-key values
+    before rotation ([TRACE] §3, the fused kv_a_proj output; [AUDIT] §2.4,
+    the rope key is cached separately).  Token j of sequence b sits at
+    position positions[b] + j; its key half is rotated there
+    (rope_interleaved, float64) before it is stored ([MLA80] §2: the key is
+    rotated at its own position before it enters the cache).
+
+    Returns (pos [B, n] int64, kv [B, n, d_c], pe [B, n, d_r], scale [B, n] or
+    None): bf16 caches hold the latent bits unchanged and the rotated key
+    rounded float64 -> float32 -> bfloat16 (nearest-even at each step); E4M3
+    caches hold e4m3_quantize_token of the token's float32 values (latent
+    exact, rotated key rounded to float32).
+    """
+    bits = np.asarray(kv_in_bits, dtype=np.uint16)
+    B, n = bits.shape[0], bits.shape[1]
+    pos = np.asarray(positions, dtype=np.int64)[:, None] + np.arange(n, dtype=np.int64)[None, :]
+    k_r = bf16_to_f64(bits[..., d_c:d_c + d_r])
+    rot = np.stack([rope_interleaved(k_r[b], pos[b], base=rope_base) for b in range(B)])
+    if dtype == "bf16":
+        return pos, bits[..., :d_c].copy(), f32_to_bf16_bits(rot.astype(np.float32)), None
+    if dtype == "fp8_e4m3":
+        v32 = np.concatenate([bf16_to_f64(bits[..., :d_c]).astype(np.float32), rot.astype(np.float32)], axis=-1)
+        codes, scale = e4m3_quantize_token(v32)
+        return pos, codes[..., :d_c], codes[..., d_c:], scale
+    raise ValueError(f"unknown cache dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
 # Cache addressing (contiguous slots or a block table) and batched decode
 # ---------------------------------------------------------------------------
 

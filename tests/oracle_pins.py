@@ -453,9 +453,94 @@ def check_cache_addressing(orc):
     assert np.array_equal(pe, [[4.0 * 2.0], [224.0]])
 
 
+# ---------------------------------------------------------------------------
+# encoders used by the cache append
+# ---------------------------------------------------------------------------
+
+def check_bf16_encode(orc):
+    """float32 -> bfloat16 nearest-even against torch's cast, exact bfloat16
+    values unchanged, and hand-made ties (to the even pattern)."""
+    rng = _rng(900)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        rng.standard_normal(1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f32_to_bf16_bits(x), ref)
+    codes = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    fin = codes[((codes >> 7) & 0xFF) != 0xFF]
+    vals = orc.bf16_to_f64(fin).astype(np.float32)
+    assert np.array_equal(orc.f32_to_bf16_bits(vals), fin)
+    # 1 + 2^-8 lies halfway between 1 (0x3F80, even) and 1 + 2^-7 (0x3F81)
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)], dtype=np.float32)
+    assert list(orc.f32_to_bf16_bits(ties)) == [0x3F80, 0x3F82, 0xBF80]
+
+
+def check_e4m3_encode(orc):
+    """E4M3 nearest-even: every finite code is its own value's encoding,
+    midpoints go to the even code, and torch's float8 cast agrees."""
+    codes = np.arange(256, dtype=np.uint8)
+    fin = codes[(codes & 0x7F) != 0x7F]
+    assert np.array_equal(orc.e4m3fn_encode(orc.e4m3fn_to_f64(fin)), fin)
+    grid = orc.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    want = np.where(np.arange(len(mids)) % 2 == 0, np.arange(len(mids)), np.arange(1, len(mids) + 1))
+    assert np.array_equal(orc.e4m3fn_encode(mids), want.astype(np.uint8))
+    eps = 1e-9 * np.maximum(grid[1:] - grid[:-1], 0)
+    assert np.array_equal(orc.e4m3fn_encode(mids - eps), np.arange(len(mids)).astype(np.uint8))
+    assert np.array_equal(orc.e4m3fn_encode(mids + eps), np.arange(1, len(mids) + 1).astype(np.uint8))
+    rng = _rng(901)
+    x = np.clip(rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000), -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e4m3fn_encode(x), ref)
+    assert orc.e4m3fn_encode(np.array([-0.0]))[0] == 0x80 and orc.e4m3fn_encode(np.array([448.0]))[0] == 0x7E
+    # per-token quantisation: the largest magnitude maps to +-448, every value
+    # is within half an E4M3 step (relative 2^-4) of value / scale
+    v = (rng.standard_normal((5, 576)) * 3).astype(np.float32)
+    c, sc = orc.e4m3_quantize_token(v)
+    assert np.allclose(sc, np.abs(v).max(axis=1) / 448.0, rtol=1e-7, atol=0)
+    back = orc.e4m3fn_to_f64(c) * sc[:, None].astype(np.float64)
+    big = np.abs(v) > 2.0 ** -6 * sc[:, None]
+    assert np.all(np.abs(back - v)[big] <= np.abs(v)[big] * 2.0 ** -4 + 1e-12)
+    assert np.all(np.abs(orc.e4m3fn_to_f64(c[np.arange(5), np.abs(v).argmax(axis=1)])) == 448.0)
+
+
+def check_cache_append(orc):
+    """Appended rows read back through the decoders: the latent half is the
+    input exactly (bf16) or within E4M3 rounding; the key half is the input
+    rotated at the row's position (RoPE by hand for one pair); positions run
+    on from positions[b]."""
+    rng = _rng(902)
+    B, n = 2, 3
+    vals = rng.standard_normal((B, n, 576)).astype(np.float32)
+    bits = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    x = orc.bf16_to_f64(bits)
+    positions = np.array([0, 41])
+    pos, kv, pe, sc = orc.cache_append_rows(bits, positions, "bf16")
+    assert pos.tolist() == [[0, 1, 2], [41, 42, 43]] and sc is None
+    assert np.array_equal(kv, bits[..., :512])
+    # pair i of the key rotated by pos * 10000^(-2i/64), written out by hand
+    for b in range(B):
+        for j in range(n):
+            p = float(pos[b, j])
+            for i in (0, 5, 31):
+                a0, a1 = x[b, j, 512 + 2 * i], x[b, j, 513 + 2 * i]
+                th = p * 10000.0 ** (-2.0 * i / 64.0)
+                want = np.array([a0 * math.cos(th) - a1 * math.sin(th), a1 * math.cos(th) + a0 * math.sin(th)])
+                got = orc.bf16_to_f64(pe[b, j, 2 * i:2 * i + 2])
+                assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-30), (b, j, i)
+    assert np.array_equal(pe[0, 0], bits[0, 0, 512:576])  # position 0: identity
+    pos8, kv8, pe8, sc8 = orc.cache_append_rows(bits, positions, "fp8_e4m3")
+    assert np.array_equal(pos8, pos)
+    back = orc.e4m3fn_to_f64(kv8) * sc8[..., None]
+    assert np.all(np.abs(back - x[..., :512]) <= np.abs(x[..., :512]) * 2.0 ** -4 + 2.0 ** -9 * sc8[..., None])
+    back_pe = orc.e4m3fn_to_f64(pe8) * sc8[..., None]
+    rot = orc.bf16_to_f64(pe)
+    assert np.all(np.abs(back_pe - rot) <= np.abs(rot) * (2.0 ** -4 + 2.0 ** -7) + 2.0 ** -9 * sc8[..., None])
+
+
 ALL_CHECKS = [
     check_cache_sizes, check_required_fields, check_bf16_decode, check_e4m3_decode,
     check_worked_example, check_brute_force, check_textbook_sdpa, check_naive_equals_absorbed,
     check_special_cases, check_split_combine, check_rope, check_prefill_decode_vs_oneshot,
     check_rope_on_content_breaks_absorption, check_cache_addressing,
+    check_bf16_encode, check_e4m3_encode, check_cache_append,
 ]

@@ -159,6 +159,63 @@ def _causal_no_mask(q_nope, q_pe_raw, c, k_r_raw, w_uk, w_uv, scale, rope_base=1
     return out
 
 
+def _bf16_truncate(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_ties_odd(x):
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lo, rem = u >> np.uint64(16), u & np.uint64(0xFFFF)
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((lo & np.uint64(1)) == np.uint64(0)))
+    return (lo + up.astype(np.uint64)).astype(np.uint16)
+
+
+def _e4m3_encode_factory(variant):
+    def e4m3fn_encode(x):
+        mod = fresh_oracle()
+        x = np.asarray(x, dtype=np.float64)
+        grid = mod.e4m3fn_to_f64(np.arange(0x7F, dtype=np.uint8))
+        a = np.abs(x)
+        hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)
+        lo = np.clip(hi - 1, 0, len(grid) - 1)
+        d_lo, d_hi = a - grid[lo], grid[hi] - a
+        tie_hi = (hi % 2 == 1) if variant == "ties_odd" else (hi % 2 == 0)
+        code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & tie_hi), hi, lo).astype(np.uint8)
+        if variant == "drop_sign":
+            return code
+        return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+    return e4m3fn_encode
+
+
+def _quantize_amax_240(v32):
+    mod = fresh_oracle()
+    v32 = np.asarray(v32, dtype=np.float32)
+    scale = np.maximum(np.max(np.abs(v32), axis=-1) / np.float32(240.0), np.finfo(np.float32).tiny).astype(np.float32)
+    q = np.clip((v32 / scale[..., None]).astype(np.float32), -448, 448)
+    return mod.e4m3fn_encode(q), scale
+
+
+def _append_factory(variant):
+    def cache_append_rows(kv_in_bits, positions, dtype, rope_base=10000.0, d_c=512, d_r=64):
+        mod = fresh_oracle()
+        bits = np.asarray(kv_in_bits, dtype=np.uint16)
+        B, n = bits.shape[0], bits.shape[1]
+        step = np.zeros(n, dtype=np.int64) if variant == "no_offset" else np.arange(n, dtype=np.int64)
+        pos = np.asarray(positions, dtype=np.int64)[:, None] + step[None, :]
+        shift = 1 if variant == "rope_plus_one" else 0
+        k_r = mod.bf16_to_f64(bits[..., d_c:d_c + d_r])
+        rot = np.stack([mod.rope_interleaved(k_r[b], pos[b] + shift, base=rope_base) for b in range(B)])
+        if variant == "fp8_unrotated" and dtype == "fp8_e4m3":
+            rot = k_r
+        if dtype == "bf16":
+            return pos, bits[..., :d_c].copy(), mod.f32_to_bf16_bits(rot.astype(np.float32)), None
+        v32 = np.concatenate([mod.bf16_to_f64(bits[..., :d_c]).astype(np.float32), rot.astype(np.float32)], axis=-1)
+        codes, scale = mod.e4m3_quantize_token(v32)
+        return pos, codes[..., :d_c], codes[..., d_c:], scale
+    return cache_append_rows
+
+
 MUTANTS = {
     "latent_attention/drop_rope_term": ("latent_attention", _latent_attention_factory("drop_rope")),
     "latent_attention/no_scale": ("latent_attention", _latent_attention_factory("no_scale")),
@@ -179,6 +236,14 @@ MUTANTS = {
     "cache_bytes/silent_defaults": ("latent_cache_bytes_per_token", _latent_bytes_default),
     "naive_attention/no_rope_key": ("naive_attention", _naive_attention_no_rope_key),
     "causal_forward/no_mask": ("causal_naive_forward", _causal_no_mask),
+    "bf16_encode/truncate": ("f32_to_bf16_bits", _bf16_truncate),
+    "bf16_encode/ties_to_odd": ("f32_to_bf16_bits", _bf16_ties_odd),
+    "e4m3_encode/ties_to_odd": ("e4m3fn_encode", _e4m3_encode_factory("ties_odd")),
+    "e4m3_encode/drop_sign": ("e4m3fn_encode", _e4m3_encode_factory("drop_sign")),
+    "e4m3_quantize/max_240": ("e4m3_quantize_token", _quantize_amax_240),
+    "cache_append/no_position_offset": ("cache_append_rows", _append_factory("no_offset")),
+    "cache_append/rope_position_plus_one": ("cache_append_rows", _append_factory("rope_plus_one")),
+    "cache_append/fp8_key_unrotated": ("cache_append_rows", _append_factory("fp8_unrotated")),
 }
 
 
