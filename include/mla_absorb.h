@@ -12,6 +12,9 @@
  *   mla_combine_splits  log-sum-exp merge of split-KV partial results
  *   mla_expand_v        out[b,h,:] = W_UV[h] . o_lat[b,h,:]                 (value absorption)
  *
+ * and mla_cache_append, which writes new tokens (latent row + rotated RoPE
+ * key, bf16 or E4M3 with a per-token scale) into the cache that decode reads.
+ *
  * The method is the one described on the source pages (cited by title):
  *   [AUDIT]  "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界":
  *            §2.2 moves W_UK onto the query, §2.3 applies W_UV after the
@@ -202,6 +205,45 @@ mla_status mla_expand_v(const mla_dims *dims, const void *o_lat, const void *w_u
                         void *stream);
 
 /*
+ * Cache append: writes num_new new tokens of every sequence into the latent
+ * cache.  Each input row is the token's fused down-projection output: 512
+ * latent values, then the 64-wide decoupled RoPE key BEFORE rotation ([AUDIT]
+ * §2.4: the RoPE key is cached separately, rotated; [MLA80] §2 and Appendix
+ * A: interleaved pairs (2i, 2i+1) turned by position * rope_base^(-2i/64)).
+ * Token j of sequence b has position positions[b] + j and is stored in that
+ * position's slot (addressing as in mla_cache above; contiguous:
+ * b * seq_stride + position, paged: through block_table).
+ *
+ *   kv_in      device bf16 [B, num_new, in_stride]; elements 0..575 of a row
+ *              are used; in_stride >= 576 and a multiple of 8 elements
+ *   positions  device int32 [B]
+ *   num_new    tokens per sequence (0 = nothing to do, no launch)
+ *   rope_base  > 0, required (DeepSeek uses 10000)
+ *
+ * bf16 cache: the latent half is copied bit for bit; the key is rotated in
+ * fp64 and rounded fp64 -> fp32 -> bf16 (nearest even at each step).
+ * E4M3 cache: the token's 576 values in fp32 (latent exact, rotated key
+ * rounded to fp32) share one scale = max(max|x| / 448, FLT_MIN), computed in
+ * fp32 and written to token_scale[slot]; each code is the OCP E4M3 value
+ * nearest to x / scale (IEEE fp32 division, clamped to +-448), ties to the
+ * even code ([G5SPEC] use case 1: 576 one-byte elements plus an fp32 scale
+ * per token).  Inputs must be finite.
+ *
+ * The call WRITES through cache->kv, cache->pe and (E4M3) cache->token_scale:
+ * they must point to writable device memory that kv_in does not overlap.
+ * Rows whose slot does not exist are skipped on the device without an error:
+ * a negative position, position >= seq_stride (contiguous), position /
+ * block_size >= max_blocks_per_seq or a negative block_table entry (paged).
+ * Block ids that are >= 0 must name blocks of the pool.  Sequence lengths are
+ * not updated: after the append, the caller's seq_lens[b] for decode is
+ * positions[b] + num_new.  Contiguous caches need seq_stride > 0; paged
+ * caches a positive block_size (any value) and max_blocks_per_seq.
+ */
+mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const void *kv_in, int64_t in_stride,
+                            const int32_t *positions, int32_t num_new, float rope_base, void *stream);
+
+/*
+ * Recommended num_splits for mla_decode_latent/*
  * Recommended num_splits for mla_decode_latent on a device with `num_cus`
  * compute units: enough workgroups to fill the chip, each split at least
  * 256 tokens.  Host-only.

@@ -23,7 +23,7 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
-            "mla_recommended_splits"]
+            "mla_recommended_splits", "mla_cache_append"]
 
 
 class MlaError(RuntimeError):
@@ -85,6 +85,9 @@ def load():
     lib.mla_combine_splits.argtypes = [D, P, P, ctypes.c_int32, P, P, P]
     lib.mla_expand_v.restype = st
     lib.mla_expand_v.argtypes = [D, P, P, P, P]
+    lib.mla_cache_append.restype = st
+    lib.mla_cache_append.argtypes = [D, ctypes.POINTER(MlaCache), P, ctypes.c_int64, P, ctypes.c_int32,
+                                     ctypes.c_float, P]
     lib.mla_recommended_splits.restype = ctypes.c_int32
     lib.mla_recommended_splits.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
     _lib = lib
@@ -253,6 +256,28 @@ def mla_expand_v(d, o_lat, w_uv, out=None, stream=None):
     _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), o_lat.device)
     _check(load().mla_expand_v(ctypes.byref(d), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream)))
     return out
+
+
+def mla_cache_append(d, cache, kv_in, positions, rope_base=10000.0, stream=None):
+    """Write kv_in [B, n, >= 576] bf16 (latent row + unrotated RoPE key per
+    token) into the cache at positions[b] + j; the cache's buffers are
+    written in place.  Rows may be a view with any row stride (multiple of 8
+    elements) as long as element and token strides nest."""
+    B = d.batch
+    if not isinstance(kv_in, torch.Tensor) or kv_in.dtype != torch.bfloat16:
+        raise TypeError("kv_in must be a bfloat16 torch.Tensor")
+    if kv_in.dim() != 3 or kv_in.shape[0] != B or kv_in.shape[2] < d.kv_lora_rank + d.qk_rope_head_dim:
+        raise ValueError(f"kv_in must have shape ({B}, n, >= {d.kv_lora_rank + d.qk_rope_head_dim}), "
+                         f"got {tuple(kv_in.shape)}")
+    n = kv_in.shape[1]
+    row = kv_in.stride(1)
+    if kv_in.stride(2) != 1 or (B > 1 and n > 0 and kv_in.stride(0) != n * row):
+        raise ValueError("kv_in rows must have unit element stride and sequences must follow each other")
+    if not kv_in.is_cuda:
+        raise ValueError("kv_in must be a device tensor")
+    _expect(positions, "positions", torch.int32, (B,), kv_in.device)
+    _check(load().mla_cache_append(ctypes.byref(d), ctypes.byref(cache), _ptr(kv_in), int(row), _ptr(positions),
+                                   int(n), float(rope_base), _stream(stream)))
 
 
 class DecodeStep:

@@ -51,11 +51,31 @@ struct CombineArgs {
   int32_t num_splits;
 };
 
+struct AppendArgs {
+  const uint16_t* kv_in;      // [B, num_new, in_stride] bf16: 512 latent, then 64 unrotated key
+  int64_t in_stride;          // elements between consecutive input rows
+  const int32_t* positions;   // [B]: position of each sequence's first new token
+  int32_t batch;
+  int32_t num_new;
+  char* kv;                   // latent element 0 of slot 0
+  char* pe;                   // rope element 0 of slot 0
+  int64_t kv_sb;              // bytes between consecutive slots (kv)
+  int64_t pe_sb;              // bytes between consecutive slots (pe)
+  float* token_scale;         // E4M3 cache: one fp32 scale per slot (else null)
+  int64_t seq_stride;         // contiguous: slots per sequence
+  const int32_t* block_table; // paged: [B, max_blocks]; null = contiguous
+  int32_t block_size;
+  int32_t max_blocks;
+  double inv_freq[32];        // rotation frequency of key pair i: base^(-2i/64)
+};
+
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
 // 128 heads, bf16 cache: 32-head waves with P.V woven into the next tile's scores.
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// fp8 selects the E4M3 cache encoding.
+hipError_t launch_cache_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 
 }  // namespace mla

@@ -259,6 +259,87 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
 }
 
+mla_status mla_cache_append(const mla_dims* dims, const mla_cache* cache, const void* kv_in, int64_t in_stride,
+                            const int32_t* positions, int32_t num_new, float rope_base, void* stream) {
+  const char* where = "mla_cache_append";
+  mla_status st = check_latent_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (dims->batch <= 0) return fail(MLA_ERR_MISSING_DIM, "batch missing (mla_dims, %s)", where);
+  if (dims->kv_lora_rank != 512)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_lora_rank %d not supported, built for 512 (%s)", dims->kv_lora_rank, where);
+  if (dims->qk_rope_head_dim != 64)
+    return fail(MLA_ERR_UNSUPPORTED, "qk_rope_head_dim %d not supported, built for 64 (%s)", dims->qk_rope_head_dim,
+                where);
+  if (rope_base == 0.0f) return fail(MLA_ERR_MISSING_DIM, "rope_base missing (%s)", where);
+  if (!(rope_base > 0.0f) || !std::isfinite(rope_base))
+    return fail(MLA_ERR_UNSUPPORTED, "rope_base must be positive and finite (%s)", where);
+  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
+  if (cache->dtype != MLA_DTYPE_BF16 && cache->dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  const int64_t stride_align = fp8 ? 16 : 8;
+  REQUIRE_PTR(cache->kv, "mla_cache.kv", where);
+  REQUIRE_PTR(cache->pe, "mla_cache.pe", where);
+  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->kv_stride, dims->kv_lora_rank, (long long)stride_align, where);
+  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->pe_stride, dims->qk_rope_head_dim, (long long)stride_align, where);
+  if (fp8) {
+    if (cache->token_scale == nullptr)
+      return fail(MLA_ERR_NULL, "mla_cache.token_scale is NULL (E4M3 cache needs one fp32 scale per slot, %s)", where);
+    if (reinterpret_cast<uintptr_t>(cache->token_scale) % 4 != 0)
+      return fail(MLA_ERR_ALIGN, "mla_cache.token_scale is not 4-byte aligned (%s)", where);
+  } else if (cache->token_scale != nullptr) {
+    return fail(MLA_ERR_BUFFER, "mla_cache.token_scale must be NULL for a bf16 cache (%s)", where);
+  }
+  if (cache->block_table != nullptr) {
+    if (reinterpret_cast<uintptr_t>(cache->block_table) % 4 != 0)
+      return fail(MLA_ERR_ALIGN, "mla_cache.block_table is not 4-byte aligned (%s)", where);
+    if (cache->block_size <= 0)
+      return fail(MLA_ERR_BAD_LENGTH, "mla_cache.block_size %d must be positive (%s)", cache->block_size, where);
+    if (cache->max_blocks_per_seq <= 0)
+      return fail(MLA_ERR_BUFFER, "mla_cache.max_blocks_per_seq %d must be positive (%s)", cache->max_blocks_per_seq,
+                  where);
+  } else if (cache->seq_stride <= 0) {
+    return fail(MLA_ERR_BUFFER, "mla_cache.seq_stride %lld must be positive (contiguous cache, %s)",
+                (long long)cache->seq_stride, where);
+  }
+  if (num_new < 0) return fail(MLA_ERR_BAD_LENGTH, "num_new %d < 0 (%s)", num_new, where);
+  if ((int64_t)dims->batch * num_new > (int64_t)1 << 31)
+    return fail(MLA_ERR_BAD_LENGTH, "batch * num_new above 2^31 rows (%s)", where);
+  REQUIRE_PTR(kv_in, "kv_in", where);
+  const int64_t row_width = dims->kv_lora_rank + dims->qk_rope_head_dim;
+  if (in_stride < row_width || in_stride % 8 != 0)
+    return fail(MLA_ERR_BUFFER, "in_stride %lld must be >= %lld and a multiple of 8 elements (%s)",
+                (long long)in_stride, (long long)row_width, where);
+  if (positions == nullptr) return fail(MLA_ERR_NULL, "positions is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(positions) % 4 != 0)
+    return fail(MLA_ERR_ALIGN, "positions is not 4-byte aligned (%s)", where);
+  if (num_new == 0) return ok();
+
+  mla::AppendArgs a{};
+  a.kv_in = static_cast<const uint16_t*>(kv_in);
+  a.in_stride = in_stride;
+  a.positions = positions;
+  a.batch = dims->batch;
+  a.num_new = num_new;
+  // the cache description is shared with decode, which only reads it
+  a.kv = const_cast<char*>(static_cast<const char*>(cache->kv));
+  a.pe = const_cast<char*>(static_cast<const char*>(cache->pe));
+  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
+  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
+  a.token_scale = const_cast<float*>(cache->token_scale);
+  a.seq_stride = cache->seq_stride;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  // pair i turns by position * base^(-2i/64); the exponent -2i/64 is exact
+  for (int i = 0; i < 32; ++i) a.inv_freq[i] = std::pow((double)rope_base, -(double)(2 * i) / 64.0);
+  return launch_result(mla::launch_cache_append(a, fp8, static_cast<hipStream_t>(stream)), where);
+}
+
 int32_t mla_recommended_splits(const mla_dims* dims, int32_t max_seq_len, int32_t num_cus) {
   if (dims == nullptr || dims->batch <= 0 || dims->num_heads <= 0 || max_seq_len <= 0 || num_cus <= 0) return 1;
   // workgroups resident per CU: 8 waves of 16 heads at most

@@ -271,3 +271,14 @@ def random_partials(batch, splits, heads, seed, device="cpu", empty_fraction=0.2
     lse = torch.where(empty.unsqueeze(-1), torch.full_like(lse, -math.inf), lse)
     o = torch.where(empty.unsqueeze(-1).unsqueeze(-1), torch.zeros_like(o), o)
     return o.to(torch.bfloat16), lse
+
+
+def random_projection_rows(batch, num_new, seed, device="cpu", width=D_K):
+    """New tokens for the cache-append step: [B, n, width] bfloat16 ~ N(0, 1),
+    each row standing for a token's fused down-projection output (512 latent
+    values, then the 64-wide RoPE key before rotation; the cache rows of the
+    workloads have the same distribution)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    return _normal(gen, (batch, num_new, width), 1.0, dev).to(torch.bfloat16)

@@ -136,3 +136,51 @@ def test_recommended_splits(lib):
     assert binding.mla_recommended_splits(binding.dims(32, 128, 0.07), 4096, 256) == 8
     assert binding.mla_recommended_splits(binding.dims(64, 16, 0.07), 4096, 256) == 16
     assert binding.mla_recommended_splits(binding.dims(1, 16, 0.07), 26, 256) == 1
+
+
+def _append(lib, d, cache, kv_in=4096, in_stride=576, positions=4096, num_new=1, rope_base=10000.0):
+    P = ctypes.c_void_p
+    return lib.mla_cache_append(ctypes.byref(d), ctypes.byref(cache) if cache is not None else None,
+                                P(kv_in) if kv_in else None, in_stride, P(positions) if positions else None,
+                                num_new, rope_base, None)
+
+
+def test_cache_append_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    base = dict(dtype=0, kv=1024, pe=2048, kv_stride=576, pe_stride=576, token_scale=None, seq_stride=64,
+                block_table=None, block_size=0, max_blocks_per_seq=0)
+
+    def cache(**kw):
+        c = dict(base)
+        c.update(kw)
+        return binding.MlaCache(**c)
+
+    def err():
+        return lib.mla_last_error().decode()
+
+    assert _append(lib, binding.dims(0, 16, 0.07), cache()) == 2 and "batch" in err()
+    assert _append(lib, binding.dims(2, 16, 0.07, kv_lora_rank=0), cache()) == 2 and "kv_lora_rank" in err()
+    assert _append(lib, binding.dims(2, 16, 0.07, qk_rope_head_dim=32), cache()) == 3
+    assert _append(lib, d, cache(), rope_base=0.0) == 2 and "rope_base" in err()
+    assert _append(lib, d, cache(), rope_base=-1.0) == 3 and "rope_base" in err()
+    assert _append(lib, d, None) == 1
+    assert _append(lib, d, cache(dtype=5)) == 3 and "dtype" in err()
+    assert _append(lib, d, cache(dtype=1)) == 1 and "token_scale" in err()
+    assert _append(lib, d, cache(token_scale=4096)) == 5 and "token_scale" in err()
+    assert _append(lib, d, cache(kv=None)) == 1 and "mla_cache.kv" in err()
+    assert _append(lib, d, cache(pe=2050)) == 6
+    assert _append(lib, d, cache(kv_stride=516)) == 5 and "kv_stride" in err()
+    assert _append(lib, d, cache(dtype=1, token_scale=4096, pe_stride=72)) == 5 and "pe_stride" in err()
+    assert _append(lib, d, cache(seq_stride=0)) == 5 and "seq_stride" in err()
+    assert _append(lib, d, cache(block_table=4096, block_size=0, max_blocks_per_seq=4)) == 4
+    assert _append(lib, d, cache(block_table=4096, block_size=64, max_blocks_per_seq=0)) == 5
+    assert _append(lib, d, cache(block_table=4098, block_size=64, max_blocks_per_seq=4)) == 6
+    assert _append(lib, d, cache(), kv_in=0) == 1 and "kv_in" in err()
+    assert _append(lib, d, cache(), kv_in=4100) == 6 and "kv_in" in err()
+    assert _append(lib, d, cache(), in_stride=572) == 5 and "in_stride" in err()
+    assert _append(lib, d, cache(), in_stride=580) == 5 and "in_stride" in err()
+    assert _append(lib, d, cache(), positions=0) == 1 and "positions" in err()
+    assert _append(lib, d, cache(), num_new=-1) == 4 and "num_new" in err()
+    # nothing to append: accepted, and nothing is launched (this machine has no GPU)
+    assert _append(lib, d, cache(), num_new=0) == 0 and err() == ""
+    assert _append(lib, d, cache(block_table=4096, block_size=48, max_blocks_per_seq=4), num_new=0) == 0
