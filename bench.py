@@ -13,6 +13,9 @@ Prints one JSON line:
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
                   bytes per launch / its mean duration from HIP events around
                   each launch, against 8 TB/s
+  append          mla_cache_append on the same shape (timed apart from the
+                  step): one token per sequence, and the whole history in one
+                  call against the HBM roofline (input read + cache write bytes)
   cpu_baseline    the float64 oracle on the host cores, on a bounded sample of
                   the same workload, in the same unit
 """
@@ -57,15 +60,16 @@ def proj_flops(B, H):
     return 2 * 2 * B * H * 128 * 512
 
 
-def traffic_from_counters(per_launch_algo_bytes):
+def traffic_from_counters(workload):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when they are missing or the kernel source changed since."""
+    or None when they are missing, were taken on another workload, or the
+    kernel source changed since."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("workload") != workload:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -168,6 +172,80 @@ def summarize_counters(args, fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def bench_append(x0, d, dev, steps):
+    """Time mla_cache_append on the workload's shape: one new token per
+    sequence (a decode step's write, launch-bound) and the whole history in one
+    call (a prefill's write, HBM-bound: reads 1152 B of bf16 input and writes
+    one cache row per token).  Writes go to buffers of their own, so the
+    decode inputs stay untouched."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    B, T = x0.batch, x0.max_seq_len
+    fp8 = x0.workload.dtype == "fp8_e4m3"
+    row_bytes = 576 + 4 if fp8 else 1152
+    ad = binding.dims(B, x0.heads, x0.scale)
+
+    def new_cache(seq_stride):
+        store = torch.empty((B * seq_stride, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        scale = torch.empty((B * seq_stride,), dtype=torch.float32, device=dev) if fp8 else None
+        return binding.make_cache(store[:, :512], store[:, 512:], seq_stride=seq_stride, token_scale=scale)
+
+    def timed(calls, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            calls[i % len(calls)]()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / n * 1e-3
+
+    # decode step: one token per sequence at position T - 1.  The launch is
+    # shorter than its host-side enqueue, so the calls are captured in a HIP
+    # graph and timed over graph replays (the GPU's own time per launch).
+    one = [datagen.random_projection_rows(B, 1, 900 + i, device=dev) for i in range(4)]
+    pos_last = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    c_dec = new_cache(T)
+    n_cap = 32
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(n_cap):
+            binding.mla_cache_append(ad, c_dec, one[k % len(one)], pos_last)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_one = e0.elapsed_time(e1) * 1e-3 / (reps * n_cap)
+    del graph
+
+    # prefill: the whole history in one call, two input and two output buffers in turn
+    ins = [datagen.random_projection_rows(B, T, 910 + i, device=dev) for i in range(2)]
+    outs = [new_cache(T) for _ in range(2)]
+    zero = torch.zeros((B,), dtype=torch.int32, device=dev)
+    pre_calls = [lambda k=k: binding.mla_cache_append(ad, outs[k % 2], ins[(k // 2) % 2], zero) for k in range(4)]
+    n_pre = max(4, min(steps, 40))
+    timed(pre_calls, 4)
+    t_all = timed(pre_calls, n_pre)
+    moved = B * T * (1152 + row_bytes)
+    del ins, outs, c_dec
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "mla_cache_append",
+        "one_token_per_seq_us": round(t_one * 1e6, 3),
+        "one_token_per_seq_timing": "HIP graph of 32 launches, replayed",
+        "whole_history_us": round(t_all * 1e6, 3),
+        "whole_history_tokens": B * T,
+        "whole_history_bytes": moved,
+        "roofline": {"bound": "hbm", "achieved": round(moved / t_all / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(moved / t_all / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +255,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="0 = library recommendation")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
@@ -281,7 +360,7 @@ def main():
     gbs_step = cache_bytes / t_step / 1e9
     gbs_dec = cache_bytes / t_dec / 1e9
     gbs_att = cache_bytes / t_att / 1e9
-    traffic = traffic_from_counters(cache_bytes)
+    traffic = traffic_from_counters(wl.name)
 
     result = {
         "metric": METRIC if wl.name == "v3_b32_s4096" else METRIC_OTHER.format(wl.description),
@@ -313,6 +392,8 @@ def main():
         "device": props.name,
         "cus": props.multi_processor_count,
     }
+    if not args.no_append:
+        result["append"] = bench_append(x0, d, dev, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x0)
     print(json.dumps(result), flush=True)

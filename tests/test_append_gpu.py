@@ -105,10 +105,8 @@ def _check(c, want, positions, seq_stride=0, table=None, block_size=None):
                     assert same, (b, j, got_scale[s], scale[b, j])
                 else:
                     assert abs(float(got_scale[s]) / float(scale[b, j]) - 1.0) <= 2.0 ** -20, (b, j)
-                if same:
-                    assert np.all(np.abs(got[s, :512].astype(np.int32) - kv[b, j].astype(np.int32)) <= 1)
-                    exact_lat = np.array_equal(got[s, :512], kv[b, j])
-                    assert exact_lat or not zero_angle, (b, j)
+                if same:  # the same scale: latent quotients and their codes are identical
+                    assert np.array_equal(got[s, :512], kv[b, j]), (b, j)
                 gk = got[s, 512:].astype(np.int32)
                 wk = pe[b, j].astype(np.int32)
             if zero_angle:
@@ -193,6 +191,40 @@ def test_append_fp8_ties_and_special_rows():
     assert sc[16] == np.finfo(np.float32).tiny
 
 
+def test_append_fp8_every_bf16_pattern():
+    """Every finite bfloat16 value in [-448, 448], appended at position 0 in
+    rows whose largest magnitude is 448 (scale exactly 1) and 448 * 2^-7
+    (scale 2^-7, values scaled down by the same power, the tiniest ones set
+    to zero so that every value stays exact): all codes equal the oracle's
+    encoder."""
+    announce("append fp8 every bf16 pattern")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f64(pats)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    vals = vals[keep]
+    per = 575
+    n_rows = -(-len(vals) // per)
+    base = np.zeros((n_rows, 576))
+    flat = np.zeros(n_rows * per)
+    flat[:len(vals)] = vals
+    base[:, 1:] = flat.reshape(n_rows, per)
+    base[:, 0] = 448.0
+    small = np.where(np.abs(base) < 2.0 ** -100, 0.0, base) * 2.0 ** -7  # stays exact in bf16
+    rows = np.concatenate([base, small])
+    rows_t = torch.from_numpy(rows.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(oracle.bf16_to_f64(bits16(rows_t)), rows)
+    B = rows.shape[0]
+    kv_in = rows_t.view(B, 1, 576).to(DEV)
+    c = Cache(B, True, seq_stride=1)
+    binding.mla_cache_append(binding.dims(B, 128, 0.07), c.desc, kv_in, torch.zeros(B, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    _, kv, pe, scale = oracle.cache_append_rows(bits16(kv_in), np.zeros(B, dtype=np.int64), "fp8_e4m3")
+    got = c.codes()
+    assert np.array_equal(c.scale.cpu().numpy(), scale[:, 0])
+    assert np.array_equal(got[:, :512], kv[:, 0])
+    assert np.array_equal(got[:, 512:], pe[:, 0])
+
+
 def test_append_then_decode_against_oracle():
     """Prefill-style append of T tokens, a decode, then a decode-style append
     of one token per sequence at position T and a decode at T + 1: the
@@ -253,6 +285,6 @@ def test_append_full_size_sampled(fp8, B, T):
                 s = float(c.scale[b * T + t])
                 assert abs(s / float(scale[0, 0]) - 1.0) <= 2.0 ** -20, (b, t)
                 if s == scale[0, 0]:
-                    assert np.all(np.abs(got[k, :512].astype(np.int32) - kv[0, 0].astype(np.int32)) <= 1)
+                    assert np.array_equal(got[k, :512], kv[0, 0]), (b, t)
             else:
                 assert np.array_equal(got[k, :512], kv[0, 0]), (b, t)
