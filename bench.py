@@ -4,7 +4,8 @@
 
 A step is the whole decode path of one layer for one batch: mla_absorb_q,
 mla_decode_latent (split-KV), mla_combine_splits and mla_expand_v, on seeded
-synthetic inputs already resident in HBM.  Inputs are rotated over several
+synthetic inputs already resident in HBM, issued as one HIP graph replay per
+step (the eager, call-by-call time is reported beside it).  Inputs are rotated over several
 replicas per step so the working set exceeds the 256 MB Infinity Cache and
 every step streams its latent cache from HBM.
 
@@ -13,6 +14,8 @@ Prints one JSON line:
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
                   bytes per launch / its mean duration from HIP events around
                   each launch, against 8 TB/s
+  fused_step      (contexts up to 2048) mla_decode_step_fused, the same step
+                  in one launch, GPU time per step from graph replays
   append          mla_cache_append on the same shape (timed apart from the
                   step): one token per sequence, and the whole history in one
                   call against the HBM roofline (input read + cache write bytes)
@@ -172,6 +175,47 @@ def summarize_counters(args, fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+FUSED_MAX_CONTEXT = 2048   # the fused one-launch step is timed on short contexts only
+
+
+def bench_fused_step(x0, d, dev, steps):
+    """mla_decode_step_fused (absorb + attention + expand in one launch) on the
+    same inputs: 32 launches captured in a HIP graph and replayed, so the
+    figure is GPU time per step."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding
+
+    cache = binding.make_cache(x0.kv_rows, x0.pe_rows, seq_stride=x0.seq_stride, block_table=x0.block_table,
+                               block_size=x0.block_size, token_scale=x0.token_scale)
+    out = torch.empty((x0.batch, x0.heads, 128), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        binding.mla_decode_step_fused(d, cache, x0.q_nope, x0.q_pe, x0.w_uk, x0.w_uv, x0.seq_lens, x0.max_seq_len,
+                                      out=out)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    n_cap = 32
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_cap):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (reps * n_cap)
+    del graph
+    return {"kernel": "mla_decode_step_fused", "step_us": round(t * 1e6, 3),
+            "timing": "HIP graph of 32 launches, replayed"}
+
+
 def bench_append(x0, d, dev, steps):
     """Time mla_cache_append on the workload's shape: one new token per
     sequence (a decode step's write, launch-bound) and the whole history in one
@@ -294,7 +338,9 @@ def main():
     wl = datagen.WORKLOADS[args.workload]
     x0 = datagen.make_inputs(wl, device=dev)
     cache_bytes = x0.cache_bytes()
-    R = args.replicas or max(2, math.ceil(512e6 / cache_bytes) + 1)
+    # enough replicas that the rotated inputs exceed the 256 MB Infinity Cache
+    # (tiny launch-bound workloads are capped: they are not bandwidth-bound)
+    R = args.replicas or min(64, max(2, math.ceil(512e6 / cache_bytes) + 1))
     reps = [x0] + [datagen.make_inputs(wl, device=dev) for _ in range(R - 1)]
     d = binding.dims(x0.batch, x0.heads, x0.scale)
     P = args.splits or binding.mla_recommended_splits(d, x0.max_seq_len, props.multi_processor_count)
@@ -318,12 +364,31 @@ def main():
         run(i)
     torch.cuda.synchronize()
 
-    # whole-step timing: K steps between two synchronisations
+    # eager step: every call launched from Python
     t0 = time.perf_counter()
     for i in range(args.steps):
         run(i)
     torch.cuda.synchronize()
+    t_step_eager = (time.perf_counter() - t0) / args.steps
+
+    # whole-step timing: K steps between two synchronisations, each step one
+    # replay of a HIP graph holding the four launches on one input replica
+    # (how a serving loop issues a decode step: no per-call host overhead)
+    graphs = []
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(i)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
+    del graphs
 
     # dominant kernel: HIP events around each decode launch (same stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -370,6 +435,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
+        "ms_per_step_eager": round(t_step_eager * 1e3, 5),
+        "step_timing": "HIP graph replay per step (four launches)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -392,6 +459,8 @@ def main():
         "device": props.name,
         "cus": props.multi_processor_count,
     }
+    if x0.max_seq_len <= FUSED_MAX_CONTEXT:
+        result["fused_step"] = bench_fused_step(x0, d, dev, args.steps)
     if not args.no_append:
         result["append"] = bench_append(x0, d, dev, args.steps)
     if not args.no_cpu_baseline:

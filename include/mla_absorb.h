@@ -13,7 +13,9 @@
  *   mla_expand_v        out[b,h,:] = W_UV[h] . o_lat[b,h,:]                 (value absorption)
  *
  * and mla_cache_append, which writes new tokens (latent row + rotated RoPE
- * key, bf16 or E4M3 with a per-token scale) into the cache that decode reads.
+ * key, bf16 or E4M3 with a per-token scale) into the cache that decode reads,
+ * and mla_decode_step_fused, the three decode stages in one launch for short
+ * contexts.
  *
  * The method is the one described on the source pages (cited by title):
  *   [AUDIT]  "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界":
@@ -205,6 +207,29 @@ mla_status mla_expand_v(const mla_dims *dims, const void *o_lat, const void *w_u
                         void *stream);
 
 /*
+ * Fused decode step for short contexts: mla_absorb_q, mla_decode_latent with
+ * one split, and mla_expand_v in ONE launch ([AUDIT] §2.2-§2.4; [MLA80]
+ * §4-§5), for shapes where launch latency dominates (a few sequences with
+ * short contexts).
+ *   q_nope  device bf16 [B, H, 128]      w_uk  device bf16 [H, 128, 512]
+ *   q_pe    device bf16 [B, H, 64]       w_uv  device bf16 [H, 128, 512]
+ *   seq_lens device int32 [B], max_seq_len as in mla_decode_latent
+ *   out     device bf16 [B, H, 128] (output)
+ *   o_lat   device bf16 [B, H, 512] (output, may be NULL)
+ *   lse     device fp32 [B, H] (output, may be NULL)
+ * Same result as the three calls up to rounding: q_lat and o_lat stay fp32
+ * between the stages (the three-call path rounds them to bf16), and every
+ * dot product is an fp32 sum.  One workgroup per (sequence, head) streams
+ * that sequence's rows, so the cost grows with H * context: long contexts
+ * belong to the split-KV mla_decode_latent.  The cache, sequence-length and
+ * error rules are those of mla_decode_latent (no split arguments).
+ */
+mla_status mla_decode_step_fused(const mla_dims *dims, const mla_cache *cache, const void *q_nope, const void *q_pe,
+                                 const void *w_uk, const void *w_uv, const int32_t *seq_lens, int32_t max_seq_len,
+                                 void *out, void *o_lat, float *lse, void *stream);
+
+/*
+ * Cache append: writes num_new new tokens/*
  * Cache append: writes num_new new tokens of every sequence into the latent
  * cache.  Each input row is the token's fused down-projection output: 512
  * latent values, then the 64-wide decoupled RoPE key BEFORE rotation ([AUDIT]

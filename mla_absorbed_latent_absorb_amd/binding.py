@@ -23,7 +23,7 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
-            "mla_recommended_splits", "mla_cache_append"]
+            "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused"]
 
 
 class MlaError(RuntimeError):
@@ -88,6 +88,8 @@ def load():
     lib.mla_cache_append.restype = st
     lib.mla_cache_append.argtypes = [D, ctypes.POINTER(MlaCache), P, ctypes.c_int64, P, ctypes.c_int32,
                                      ctypes.c_float, P]
+    lib.mla_decode_step_fused.restype = st
+    lib.mla_decode_step_fused.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, P, P, ctypes.c_int32, P, P, P, P]
     lib.mla_recommended_splits.restype = ctypes.c_int32
     lib.mla_recommended_splits.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
     _lib = lib
@@ -256,6 +258,35 @@ def mla_expand_v(d, o_lat, w_uv, out=None, stream=None):
     _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), o_lat.device)
     _check(load().mla_expand_v(ctypes.byref(d), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream)))
     return out
+
+
+def mla_decode_step_fused(d, cache, q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, out=None, o_lat=None,
+                          lse=None, want_latent=False, stream=None):
+    """The three decode stages in one launch (short contexts).  Returns out,
+    or (out, o_lat, lse) with want_latent=True."""
+    B, H = d.batch, d.num_heads
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", torch.bfloat16, (B, H, d.qk_nope_head_dim))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
+    _expect(w_uk, "w_uk", torch.bfloat16, (H, d.qk_nope_head_dim, d.kv_lora_rank), dev)
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, d.v_head_dim, d.kv_lora_rank), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if out is None:
+        out = torch.empty((B, H, d.v_head_dim), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), dev)
+    if want_latent:
+        if o_lat is None:
+            o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    if o_lat is not None:
+        _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_decode_step_fused(ctypes.byref(d), ctypes.byref(cache), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
+                                        _ptr(w_uv), _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(o_lat),
+                                        _ptr(lse), _stream(stream)))
+    return (out, o_lat, lse) if want_latent else out
 
 
 def mla_cache_append(d, cache, kv_in, positions, rope_base=10000.0, stream=None):

@@ -88,6 +88,51 @@ int32_t split_chunk(int32_t max_seq_len, int32_t num_splits) {
   return (int32_t)(((per + 31) / 32) * 32);
 }
 
+// Checks of a cache description read by decode (shared by mla_decode_latent and
+// mla_decode_step_fused).
+mla_status check_read_cache(const mla_dims* dims, const mla_cache* cache, int32_t max_seq_len, const char* where) {
+  if (cache->dtype != MLA_DTYPE_BF16 && cache->dtype != MLA_DTYPE_FP8_E4M3)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  // 16-byte copies: row strides must be multiples of 16 bytes
+  const int64_t stride_align = fp8 ? 16 : 8;
+  REQUIRE_PTR(cache->kv, "mla_cache.kv", where);
+  REQUIRE_PTR(cache->pe, "mla_cache.pe", where);
+  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->kv_stride, dims->kv_lora_rank, (long long)stride_align, where);
+  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % stride_align != 0)
+    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of %lld elements (%s)",
+                (long long)cache->pe_stride, dims->qk_rope_head_dim, (long long)stride_align, where);
+  // the kernels address the rows of one 32-token tile with 32-bit offsets
+  if (cache->kv_stride > (int64_t)1 << 23 || cache->pe_stride > (int64_t)1 << 23)
+    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld / pe_stride %lld above %lld elements (%s)",
+                (long long)cache->kv_stride, (long long)cache->pe_stride, (long long)1 << 23, where);
+  if (fp8) {
+    if (cache->token_scale == nullptr)
+      return fail(MLA_ERR_NULL, "mla_cache.token_scale is NULL (E4M3 cache needs one fp32 scale per slot, %s)", where);
+    if (reinterpret_cast<uintptr_t>(cache->token_scale) % 4 != 0)
+      return fail(MLA_ERR_ALIGN, "mla_cache.token_scale is not 4-byte aligned (%s)", where);
+  } else if (cache->token_scale != nullptr) {
+    return fail(MLA_ERR_BUFFER, "mla_cache.token_scale must be NULL for a bf16 cache (%s)", where);
+  }
+  if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
+  if (cache->block_table != nullptr) {
+    if (cache->block_size <= 0 || cache->block_size % 32 != 0)
+      return fail(MLA_ERR_BAD_LENGTH, "mla_cache.block_size %d must be a positive multiple of 32 (%s)",
+                  cache->block_size, where);
+    const int64_t need = ((int64_t)max_seq_len + cache->block_size - 1) / cache->block_size;
+    if (cache->max_blocks_per_seq < need)
+      return fail(MLA_ERR_BUFFER, "mla_cache.max_blocks_per_seq %d < %lld blocks for max_seq_len %d (%s)",
+                  cache->max_blocks_per_seq, (long long)need, max_seq_len, where);
+  } else {
+    if (cache->seq_stride < max_seq_len)
+      return fail(MLA_ERR_BUFFER, "mla_cache.seq_stride %lld < max_seq_len %d (contiguous cache, %s)",
+                  (long long)cache->seq_stride, max_seq_len, where);
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,51 +218,15 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   mla_status st = check_dims(dims, where);
   if (st != MLA_OK) return st;
   if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
-  if (cache->dtype != MLA_DTYPE_BF16 && cache->dtype != MLA_DTYPE_FP8_E4M3)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_cache.dtype %d unknown (%s)", cache->dtype, where);
+  st = check_read_cache(dims, cache, max_seq_len, where);
+  if (st != MLA_OK) return st;
   const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
-  // 16-byte copies: row strides must be multiples of 16 bytes
-  const int64_t stride_align = fp8 ? 16 : 8;
-  REQUIRE_PTR(cache->kv, "mla_cache.kv", where);
-  REQUIRE_PTR(cache->pe, "mla_cache.pe", where);
   REQUIRE_PTR(q_lat, "q_lat", where);
   REQUIRE_PTR(q_pe, "q_pe", where);
   if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
-  if (cache->kv_stride < dims->kv_lora_rank || cache->kv_stride % stride_align != 0)
-    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld must be >= %d and a multiple of %lld elements (%s)",
-                (long long)cache->kv_stride, dims->kv_lora_rank, (long long)stride_align, where);
-  if (cache->pe_stride < dims->qk_rope_head_dim || cache->pe_stride % stride_align != 0)
-    return fail(MLA_ERR_BUFFER, "mla_cache.pe_stride %lld must be >= %d and a multiple of %lld elements (%s)",
-                (long long)cache->pe_stride, dims->qk_rope_head_dim, (long long)stride_align, where);
-  // the kernels address the rows of one 32-token tile with 32-bit offsets
-  if (cache->kv_stride > (int64_t)1 << 23 || cache->pe_stride > (int64_t)1 << 23)
-    return fail(MLA_ERR_BUFFER, "mla_cache.kv_stride %lld / pe_stride %lld above %lld elements (%s)",
-                (long long)cache->kv_stride, (long long)cache->pe_stride, (long long)1 << 23, where);
-  if (fp8) {
-    if (cache->token_scale == nullptr)
-      return fail(MLA_ERR_NULL, "mla_cache.token_scale is NULL (E4M3 cache needs one fp32 scale per slot, %s)", where);
-    if (reinterpret_cast<uintptr_t>(cache->token_scale) % 4 != 0)
-      return fail(MLA_ERR_ALIGN, "mla_cache.token_scale is not 4-byte aligned (%s)", where);
-  } else if (cache->token_scale != nullptr) {
-    return fail(MLA_ERR_BUFFER, "mla_cache.token_scale must be NULL for a bf16 cache (%s)", where);
-  }
-  if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
   if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
   if ((int64_t)dims->batch * num_splits > (int64_t)1 << 30)
     return fail(MLA_ERR_BAD_LENGTH, "batch * num_splits too large (%s)", where);
-  if (cache->block_table != nullptr) {
-    if (cache->block_size <= 0 || cache->block_size % 32 != 0)
-      return fail(MLA_ERR_BAD_LENGTH, "mla_cache.block_size %d must be a positive multiple of 32 (%s)",
-                  cache->block_size, where);
-    const int64_t need = ((int64_t)max_seq_len + cache->block_size - 1) / cache->block_size;
-    if (cache->max_blocks_per_seq < need)
-      return fail(MLA_ERR_BUFFER, "mla_cache.max_blocks_per_seq %d < %lld blocks for max_seq_len %d (%s)",
-                  cache->max_blocks_per_seq, (long long)need, max_seq_len, where);
-  } else {
-    if (cache->seq_stride < max_seq_len)
-      return fail(MLA_ERR_BUFFER, "mla_cache.seq_stride %lld < max_seq_len %d (contiguous cache, %s)",
-                  (long long)cache->seq_stride, max_seq_len, where);
-  }
   if (num_splits == 1) {
     REQUIRE_PTR(o_lat, "o_lat", where);
     if (lse == nullptr) return fail(MLA_ERR_NULL, "lse is NULL (%s)", where);
@@ -257,6 +266,52 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
   a.o_lat = static_cast<uint16_t*>(o_lat);
   a.lse = lse;
   return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
+}
+
+mla_status mla_decode_step_fused(const mla_dims* dims, const mla_cache* cache, const void* q_nope, const void* q_pe,
+                                 const void* w_uk, const void* w_uv, const int32_t* seq_lens, int32_t max_seq_len,
+                                 void* out, void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_decode_step_fused";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
+  st = check_read_cache(dims, cache, max_seq_len, where);
+  if (st != MLA_OK) return st;
+  REQUIRE_PTR(q_nope, "q_nope", where);
+  REQUIRE_PTR(q_pe, "q_pe", where);
+  REQUIRE_PTR(w_uk, "w_uk", where);
+  REQUIRE_PTR(w_uv, "w_uv", where);
+  if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
+  REQUIRE_PTR(out, "out", where);
+  if (o_lat != nullptr && !aligned16(o_lat)) return fail(MLA_ERR_ALIGN, "o_lat is not 16-byte aligned (%s)", where);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  if ((int64_t)dims->batch * dims->num_heads > (int64_t)1 << 30)
+    return fail(MLA_ERR_BAD_LENGTH, "batch * num_heads too large (%s)", where);
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  mla::FusedStepArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.kv = static_cast<const char*>(cache->kv);
+  a.pe = static_cast<const char*>(cache->pe);
+  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
+  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
+  a.seq_stride = cache->seq_stride;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.token_scale = cache->token_scale;
+  a.seq_lens = seq_lens;
+  a.batch = dims->batch;
+  a.num_heads = dims->num_heads;
+  a.max_seq_len = max_seq_len;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  a.out = static_cast<uint16_t*>(out);
+  a.o_lat = static_cast<uint16_t*>(o_lat);
+  a.lse = lse;
+  return launch_result(mla::launch_decode_step_fused(a, fp8, static_cast<hipStream_t>(stream)), where);
 }
 
 mla_status mla_cache_append(const mla_dims* dims, const mla_cache* cache, const void* kv_in, int64_t in_stride,

@@ -184,3 +184,36 @@ def test_cache_append_validation(lib):
     # nothing to append: accepted, and nothing is launched (this machine has no GPU)
     assert _append(lib, d, cache(), num_new=0) == 0 and err() == ""
     assert _append(lib, d, cache(block_table=4096, block_size=48, max_blocks_per_seq=4), num_new=0) == 0
+
+
+def test_decode_step_fused_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    P = ctypes.c_void_p
+    base = dict(dtype=0, kv=1024, pe=2048, kv_stride=576, pe_stride=576, token_scale=None, seq_stride=64,
+                block_table=None, block_size=0, max_blocks_per_seq=0)
+
+    def call(cache=True, max_len=64, qn=16, qpe=16, wuk=16, wuv=16, lens=16, out=16, o_lat=0, lse=0, dd=d, **kw):
+        c = dict(base)
+        c.update(kw)
+        cc = binding.MlaCache(**c)
+        return lib.mla_decode_step_fused(ctypes.byref(dd), ctypes.byref(cc) if cache else None, P(qn), P(qpe),
+                                         P(wuk) if wuk else None, P(wuv) if wuv else None, P(lens) if lens else None,
+                                         max_len, P(out) if out else None, P(o_lat) if o_lat else None,
+                                         P(lse) if lse else None, None)
+
+    def err():
+        return lib.mla_last_error().decode()
+
+    assert call(dd=binding.dims(2, 0, 0.07)) == 2 and "num_heads" in err()
+    assert call(cache=False) == 1 and "cache" in err()
+    assert call(dtype=1) == 1 and "token_scale" in err()
+    assert call(kv_stride=500) == 5 and "kv_stride" in err()
+    assert call(max_len=0) == 4
+    assert call(seq_stride=32) == 5 and "seq_stride" in err()
+    assert call(wuk=0) == 1 and "w_uk" in err()
+    assert call(wuv=8) == 6 and "w_uv" in err()
+    assert call(lens=0) == 1 and "seq_lens" in err()
+    assert call(out=0) == 1 and "out" in err()
+    assert call(o_lat=8) == 6 and "o_lat" in err()
+    assert call(lse=2) == 6 and "lse" in err()
+    assert call(block_table=4096, block_size=48, max_blocks_per_seq=4) == 4
