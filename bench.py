@@ -16,6 +16,10 @@ Prints one JSON line:
                   each launch, against 8 TB/s
   fused_step      (contexts up to 2048) mla_decode_step_fused, the same step
                   in one launch, GPU time per step from graph replays
+  naive           mla_naive_decode (expand every step) on the same inputs,
+                  and the absorbed step's speedup over it
+  crossover_v2lite_b1   naive vs absorbed vs fused against context length
+                  (H=16, one sequence)
   append          mla_cache_append on the same shape (timed apart from the
                   step): one token per sequence, and the whole history in one
                   call against the HBM roofline (input read + cache write bytes)
@@ -110,9 +114,9 @@ COPY_ELEMS = 1 << 28          # float32 elements of the calibration copy (1 GiB 
 PMC_COMMANDS = [
     "export TMPDIR=/tmp",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $PWD/gpurun_out/pmc_fetch -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $PWD/gpurun_out/pmc_write -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive",
     "python bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
     "gpurun_out/pmc_write/run_counter_collection.csv",
 ]
@@ -173,6 +177,97 @@ def summarize_counters(args, fetch_csv, write_csv):
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
+
+
+def graph_time_per_call(fn, n_cap, reps):
+    """GPU time per call of fn: n_cap calls captured in one HIP graph, replayed
+    `reps` times between two events (one untimed replay first)."""
+    import torch
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_cap):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e-3 / (reps * n_cap)
+
+
+NAIVE_MAX_WORKSPACE = 16 << 30   # expanded rows the naive baseline may hold
+CROSSOVER_CONTEXTS = [64, 256, 1024, 4096, 16384]
+
+
+def bench_naive(x0, d, dev, absorbed_step_s):
+    """The naive (expand every step) decode on the workload, against the
+    absorbed step; None when its expanded rows would exceed 16 GiB."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding
+
+    need = binding.mla_naive_workspace_bytes(d, x0.max_seq_len)
+    if need > NAIVE_MAX_WORKSPACE:
+        return None
+    cache = binding.make_cache(x0.kv_rows, x0.pe_rows, seq_stride=x0.seq_stride, block_table=x0.block_table,
+                               block_size=x0.block_size, token_scale=x0.token_scale)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((x0.batch, x0.heads, 128), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        binding.mla_naive_decode(d, cache, x0.q_nope, x0.q_pe, x0.w_uk, x0.w_uv, x0.seq_lens, x0.max_seq_len,
+                                 workspace=ws, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    t = graph_time_per_call(call, 4, 3)
+    flops = 2 * 2 * x0.heads * 128 * 512 * int(x0.seq_lens.to(torch.int64).sum().item())
+    del ws
+    torch.cuda.empty_cache()
+    return {"kernel": "mla_naive_decode", "step_us": round(t * 1e6, 2),
+            "absorbed_speedup": round(t / absorbed_step_s, 2),
+            "expand_tflops": round(flops / t / 1e12, 1), "workspace_bytes": need}
+
+
+def bench_crossover(dev):
+    """Naive vs absorbed (four calls) vs fused one-launch step against context
+    length at the V2-Lite shape with one sequence (H=16), the setting of the
+    pages' naive-vs-absorbed latency comparison; GPU time per step from graph
+    replays."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    rows = []
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    for T in CROSSOVER_CONTEXTS:
+        x = datagen.make_inputs(datagen.WORKLOADS["v2lite_b64_s4096"], device=dev, batch=1, seq_len=T)
+        d = binding.dims(1, x.heads, x.scale)
+        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+        P = binding.mla_recommended_splits(d, T, ncu)
+        step = binding.DecodeStep(d, cache, x.seq_lens, T, P, dev)
+        ws = torch.empty(binding.mla_naive_workspace_bytes(d, T), dtype=torch.uint8, device=dev)
+        out = torch.empty((1, x.heads, 128), dtype=torch.bfloat16, device=dev)
+        absorbed = lambda: step(x.q_nope, x.q_pe, x.w_uk, x.w_uv)
+        naive = lambda: binding.mla_naive_decode(d, cache, x.q_nope, x.q_pe, x.w_uk, x.w_uv, x.seq_lens, T,
+                                                 workspace=ws, out=out)
+        fused = lambda: binding.mla_decode_step_fused(d, cache, x.q_nope, x.q_pe, x.w_uk, x.w_uv, x.seq_lens, T,
+                                                      out=out)
+        for f in (absorbed, naive, fused):
+            f()
+        torch.cuda.synchronize()
+        row = {"context": T, "splits": P,
+               "absorbed_us": round(graph_time_per_call(absorbed, 16, 4) * 1e6, 2),
+               "naive_us": round(graph_time_per_call(naive, 16, 4) * 1e6, 2)}
+        if T <= FUSED_MAX_CONTEXT:
+            row["fused_us"] = round(graph_time_per_call(fused, 16, 4) * 1e6, 2)
+        rows.append(row)
+        del ws, step
+    torch.cuda.empty_cache()
+    return rows
 
 
 FUSED_MAX_CONTEXT = 2048   # the fused one-launch step is timed on short contexts only
@@ -300,6 +395,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough for > 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
+    ap.add_argument("--no-naive", action="store_true", help="skip the naive-decode baseline and context sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
@@ -457,6 +553,9 @@ def main():
     }
     if x0.max_seq_len <= FUSED_MAX_CONTEXT:
         result["fused_step"] = bench_fused_step(x0, d, dev, args.steps)
+    if not args.no_naive:
+        result["naive"] = bench_naive(x0, d, dev, t_step)
+        result["crossover_v2lite_b1"] = bench_crossover(dev)
     if not args.no_append:
         result["append"] = bench_append(x0, d, dev, args.steps)
     if not args.no_cpu_baseline:

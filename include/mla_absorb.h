@@ -15,7 +15,7 @@
  * and mla_cache_append, which writes new tokens (latent row + rotated RoPE
  * key, bf16 or E4M3 with a per-token scale) into the cache that decode reads,
  * and mla_decode_step_fused, the three decode stages in one launch for short
- * contexts.
+ * contexts, and mla_naive_decode, the expand-every-step baseline.
  *
  * The method is the one described on the source pages (cited by title):
  *   [AUDIT]  "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界":
@@ -229,6 +229,54 @@ mla_status mla_decode_step_fused(const mla_dims *dims, const mla_cache *cache, c
                                  void *out, void *o_lat, float *lse, void *stream);
 
 /*
+ * Naive decode, the baseline the absorbed path is compared with ([MLA80] §4
+ * path A and §5: the base decode re-applies the up-projections to the whole
+ * latent cache every step; [AUDIT] §2: per-head expanded keys and values).
+ * Every step expands each cached token t < seq_lens[b] into
+ *   k_nope[t,h] = W_UK[h] c_t,  v[t,h] = W_UV[h] c_t      (bf16, in workspace)
+ * and runs multi-head attention with keys [k_nope[t,h] | kR_t] and values
+ * v[t,h]: out[b,h] = sum_t softmax_t(softmax_scale * (q_nope . k_nope +
+ * q_pe . kR_t)) v[t,h].  Same result as the absorbed path up to rounding.
+ *   q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, cache: as in
+ *     mla_absorb_q / mla_decode_latent / mla_expand_v
+ *   workspace  device, at least mla_naive_workspace_bytes() bytes: the
+ *              expanded rows [B, max_seq_len, H, 256] bf16 (k_nope | v),
+ *              owned by the caller and overwritten
+ *   out        device bf16 [B, H, 128] (output)
+ * Two launches (an expansion GEMM on 32x32x16 bf16 MFMAs, then attention).
+ * batch must be at most 65535.
+ */
+mla_status mla_naive_workspace_bytes(const mla_dims *dims, int32_t max_seq_len, size_t *bytes);
+mla_status mla_naive_decode(const mla_dims *dims, const mla_cache *cache, const void *q_nope, const void *q_pe,
+                            const void *w_uk, const void *w_uv, const int32_t *seq_lens, int32_t max_seq_len,
+                            void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/*
+ * Cache append: writes num_new new tokens/*
+ * Cache append: writes num_new new tokens/*
+ * Naive decode, the baseline the absorbed path is compared with ([MLA80] §4
+ * path A and §5: the base decode re-applies the up-projections to the whole
+ * latent cache every step; [AUDIT] §2: per-head expanded keys and values).
+ * Every step expands each cached token t < seq_lens[b] into
+ *   k_nope[t,h] = W_UK[h] c_t,  v[t,h] = W_UV[h] c_t      (bf16, in workspace)
+ * and runs multi-head attention with keys [k_nope[t,h] | kR_t] and values
+ * v[t,h]: out[b,h] = sum_t softmax_t(softmax_scale * (q_nope . k_nope +
+ * q_pe . kR_t)) v[t,h].  Same result as the absorbed path up to rounding.
+ *   q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, cache: as in
+ *     mla_absorb_q / mla_decode_latent / mla_expand_v
+ *   workspace  device, at least mla_naive_workspace_bytes() bytes: the
+ *              expanded rows [B, max_seq_len, H, 256] bf16 (k_nope | v),
+ *              owned by the caller and overwritten
+ *   out        device bf16 [B, H, 128] (output)
+ * Two launches (an expansion GEMM on 32x32x16 bf16 MFMAs, then attention).
+ * batch must be at most 65535.
+ */
+mla_status mla_naive_workspace_bytes(const mla_dims *dims, int32_t max_seq_len, size_t *bytes);
+mla_status mla_naive_decode(const mla_dims *dims, const mla_cache *cache, const void *q_nope, const void *q_pe,
+                            const void *w_uk, const void *w_uv, const int32_t *seq_lens, int32_t max_seq_len,
+                            void *workspace, size_t workspace_bytes, void *out, void *stream);
+
+/*
  * Cache append: writes num_new new tokens/*
  * Cache append: writes num_new new tokens of every sequence into the latent
  * cache.  Each input row is the token's fused down-projection output: 512
@@ -271,7 +319,9 @@ mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const 
  * Recommended num_splits for mla_decode_latent/*
  * Recommended num_splits for mla_decode_latent on a device with `num_cus`
  * compute units: enough workgroups to fill the chip, each split at least
- * 256 tokens.  Host-only.
+ * max_seq_len / 32 tokens, kept within [32, 256] (measured on MI355X: with few
+ * sequences, shorter splits cut latency until the merge and the per-split
+ * setup dominate).  Host-only.
  */
 int32_t mla_recommended_splits(const mla_dims *dims, int32_t max_seq_len, int32_t num_cus);
 

@@ -23,7 +23,8 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
-            "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused"]
+            "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused", "mla_naive_workspace_bytes",
+            "mla_naive_decode"]
 
 
 class MlaError(RuntimeError):
@@ -90,6 +91,11 @@ def load():
                                      ctypes.c_float, P]
     lib.mla_decode_step_fused.restype = st
     lib.mla_decode_step_fused.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, P, P, ctypes.c_int32, P, P, P, P]
+    lib.mla_naive_workspace_bytes.restype = st
+    lib.mla_naive_workspace_bytes.argtypes = [D, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_naive_decode.restype = st
+    lib.mla_naive_decode.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
+                                     P, P]
     lib.mla_recommended_splits.restype = ctypes.c_int32
     lib.mla_recommended_splits.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
     _lib = lib
@@ -287,6 +293,37 @@ def mla_decode_step_fused(d, cache, q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_
                                         _ptr(w_uv), _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(o_lat),
                                         _ptr(lse), _stream(stream)))
     return (out, o_lat, lse) if want_latent else out
+
+
+def mla_naive_workspace_bytes(d, max_seq_len):
+    out = ctypes.c_size_t(0)
+    _check(load().mla_naive_workspace_bytes(ctypes.byref(d), int(max_seq_len), ctypes.byref(out)))
+    return out.value
+
+
+def mla_naive_decode(d, cache, q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, workspace=None, out=None,
+                     stream=None):
+    """Expand-every-step decode (baseline).  workspace: a uint8 device tensor of
+    at least mla_naive_workspace_bytes bytes (allocated here if None)."""
+    B, H = d.batch, d.num_heads
+    dev = q_nope.device
+    _expect(q_nope, "q_nope", torch.bfloat16, (B, H, d.qk_nope_head_dim))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
+    _expect(w_uk, "w_uk", torch.bfloat16, (H, d.qk_nope_head_dim, d.kv_lora_rank), dev)
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, d.v_head_dim, d.kv_lora_rank), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    need = mla_naive_workspace_bytes(d, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty((B, H, d.v_head_dim), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), dev)
+    _check(load().mla_naive_decode(ctypes.byref(d), ctypes.byref(cache), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk),
+                                   _ptr(w_uv), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    return out
 
 
 def mla_cache_append(d, cache, kv_in, positions, rope_base=10000.0, stream=None):

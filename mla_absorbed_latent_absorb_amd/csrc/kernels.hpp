@@ -93,6 +93,29 @@ struct FusedStepArgs {
   float* lse;                 // [B, H] fp32 or null
 };
 
+struct NaiveArgs {
+  const uint16_t* q_nope;     // [B, H, 128] bf16
+  const uint16_t* q_pe;       // [B, H, 64] bf16
+  const uint16_t* w_uk;       // [H, 128, 512] bf16
+  const uint16_t* w_uv;       // [H, 128, 512] bf16
+  const char* kv;             // cache addressing as in DecodeArgs
+  const char* pe;
+  int64_t kv_sb;
+  int64_t pe_sb;
+  int64_t seq_stride;
+  const int32_t* block_table;
+  int32_t block_size;
+  int32_t max_blocks;
+  const float* token_scale;
+  const int32_t* seq_lens;    // [B]
+  int32_t batch;
+  int32_t num_heads;
+  int32_t max_seq_len;
+  float scale_log2;           // softmax scale * log2(e)
+  uint16_t* ws;               // [B, max_seq_len, H, 256] bf16: expanded k_nope | v per token and head
+  uint16_t* out;              // [B, H, 128] bf16
+};
+
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
 // 128 heads, bf16 cache: 32-head waves with P.V woven into the next tile's scores.
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);
@@ -100,6 +123,8 @@ hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_decode_step_fused(const FusedStepArgs& a, bool fp8, hipStream_t stream);
+// Naive decode: expansion GEMM into a.ws, then attention over the expanded rows.
+hipError_t launch_naive_decode(const NaiveArgs& a, bool fp8, hipStream_t stream);
 // fp8 selects the E4M3 cache encoding.
 hipError_t launch_cache_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 

@@ -314,6 +314,62 @@ mla_status mla_decode_step_fused(const mla_dims* dims, const mla_cache* cache, c
   return launch_result(mla::launch_decode_step_fused(a, fp8, static_cast<hipStream_t>(stream)), where);
 }
 
+mla_status mla_naive_workspace_bytes(const mla_dims* dims, int32_t max_seq_len, size_t* bytes) {
+  const char* where = "mla_naive_workspace_bytes";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr) return fail(MLA_ERR_NULL, "bytes is NULL (%s)", where);
+  if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
+  *bytes = (size_t)dims->batch * (size_t)max_seq_len * (size_t)dims->num_heads * (dims->qk_nope_head_dim + dims->v_head_dim) * 2;
+  return ok();
+}
+
+mla_status mla_naive_decode(const mla_dims* dims, const mla_cache* cache, const void* q_nope, const void* q_pe,
+                            const void* w_uk, const void* w_uv, const int32_t* seq_lens, int32_t max_seq_len,
+                            void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  const char* where = "mla_naive_decode";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
+  st = check_read_cache(dims, cache, max_seq_len, where);
+  if (st != MLA_OK) return st;
+  REQUIRE_PTR(q_nope, "q_nope", where);
+  REQUIRE_PTR(q_pe, "q_pe", where);
+  REQUIRE_PTR(w_uk, "w_uk", where);
+  REQUIRE_PTR(w_uv, "w_uv", where);
+  if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
+  REQUIRE_PTR(workspace, "workspace", where);
+  REQUIRE_PTR(out, "out", where);
+  const size_t need = (size_t)dims->batch * (size_t)max_seq_len * (size_t)dims->num_heads * 256 * 2;
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_BUFFER, "workspace_bytes %zu < %zu needed (B * max_seq_len * H * 256 bf16, %s)",
+                workspace_bytes, need, where);
+  if (dims->batch > 65535) return fail(MLA_ERR_BAD_LENGTH, "batch %d above 65535 (%s)", dims->batch, where);
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  mla::NaiveArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.w_uk = static_cast<const uint16_t*>(w_uk);
+  a.w_uv = static_cast<const uint16_t*>(w_uv);
+  a.kv = static_cast<const char*>(cache->kv);
+  a.pe = static_cast<const char*>(cache->pe);
+  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
+  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
+  a.seq_stride = cache->seq_stride;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.token_scale = cache->token_scale;
+  a.seq_lens = seq_lens;
+  a.batch = dims->batch;
+  a.num_heads = dims->num_heads;
+  a.max_seq_len = max_seq_len;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  a.ws = static_cast<uint16_t*>(workspace);
+  a.out = static_cast<uint16_t*>(out);
+  return launch_result(mla::launch_naive_decode(a, fp8, static_cast<hipStream_t>(stream)), where);
+}
+
 mla_status mla_cache_append(const mla_dims* dims, const mla_cache* cache, const void* kv_in, int64_t in_stride,
                             const int32_t* positions, int32_t num_new, float rope_base, void* stream) {
   const char* where = "mla_cache_append";
@@ -401,7 +457,11 @@ int32_t mla_recommended_splits(const mla_dims* dims, int32_t max_seq_len, int32_
   const int wg_per_cu = dims->num_heads >= 128 ? 1 : (dims->num_heads >= 64 ? 2 : 4);
   const int64_t want = (int64_t)num_cus * wg_per_cu;
   int64_t p = (want + dims->batch - 1) / dims->batch;
-  const int64_t max_p = (max_seq_len + 255) / 256;
+  // shortest split: 1/32 of the context, within [32, 256] tokens (each split
+  // pays a fixed prologue and epilogue; short splits keep few sequences busy)
+  int64_t min_tokens = max_seq_len / 32;
+  min_tokens = min_tokens < 32 ? 32 : (min_tokens > 256 ? 256 : min_tokens);
+  const int64_t max_p = (max_seq_len + min_tokens - 1) / min_tokens;
   if (p > max_p) p = max_p;
   if (p < 1) p = 1;
   return (int32_t)p;

@@ -217,3 +217,28 @@ def test_decode_step_fused_validation(lib):
     assert call(o_lat=8) == 6 and "o_lat" in err()
     assert call(lse=2) == 6 and "lse" in err()
     assert call(block_table=4096, block_size=48, max_blocks_per_seq=4) == 4
+
+
+def test_naive_decode_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    P = ctypes.c_void_p
+    need = binding.mla_naive_workspace_bytes(d, 64)
+    assert need == 2 * 64 * 16 * 256 * 2
+    cache = binding.MlaCache(dtype=0, kv=1024, pe=2048, kv_stride=576, pe_stride=576, token_scale=None,
+                             seq_stride=64, block_table=None, block_size=0, max_blocks_per_seq=0)
+
+    def call(ws=4096, ws_bytes=need, out=16, wuk=16, max_len=64):
+        return lib.mla_naive_decode(ctypes.byref(d), ctypes.byref(cache), P(16), P(16), P(wuk) if wuk else None,
+                                    P(16), P(16), max_len, P(ws) if ws else None, ws_bytes, P(out) if out else None,
+                                    None)
+
+    def err():
+        return lib.mla_last_error().decode()
+
+    assert call(ws=0) == 1 and "workspace" in err()
+    assert call(ws_bytes=need - 1) == 5 and "workspace_bytes" in err()
+    assert call(out=0) == 1 and "out" in err()
+    assert call(wuk=0) == 1 and "w_uk" in err()
+    assert call(max_len=0) == 4
+    with pytest.raises(binding.MlaError):
+        binding.mla_naive_workspace_bytes(d, 0)
