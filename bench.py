@@ -144,6 +144,30 @@ def _pick(means, pattern):
     return hits[0]
 
 
+def summarize_trace(trace_csv):
+    """Print a markdown table of this library's kernels from a rocprofv3
+    --kernel-trace CSV, one line per (kernel, launch grid): calls and
+    average / min / max duration in microseconds."""
+    import csv
+    groups = {}
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if "mla::" not in name:
+                continue
+            short = name.replace("(anonymous namespace)::", "").split("(")[0]
+            short = short.replace("void ", "").replace("mla::", "")
+            grid = "x".join(str(int(row[k]) // (int(row[w]) if k == "Grid_Size_X" else 1))
+                            for k, w in (("Grid_Size_X", "Workgroup_Size_X"), ("Grid_Size_Y", ""),
+                                         ("Grid_Size_Z", "")))
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3
+            groups.setdefault((short, grid), []).append(d)
+    print("| kernel | workgroups (x*y*z) | calls | average (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|")
+    for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k}` | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+
+
 def summarize_counters(args, fetch_csv, write_csv):
     """HBM bytes per decode launch = counter KiB x 1024, each counter scaled by
     (known bytes / counter reading) of the calibration copy kernel."""
@@ -399,11 +423,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="print this library's kernel durations from a rocprofv3 --kernel-trace CSV, grouped by "
+                         "kernel and launch grid, and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM byte counter file from two rocprofv3 --pmc runs of "
                          "'bench.py --copy-calibration' (FETCH_SIZE, then WRITE_SIZE) and exit")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_counters:
         summarize_counters(args, *args.summarize_counters)
         return
