@@ -185,6 +185,33 @@ mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const
                              float *lse, void *stream);
 
 /*
+ * Absorbed chunked prefill ([MLA80] §2 cache test and §5: prefill, then
+ * decode against the cache; [AUDIT] §2.2-§2.4: absorbed scores and latent
+ * aggregation; [G5SPEC] use case 2: prefill is compute-bound): num_q query
+ * tokens per sequence at positions q_start[b] + i, i < num_q, each attending
+ * causally to the cached tokens 0 .. q_start[b] + i (its own row included, so
+ * the chunk must be in the cache already, e.g. by mla_cache_append):
+ *   s_t   = softmax_scale * (q_lat[b,i,h] . c_t + q_pe[b,i,h] . kR_t)
+ *   o_lat[b,i,h] = sum_t softmax(s)_t c_t,  lse[b,i,h] = ln sum_t exp(s_t)
+ *   q_lat   device bf16 [B, num_q, H, 512]  (mla_absorb_q with batch B*num_q)
+ *   q_pe    device bf16 [B, num_q, H, 64]   (rotated at each query's position)
+ *   q_start device int32 [B]
+ *   max_seq_len  host bound of q_start[b] + num_q (positions past it are
+ *                clamped to it); sizes the split chunks as in decode
+ *   num_splits, o_part, lse_part, o_lat, lse: as mla_decode_latent with B*num_q
+ *                query rows (o_lat [B, num_q, H, 512], partials
+ *                [B*num_q, P, H, 512], merged by mla_combine_splits with batch
+ *                B*num_q)
+ * Every query row runs the decode kernel's schedule over its own causal
+ * prefix (the 576-wide tile of cached rows feeds the query's 128 heads, or
+ * 16..64 heads for smaller H); the chunk's MLP projections around it are
+ * mla_absorb_q / mla_expand_v with batch B*num_q.
+ */
+mla_status mla_prefill_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat, const void *q_pe,
+                              const int32_t *q_start, int32_t num_q, int32_t max_seq_len, int32_t num_splits,
+                              void *o_part, float *lse_part, void *o_lat, float *lse, void *stream);
+
+/*
  * Split-KV merge: LSE = ln sum_i exp(lse_part[b,i,h]),
  * o_lat[b,h] = sum_i exp(lse_part[b,i,h] - LSE) * o_part[b,i,h]; splits with
  * lse = -inf carry no weight.

@@ -24,7 +24,7 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
             "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused", "mla_naive_workspace_bytes",
-            "mla_naive_decode"]
+            "mla_naive_decode", "mla_prefill_latent"]
 
 
 class MlaError(RuntimeError):
@@ -96,6 +96,9 @@ def load():
     lib.mla_naive_decode.restype = st
     lib.mla_naive_decode.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, P, P, ctypes.c_int32, P, ctypes.c_size_t,
                                      P, P]
+    lib.mla_prefill_latent.restype = st
+    lib.mla_prefill_latent.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, P, P, P, P, P]
     lib.mla_recommended_splits.restype = ctypes.c_int32
     lib.mla_recommended_splits.argtypes = [D, ctypes.c_int32, ctypes.c_int32]
     _lib = lib
@@ -233,6 +236,43 @@ def mla_decode_latent(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_splits=1
                                     _ptr(lse_part) if num_splits > 1 else None,
                                     _ptr(o_lat) if num_splits == 1 else None,
                                     _ptr(lse) if num_splits == 1 else None, _stream(stream)))
+    return (o_lat, lse) if num_splits == 1 else (o_part, lse_part)
+
+
+def mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_seq_len, num_splits=1, o_part=None, lse_part=None,
+                       o_lat=None, lse=None, stream=None):
+    """Causal latent attention of a prefill chunk: q_lat [B, L, H, 512],
+    q_pe [B, L, H, 64], q_start [B] int32.  num_splits == 1 returns
+    (o_lat [B, L, H, 512], lse [B, L, H]); num_splits > 1 returns the partials
+    (o_part [B*L, P, H, 512], lse_part [B*L, P, H])."""
+    B, H = d.batch, d.num_heads
+    dev = q_lat.device
+    if q_lat.dim() != 4:
+        raise ValueError("q_lat must be [B, L, H, 512]")
+    L = q_lat.shape[1]
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, L, H, d.kv_lora_rank))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, L, H, d.qk_rope_head_dim), dev)
+    _expect(q_start, "q_start", torch.int32, (B,), dev)
+    if num_splits == 1:
+        if o_lat is None:
+            o_lat = torch.empty((B, L, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((B, L, H), dtype=torch.float32, device=dev)
+        _expect(o_lat, "o_lat", torch.bfloat16, (B, L, H, d.kv_lora_rank), dev)
+        _expect(lse, "lse", torch.float32, (B, L, H), dev)
+    else:
+        if o_part is None:
+            o_part = torch.empty((B * L, num_splits, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+        if lse_part is None:
+            lse_part = torch.empty((B * L, num_splits, H), dtype=torch.float32, device=dev)
+        _expect(o_part, "o_part", torch.bfloat16, (B * L, num_splits, H, d.kv_lora_rank), dev)
+        _expect(lse_part, "lse_part", torch.float32, (B * L, num_splits, H), dev)
+    _check(load().mla_prefill_latent(ctypes.byref(d), ctypes.byref(cache), _ptr(q_lat), _ptr(q_pe), _ptr(q_start),
+                                     int(L), int(max_seq_len), int(num_splits),
+                                     _ptr(o_part) if num_splits > 1 else None,
+                                     _ptr(lse_part) if num_splits > 1 else None,
+                                     _ptr(o_lat) if num_splits == 1 else None,
+                                     _ptr(lse) if num_splits == 1 else None, _stream(stream)))
     return (o_lat, lse) if num_splits == 1 else (o_part, lse_part)
 
 

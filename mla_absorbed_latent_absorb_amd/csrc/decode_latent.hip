@@ -71,11 +71,13 @@ void decode_latent_kernel(DecodeArgs a) {
   const int hl = lane & 15;   // row/column within a 16-block
   const int g4 = lane >> 4;   // 16-lane group
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int b = item / a.num_splits;
+  const int b = item / a.num_splits;  // query row: its queries and outputs
   const int split = item - b * a.num_splits;
+  const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
   const int h = w * 16 + hl;  // head whose scores this lane computes
 
-  int T = a.seq_lens[b];
+  // decode: the sequence's length; prefill: causal, tokens up to the query's own position
+  int T = a.q_start == nullptr ? a.seq_lens[b] : a.q_start[cb] + (b - cb * a.q_per_seq) + 1;
   T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
   const int t_begin = split * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
@@ -134,10 +136,10 @@ void decode_latent_kernel(DecodeArgs a) {
       // the compiler wait for every tile copy in flight before using it.
       const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
           reinterpret_cast<uintptr_t>(a.block_table));
-      const int blk = table[(size_t)b * a.max_blocks + t0 / a.block_size];
+      const int blk = table[(size_t)cb * a.max_blocks + t0 / a.block_size];
       ts.slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
     } else {
-      ts.slot0 = (int64_t)b * a.seq_stride + t0;
+      ts.slot0 = (int64_t)cb * a.seq_stride + t0;
     }
     ts.dst = lds0 + buf * (FP8 ? kRawTileBytes : kTileBytes);
     return ts;

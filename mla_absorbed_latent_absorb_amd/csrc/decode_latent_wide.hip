@@ -147,11 +147,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   const int h32 = lane & 31;
   const int g2 = lane >> 5;
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int b = item / a.num_splits;
+  const int b = item / a.num_splits;  // query row: its queries and outputs
   const int split = item - b * a.num_splits;
+  const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
   const int col0 = w * C;  // first latent column of the wave's P.V share
 
-  int T = a.seq_lens[b];
+  // decode: the sequence's length; prefill: causal, tokens up to the query's own position
+  int T = a.q_start == nullptr ? a.seq_lens[b] : a.q_start[cb] + (b - cb * a.q_per_seq) + 1;
   T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
   const int t_begin = split * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
@@ -194,10 +196,10 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       // tile copy in flight before using it
       const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
           reinterpret_cast<uintptr_t>(a.block_table));
-      const int blk = table[(size_t)b * a.max_blocks + t0 / a.block_size];
+      const int blk = table[(size_t)cb * a.max_blocks + t0 / a.block_size];
       slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
     } else {
-      slot0 = (int64_t)b * a.seq_stride + t0;
+      slot0 = (int64_t)cb * a.seq_stride + t0;
     }
     ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
     ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);

@@ -20,7 +20,9 @@ struct DecodeArgs {
   const float* token_scale;   // E4M3 cache: one fp32 scale per slot (else null)
   int32_t fp8;                // cache holds OCP E4M3 codes
   const int32_t* seq_lens;    // [B]
-  int32_t batch;
+  int32_t q_per_seq;          // query rows per cached sequence: 1 (decode) or L (prefill chunk)
+  const int32_t* q_start;     // prefill: [B] position of each sequence's first query; null: decode
+  int32_t batch;              // query rows (decode: sequences; prefill: sequences * L)
   int32_t num_heads;
   int32_t num_splits;
   int32_t chunk;              // tokens per split, multiple of 32

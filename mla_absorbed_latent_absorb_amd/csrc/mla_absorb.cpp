@@ -133,6 +133,69 @@ mla_status check_read_cache(const mla_dims* dims, const mla_cache* cache, int32_
   return MLA_OK;
 }
 
+// Latent attention for decode (one query row per sequence, lengths from
+// seq_lens) or a prefill chunk (q_per_seq query rows per sequence, causal
+// lengths from q_start); the caller has checked the mode-specific arguments.
+mla_status latent_attention_rows(const char* where, const mla_dims* dims, const mla_cache* cache, const void* q_lat,
+                                 const void* q_pe, const int32_t* seq_lens, const int32_t* q_start,
+                                 int32_t q_per_seq, int32_t max_seq_len, int32_t num_splits, void* o_part,
+                                 float* lse_part, void* o_lat, float* lse, void* stream) {
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
+  st = check_read_cache(dims, cache, max_seq_len, where);
+  if (st != MLA_OK) return st;
+  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
+  REQUIRE_PTR(q_lat, "q_lat", where);
+  REQUIRE_PTR(q_pe, "q_pe", where);
+  if (q_start == nullptr && seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
+  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
+  const int64_t rows = (int64_t)dims->batch * q_per_seq;
+  if (rows * num_splits > (int64_t)1 << 30)
+    return fail(MLA_ERR_BAD_LENGTH, "query rows * num_splits too large (%s)", where);
+  if (num_splits == 1) {
+    REQUIRE_PTR(o_lat, "o_lat", where);
+    if (lse == nullptr) return fail(MLA_ERR_NULL, "lse is NULL (%s)", where);
+    if (o_part != nullptr || lse_part != nullptr)
+      return fail(MLA_ERR_BUFFER, "o_part/lse_part must be NULL when num_splits == 1 (%s)", where);
+  } else {
+    REQUIRE_PTR(o_part, "o_part", where);
+    if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+    if (o_lat != nullptr || lse != nullptr)
+      return fail(MLA_ERR_BUFFER, "o_lat/lse must be NULL when num_splits > 1; merge with mla_combine_splits (%s)",
+                  where);
+  }
+
+  mla::DecodeArgs a{};
+  a.q_lat = static_cast<const uint16_t*>(q_lat);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.kv = static_cast<const char*>(cache->kv);
+  a.pe = static_cast<const char*>(cache->pe);
+  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
+  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
+  a.token_scale = cache->token_scale;
+  a.fp8 = fp8 ? 1 : 0;
+  a.seq_stride = cache->seq_stride;
+  a.block_table = cache->block_table;
+  a.block_size = cache->block_size;
+  a.max_blocks = cache->max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.q_per_seq = q_per_seq;
+  a.q_start = q_start;
+  a.batch = (int32_t)rows;
+  a.num_heads = dims->num_heads;
+  a.num_splits = num_splits;
+  a.chunk = split_chunk(max_seq_len, num_splits);
+  a.max_seq_len = max_seq_len;
+  a.scale = dims->softmax_scale;
+  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
+  a.o_part = static_cast<uint16_t*>(o_part);
+  a.lse_part = lse_part;
+  a.o_lat = static_cast<uint16_t*>(o_lat);
+  a.lse = lse;
+  return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,57 +278,20 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
                              const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_part,
                              float* lse_part, void* o_lat, float* lse, void* stream) {
   const char* where = "mla_decode_latent";
-  mla_status st = check_dims(dims, where);
-  if (st != MLA_OK) return st;
-  if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
-  st = check_read_cache(dims, cache, max_seq_len, where);
-  if (st != MLA_OK) return st;
-  const bool fp8 = cache->dtype == MLA_DTYPE_FP8_E4M3;
-  REQUIRE_PTR(q_lat, "q_lat", where);
-  REQUIRE_PTR(q_pe, "q_pe", where);
-  if (seq_lens == nullptr) return fail(MLA_ERR_NULL, "seq_lens is NULL (%s)", where);
-  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
-  if ((int64_t)dims->batch * num_splits > (int64_t)1 << 30)
-    return fail(MLA_ERR_BAD_LENGTH, "batch * num_splits too large (%s)", where);
-  if (num_splits == 1) {
-    REQUIRE_PTR(o_lat, "o_lat", where);
-    if (lse == nullptr) return fail(MLA_ERR_NULL, "lse is NULL (%s)", where);
-    if (o_part != nullptr || lse_part != nullptr)
-      return fail(MLA_ERR_BUFFER, "o_part/lse_part must be NULL when num_splits == 1 (%s)", where);
-  } else {
-    REQUIRE_PTR(o_part, "o_part", where);
-    if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
-    if (o_lat != nullptr || lse != nullptr)
-      return fail(MLA_ERR_BUFFER, "o_lat/lse must be NULL when num_splits > 1; merge with mla_combine_splits (%s)",
-                  where);
-  }
+  return latent_attention_rows(where, dims, cache, q_lat, q_pe, seq_lens, nullptr, 1, max_seq_len, num_splits, o_part,
+                               lse_part, o_lat, lse, stream);
+}
 
-  mla::DecodeArgs a{};
-  a.q_lat = static_cast<const uint16_t*>(q_lat);
-  a.q_pe = static_cast<const uint16_t*>(q_pe);
-  a.kv = static_cast<const char*>(cache->kv);
-  a.pe = static_cast<const char*>(cache->pe);
-  a.kv_sb = cache->kv_stride * (fp8 ? 1 : 2);
-  a.pe_sb = cache->pe_stride * (fp8 ? 1 : 2);
-  a.token_scale = cache->token_scale;
-  a.fp8 = fp8 ? 1 : 0;
-  a.seq_stride = cache->seq_stride;
-  a.block_table = cache->block_table;
-  a.block_size = cache->block_size;
-  a.max_blocks = cache->max_blocks_per_seq;
-  a.seq_lens = seq_lens;
-  a.batch = dims->batch;
-  a.num_heads = dims->num_heads;
-  a.num_splits = num_splits;
-  a.chunk = split_chunk(max_seq_len, num_splits);
-  a.max_seq_len = max_seq_len;
-  a.scale = dims->softmax_scale;
-  a.scale_log2 = dims->softmax_scale * 1.4426950408889634f;
-  a.o_part = static_cast<uint16_t*>(o_part);
-  a.lse_part = lse_part;
-  a.o_lat = static_cast<uint16_t*>(o_lat);
-  a.lse = lse;
-  return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
+mla_status mla_prefill_latent(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
+                              const int32_t* q_start, int32_t num_q, int32_t max_seq_len, int32_t num_splits,
+                              void* o_part, float* lse_part, void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_prefill_latent";
+  if (num_q < 1) return fail(MLA_ERR_BAD_LENGTH, "num_q %d < 1 (%s)", num_q, where);
+  if (q_start == nullptr) return fail(MLA_ERR_NULL, "q_start is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(q_start) % 4 != 0)
+    return fail(MLA_ERR_ALIGN, "q_start is not 4-byte aligned (%s)", where);
+  return latent_attention_rows(where, dims, cache, q_lat, q_pe, nullptr, q_start, num_q, max_seq_len, num_splits,
+                               o_part, lse_part, o_lat, lse, stream);
 }
 
 mla_status mla_decode_step_fused(const mla_dims* dims, const mla_cache* cache, const void* q_nope, const void* q_pe,

@@ -242,3 +242,26 @@ def test_naive_decode_validation(lib):
     assert call(max_len=0) == 4
     with pytest.raises(binding.MlaError):
         binding.mla_naive_workspace_bytes(d, 0)
+
+
+def test_prefill_latent_validation(lib):
+    d = binding.dims(2, 16, 0.07)
+    P = ctypes.c_void_p
+    cache = binding.MlaCache(dtype=0, kv=1024, pe=2048, kv_stride=576, pe_stride=576, token_scale=None,
+                             seq_stride=64, block_table=None, block_size=0, max_blocks_per_seq=0)
+
+    def call(starts=16, num_q=4, max_len=64, splits=1, o_lat=64, lse=64):
+        return lib.mla_prefill_latent(ctypes.byref(d), ctypes.byref(cache), P(16), P(16), P(starts) if starts else None,
+                                      num_q, max_len, splits, None, None, P(o_lat) if o_lat else None,
+                                      P(lse) if lse else None, None)
+
+    def err():
+        return lib.mla_last_error().decode()
+
+    assert call(starts=0) == 1 and "q_start" in err()
+    assert call(starts=18) == 6 and "q_start" in err()
+    assert call(num_q=0) == 4 and "num_q" in err()
+    assert call(max_len=0) == 4
+    assert call(max_len=128) == 5 and "seq_stride" in err()
+    assert call(splits=2) == 1 and "o_part" in err()
+    assert call(o_lat=0) == 1 and "o_lat" in err()
