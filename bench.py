@@ -16,6 +16,8 @@ Prints one JSON line:
                   each launch, against 8 TB/s
   fused_step      (contexts up to 2048) mla_decode_step_fused, the same step
                   in one launch, GPU time per step from graph replays
+  prefill         mla_prefill_latent on prompt / chunk shapes, TFLOP/s against
+                  the bf16 MFMA peak
   naive           mla_naive_decode (expand every step) on the same inputs,
                   and the absorbed step's speedup over it
   crossover_v2lite_b1   naive vs absorbed vs fused against context length
@@ -114,9 +116,9 @@ COPY_ELEMS = 1 << 28          # float32 elements of the calibration copy (1 GiB 
 PMC_COMMANDS = [
     "export TMPDIR=/tmp",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $PWD/gpurun_out/pmc_fetch -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $PWD/gpurun_out/pmc_write -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill",
     "python bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
     "gpurun_out/pmc_write/run_counter_collection.csv",
 ]
@@ -294,6 +296,44 @@ def bench_crossover(dev):
     return rows
 
 
+PREFILL_CASES = [  # (name, workload, heads, batch, context, chunk)
+    ("v3_last_chunk", "v3_b32_s4096", 128, 2, 4096, 512),
+    ("v3_prompt_4096", "v3_b32_s4096", 128, 1, 4096, 4096),
+    ("v2lite_prompt_4096", "v2lite_b64_s4096", 16, 1, 4096, 4096),
+]
+
+
+def bench_prefill(dev):
+    """mla_prefill_latent (causal latent attention of a prefill chunk whose rows
+    are already cached) against the bf16 MFMA peak: FLOPs = sum over query
+    rows of 2 * H * (576 + 512) * (causal prefix length)."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    res = {}
+    for name, wl, H, B, S, L in PREFILL_CASES:
+        x = datagen.make_inputs(datagen.WORKLOADS[wl], device=dev, batch=B, seq_len=S, heads=H)
+        d = binding.dims(B, H, x.scale)
+        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride)
+        q_lat = datagen.random_latent_queries(B * L, H, 5, device=dev).view(B, L, H, 512)
+        q_pe = datagen.random_latent_queries(B * L, H, 6, device=dev)[..., :64].contiguous().view(B, L, H, 64)
+        q_start = torch.full((B,), S - L, dtype=torch.int32, device=dev)
+        o_lat = torch.empty((B, L, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, L, H), dtype=torch.float32, device=dev)
+        call = lambda: binding.mla_prefill_latent(d, cache, q_lat, q_pe, q_start, S, o_lat=o_lat, lse=lse)
+        call()
+        torch.cuda.synchronize()
+        t = graph_time_per_call(call, 2, 3)
+        rows_tokens = B * sum(S - L + i + 1 for i in range(L))
+        flops = 2 * H * (576 + 512) * rows_tokens
+        tf = flops / t / 1e12
+        res[name] = {"heads": H, "batch": B, "context": S, "chunk": L, "us": round(t * 1e6, 1),
+                     "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+        del x, q_lat, q_pe, o_lat
+    torch.cuda.empty_cache()
+    return res
+
+
 FUSED_MAX_CONTEXT = 2048   # the fused one-launch step is timed on short contexts only
 
 
@@ -420,6 +460,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--no-naive", action="store_true", help="skip the naive-decode baseline and context sweep")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
@@ -583,6 +624,8 @@ def main():
     }
     if x0.max_seq_len <= FUSED_MAX_CONTEXT:
         result["fused_step"] = bench_fused_step(x0, d, dev, args.steps)
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(dev)
     if not args.no_naive:
         result["naive"] = bench_naive(x0, d, dev, t_step)
         result["crossover_v2lite_b1"] = bench_crossover(dev)

@@ -70,9 +70,14 @@ void decode_latent_kernel(DecodeArgs a) {
   const int w = wave_id();
   const int hl = lane & 15;   // row/column within a 16-block
   const int g4 = lane >> 4;   // 16-lane group
-  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int b = item / a.num_splits;  // query row: its queries and outputs
-  const int split = item - b * a.num_splits;
+  // decode: a sequence's splits share an XCD (and its L2 copy of the
+  // queries); prefill rows go round-robin over the XCDs, longest first
+  const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // query row: its queries and outputs.  Prefill rows run last query first:
+  // the longest causal prefixes start earliest, so the launch ends balanced.
+  const int qrow = item / a.num_splits;
+  const int split = item - qrow * a.num_splits;
+  const int b = a.q_start == nullptr ? qrow : a.batch - 1 - qrow;
   const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
   const int h = w * 16 + hl;  // head whose scores this lane computes
 

@@ -146,9 +146,14 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // P.V / output layout (32x32 tiles): head 32 n + h32, columns 8 (j/4) + 4 g2 + j%4
   const int h32 = lane & 31;
   const int g2 = lane >> 5;
-  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int b = item / a.num_splits;  // query row: its queries and outputs
-  const int split = item - b * a.num_splits;
+  // decode: a sequence's splits share an XCD (and its L2 copy of the
+  // queries); prefill rows go round-robin over the XCDs, longest first
+  const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // query row: its queries and outputs.  Prefill rows run last query first:
+  // the longest causal prefixes start earliest, so the launch ends balanced.
+  const int qrow = item / a.num_splits;
+  const int split = item - qrow * a.num_splits;
+  const int b = a.q_start == nullptr ? qrow : a.batch - 1 - qrow;
   const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
   const int col0 = w * C;  // first latent column of the wave's P.V share
 
