@@ -195,17 +195,18 @@ mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const
  *   o_lat[b,i,h] = sum_t softmax(s)_t c_t,  lse[b,i,h] = ln sum_t exp(s_t)
  *   q_lat   device bf16 [B, num_q, H, 512]  (mla_absorb_q with batch B*num_q)
  *   q_pe    device bf16 [B, num_q, H, 64]   (rotated at each query's position)
- *   q_start device int32 [B]
+ *   q_start device int32 [B], each >= 0 (a negative start is taken as 0)
  *   max_seq_len  host bound of q_start[b] + num_q (positions past it are
  *                clamped to it); sizes the split chunks as in decode
  *   num_splits, o_part, lse_part, o_lat, lse: as mla_decode_latent with B*num_q
  *                query rows (o_lat [B, num_q, H, 512], partials
  *                [B*num_q, P, H, 512], merged by mla_combine_splits with batch
  *                B*num_q)
- * Every query row runs the decode kernel's schedule over its own causal
- * prefix (the 576-wide tile of cached rows feeds the query's 128 heads, or
- * 16..64 heads for smaller H); the chunk's MLP projections around it are
- * mla_absorb_q / mla_expand_v with batch B*num_q.
+ * Each query runs the decode kernel's schedule over its own causal prefix:
+ * with 128 heads one workgroup per query; with fewer heads, a bf16 cache
+ * and one split, 128 / H consecutive queries of a sequence share a
+ * workgroup (128 rows per 576-wide tile of cached rows).  The projections
+ * around it are mla_absorb_q / mla_expand_v with batch B*num_q.
  */
 mla_status mla_prefill_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat, const void *q_pe,
                               const int32_t *q_start, int32_t num_q, int32_t max_seq_len, int32_t num_splits,

@@ -82,7 +82,7 @@ void decode_latent_kernel(DecodeArgs a) {
   const int h = w * 16 + hl;  // head whose scores this lane computes
 
   // decode: the sequence's length; prefill: causal, tokens up to the query's own position
-  int T = a.q_start == nullptr ? a.seq_lens[b] : a.q_start[cb] + (b - cb * a.q_per_seq) + 1;
+  int T = a.q_start == nullptr ? a.seq_lens[b] : max(a.q_start[cb], 0) + (b - cb * a.q_per_seq) + 1;
   T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
   const int t_begin = split * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
@@ -544,6 +544,8 @@ hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
   }
+  // prefill with fewer heads: 128 / H queries per workgroup of the wide kernel
+  if (a.q_group > 1) return launch_decode_latent_wide(a, stream);
   switch (a.num_heads) {
     case 128: return launch_decode_latent_wide(a, stream);
     case 16: return launch_nw<1, 1, false>(a, grid, stream);

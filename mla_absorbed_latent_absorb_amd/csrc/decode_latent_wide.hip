@@ -153,27 +153,48 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // the longest causal prefixes start earliest, so the launch ends balanced.
   const int qrow = item / a.num_splits;
   const int split = item - qrow * a.num_splits;
-  const int b = a.q_start == nullptr ? qrow : a.batch - 1 - qrow;
-  const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
+  // Workgroup rows: decode, one sequence (128 heads); prefill, one query (128
+  // heads), or with fewer heads a group of QG = 128 / H consecutive queries of
+  // one sequence (row r = query r / H, head r % H; one split).
+  const int QG = a.q_group;
+  const int groups = (a.q_per_seq + QG - 1) / QG;                     // workgroups per sequence
+  const int n_wg = QG > 1 ? (a.batch / a.q_per_seq) * groups : a.batch;
+  const int b = a.q_start == nullptr ? qrow : n_wg - 1 - qrow;
+  const int cb = b / groups;                // the sequence whose cached rows it reads
+  const int i0 = (b - cb * groups) * QG;    // its first query
+  const int nq = min(QG, a.q_per_seq - i0);  // queries in this workgroup
+  const size_t row0 = (size_t)cb * a.q_per_seq + i0;  // first query row (decode: the sequence)
+  const int Hq = a.num_heads;              // heads per query
+  const int n_rows = nq * Hq;               // rows that are stored (the rest repeat the last query)
   const int col0 = w * C;  // first latent column of the wave's P.V share
 
   // decode: the sequence's length; prefill: causal, tokens up to the query's own position
-  int T = a.q_start == nullptr ? a.seq_lens[b] : a.q_start[cb] + (b - cb * a.q_per_seq) + 1;
-  T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
+  auto length_of = [&](int qi) {
+    int t = a.q_start == nullptr ? a.seq_lens[b] : max(a.q_start[cb], 0) + qi + 1;
+    return t < 0 ? 0 : (t > a.max_seq_len ? a.max_seq_len : t);
+  };
+  const int T = length_of(i0 + nq - 1);
   const int t_begin = split * a.chunk;
   const int t_end = min(T, t_begin + a.chunk);
+  // query of each 16-row half of this wave (rows 32w + 16hh .. +15) and its tokens
+  int qo[2], t_end_h[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    qo[hh] = min((32 * w + 16 * hh) / Hq, nq - 1);
+    t_end_h[hh] = QG > 1 ? min(length_of(i0 + qo[hh]), t_begin + a.chunk) : t_end;
+  }
   const bool final_out = a.num_splits == 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  uint16_t* const out_rows = final_out ? a.o_lat + (size_t)b * a.num_heads * kDc
-                                       : a.o_part + ((size_t)b * a.num_splits + split) * a.num_heads * kDc;
-  float* const lse_out = final_out ? a.lse + (size_t)b * a.num_heads
-                                   : a.lse_part + ((size_t)b * a.num_splits + split) * a.num_heads;
+  uint16_t* const out_rows = final_out ? a.o_lat + row0 * Hq * kDc
+                                       : a.o_part + ((size_t)b * a.num_splits + split) * Hq * kDc;
+  float* const lse_out = final_out ? a.lse + row0 * Hq : a.lse_part + ((size_t)b * a.num_splits + split) * Hq;
 
   if (t_begin >= t_end) {
     // No tokens in this range: zero weight (o = 0, lse = -inf).
     for (int r = 0; r < 32; ++r)
-      *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * w + r) * kDc + lane * 8) = u32x4{0u, 0u, 0u, 0u};
-    if (g2 == 0) lse_out[32 * w + h32] = -INFINITY;
+      if (32 * w + r < n_rows)
+        *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * w + r) * kDc + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+    if (g2 == 0 && 32 * w + h32 < n_rows) lse_out[32 * w + h32] = -INFINITY;
     return;
   }
 
@@ -247,7 +268,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // 1024 i, head j's chunk k at slot 8 (j % 8) + (k ^ ((j / 2) % 8)).  Both
   // make the 16 rows that one fragment read touches land in 16 bank slots.
   auto stage_q = [&](int hh) {
-    const size_t head0 = (size_t)b * a.num_heads + 32 * w + 16 * hh;
+    const size_t head0 = (row0 + (size_t)qo[hh]) * Hq + (size_t)((32 * w + 16 * hh) % Hq);
     const uint32_t ln = lane_id();
     const char* ql = uniform_ptr(reinterpret_cast<const char*>(a.q_lat + head0 * kDc));
     const char* qr = uniform_ptr(reinterpret_cast<const char*>(a.q_pe + head0 * kDr));
@@ -465,7 +486,8 @@ void decode_latent_wide_kernel(DecodeArgs a) {
 
     // ---- P.V phase with the online softmax of tile tq ----
     Scores& sp = sc;
-    const int nvalid = min(kTile, t_end - (t_begin + tq * kTile));
+    const int t0q = t_begin + tq * kTile;
+    const int nvalid_h[2] = {min(kTile, t_end_h[0] - t0q), min(kTile, t_end_h[1] - t0q)};
     float mx[2], alpha[2], mb[2];
     bool any_grow = false;
     auto softmax_chunk = [&](int c) {
@@ -474,14 +496,16 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         drain_v(sp[0][1], false);
         drain_v(sp[1][0], false);
         drain_v(sp[1][1], false);
-        if (nvalid < kTile) {  // ragged tail: tokens 16 th + 4 q4 + j at or past nvalid
+        // ragged tail (and, in a query group, tokens past each half's own
+        // query): tokens 16 th + 4 q4 + j at or past the half's count
+        if (min(nvalid_h[0], nvalid_h[1]) < kTile) {
 #pragma unroll
           for (int th = 0; th < 2; ++th)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (16 * th + 4 * q4 + j >= nvalid) sp[th][hh][j] = -INFINITY;
+                if (16 * th + 4 * q4 + j >= nvalid_h[hh]) sp[th][hh][j] = -INFINITY;
         }
       } else if (c == 1 || c == 2) {
         const int hh = c - 1;
@@ -597,7 +621,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int hd = 32 * w + 16 * hh + h16;
       lds_write_f32(lds0 + kAlphaOff + hd * 4, 1.0f / l_tot[hh]);
-      lse_out[hd] = m_ref[hh] * a.scale + __logf(l_tot[hh]);
+      if (hd < n_rows) lse_out[hd] = m_ref[hh] * a.scale + __logf(l_tot[hh]);
     }
   }
   barrier();
@@ -634,14 +658,17 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       const uint32_t L = (uint32_t)(64 * k + lane);
       const uint32_t row = L / RC, ch = L % RC;
       const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
-      *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v;
+      if ((int)(32 * n + row) < n_rows)
+        *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v;
     }
   }
 }
 
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_heads != 128 || a.fp8) return hipErrorInvalidValue;
-  const int grid = a.batch * a.num_splits;
+  if (a.fp8 || a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1)))
+    return hipErrorInvalidValue;
+  const int groups = (a.q_per_seq + a.q_group - 1) / a.q_group;
+  const int grid = (a.q_group > 1 ? (a.batch / a.q_per_seq) * groups : a.batch) * a.num_splits;
   if (a.block_table != nullptr) {
     hipLaunchKernelGGL((decode_latent_wide_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a);
   } else {

@@ -22,6 +22,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;    // [B]
   int32_t q_per_seq;          // query rows per cached sequence: 1 (decode) or L (prefill chunk)
   const int32_t* q_start;     // prefill: [B] position of each sequence's first query; null: decode
+  int32_t q_group;            // prefill with H < 128 heads (wide kernel, one split): consecutive
+                              // queries per workgroup, 128 / H (128 rows); else 1
   int32_t batch;              // query rows (decode: sequences; prefill: sequences * L)
   int32_t num_heads;
   int32_t num_splits;

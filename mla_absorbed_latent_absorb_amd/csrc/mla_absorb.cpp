@@ -182,6 +182,8 @@ mla_status latent_attention_rows(const char* where, const mla_dims* dims, const 
   a.seq_lens = seq_lens;
   a.q_per_seq = q_per_seq;
   a.q_start = q_start;
+  // prefill chunks with fewer than 128 heads: 128 / H queries share a workgroup
+  a.q_group = (q_start != nullptr && !fp8 && num_splits == 1 && dims->num_heads < 128) ? 128 / dims->num_heads : 1;
   a.batch = (int32_t)rows;
   a.num_heads = dims->num_heads;
   a.num_splits = num_splits;

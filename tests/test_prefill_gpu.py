@@ -54,6 +54,9 @@ def _oracle_rows(x, q_lat, q_pe, q_start, max_len, rows):
     ("v3_b128_paged", 2, 400, 32, 33, [300, 360], 1),         # paged cache
     ("v3_b64_s32768_fp8", 2, 160, 128, 20, [140, 31], 1),     # E4M3 cache
     ("v3_b32_s4096", 2, 700, 64, 9, [650, 200], 3),           # split-KV + merge over B*L rows
+    ("v2lite_b64_s4096", 2, 300, 16, 21, [0, 250], 1),        # 8-query groups with a 5-query tail
+    ("v3_b32_s4096", 3, 260, 32, 6, [100, 0, 254], 1),        # 4-query groups with a 2-query tail
+    ("v3_b32_s4096", 2, 200, 64, 3, [190, 5], 1),             # 2-query groups with a 1-query tail
 ])
 def test_prefill_against_oracle(workload, B, S, H, L, starts, P):
     announce(f"prefill {workload} B={B} S={S} H={H} L={L} starts={starts} P={P}")
