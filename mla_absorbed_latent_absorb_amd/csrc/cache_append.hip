@@ -29,7 +29,7 @@
 namespace mla {
 namespace {
 
-constexpr int kAppendWaves = 4;  // tokens per workgroup
+constexpr int kAppendWaves = 4;  // waves per workgroup (two tokens each)
 
 // fp32 -> bf16 bit pattern, nearest, ties to the even pattern (finite x).
 __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
