@@ -92,14 +92,19 @@ __device__ __forceinline__ void acc_fence_write(f32x16& c, bool last) {
   else asm volatile("" : "+a"(c));
 }
 
-// XOR swizzle of the 16-byte chunk index of latent row r in an LDS tile.
-// Chosen by measurement (rocprofv3 SQ_LDS_BANK_CONFLICT on this kernel's two
-// read patterns, over 34 candidate swizzles): the score K fragment read (16
-// consecutive rows, one chunk each, 1 KiB apart) is free of bank conflicts,
-// and the transposing V^T read (4 consecutive rows x 4 adjacent chunks) costs
-// 2 extra cycles per instruction.  No candidate made both free; the K reads
-// are twice as many.  A bijection of r % 16 that touches the chunk bits only.
-__device__ __forceinline__ uint32_t lat_swizzle(uint32_t r) { return ((r & 1u) << 3) | ((r >> 1) & 7u); }
+// Latent rows of a tile in LDS: 32 blocks of 1 KiB, block 8 (r / 8) + c / 8
+// holding 16-byte chunks c .. c+7 (c a multiple of 8) of rows r .. r+7 (r a
+// multiple of 8) as eight 128-byte rows, chunk c of row r at 16-byte slot
+// (c % 8) ^ lat_swz(r).  A direct-to-LDS copy fills one block (eight rows x
+// 128 bytes, whole cache lines) from a per-lane source offset that stays the
+// same for every block of a wave; the K fragment read (16 rows, one chunk)
+// and the transposing V^T read (4 rows x 4 adjacent chunks) become a per-lane
+// base plus an immediate.  The swizzle was chosen by measurement (LDS read
+// rate of both patterns over 264 candidates): both reads run at the best
+// rate seen for them (~210 and ~160 B/clk per CU with 8 waves).
+__device__ __forceinline__ uint32_t lat_swz(uint32_t r) {
+  return (((r >> 1) & 1u) * 6u) ^ (((r >> 2) & 1u) * 4u) ^ (((r >> 3) & 1u) * 3u);
+}
 
 }  // namespace
 
@@ -202,20 +207,38 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   const char* kv_base = uniform_ptr(a.kv);
   const char* pe_base = uniform_ptr(a.pe);
 
-  // ---- tile copies (HBM -> LDS, 16 B per lane, rows swizzled by chunk) ----
+  // ---- tile copies (HBM -> LDS, 16 B per lane) ----
+  // Wave w copies latent blocks (w, k), k = 0..7 (rows 8w .. 8w+7, chunks
+  // 8k .. 8k+7) and RoPE rows 8w .. 8w+7 of each tile.  Every iteration
+  // issues one tile's copies, also past the last tile: those re-read the last
+  // tile's rows into ring buffers that nobody reads, or, for the RoPE buffer
+  // that the last iteration scores again, that tile's own bytes.  So the
+  // number of copies in flight never depends on the tile count.
+  static_assert(KV_PW == 8 && PE_PW == 1, "one latent block row and one RoPE copy per wave");
   struct TileSrc {
-    const char* kv0;  // latent row of the tile's first token (rows of a tile share a page)
+    const char* kv0;  // latent row of the source tile's first token (rows of a tile share a page)
     const char* pe0;  // its RoPE row
-    int last;         // last valid row (rows past it re-read it)
+    uint32_t kvoff;   // per-lane source offset of the wave's latent copies (rows past the end re-read the last)
+    uint32_t peoff;   // per-lane source offset of the wave's RoPE copy
     uint32_t lat;     // LDS latent buffer
     uint32_t pe;      // LDS RoPE buffer
   };
   auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NBUF) * kLatBytes; };
   auto pe_buf = [&](int tile) -> uint32_t { return lds0 + kPeRing + (uint32_t)(tile % NPE) * kPeBytes; };
+  // Row offsets inside a tile fit 32 bits (token strides are below 2^24 bytes).
+  const uint32_t kv_sb32 = (uint32_t)a.kv_sb, pe_sb32 = (uint32_t)a.pe_sb;
+  // source offsets of the lane's row r = 8w + l/8 in a whole tile
+  uint32_t kvoff_full, peoff_full;
+  {
+    const uint32_t ln = lane_id();
+    const uint32_t r = 8u * (uint32_t)w + (ln >> 3);
+    kvoff_full = r * kv_sb32 + (((ln & 7u) ^ lat_swz(r)) << 4);
+    peoff_full = r * pe_sb32 + (((ln & 7u) ^ pe_swizzle(r)) << 4);
+  }
   auto tile_src = [&](int tile) -> TileSrc {
-    const int t0 = t_begin + tile * kTile;
-    TileSrc ts;
-    ts.last = min(kTile, t_end - t0) - 1;
+    const int src = min(tile, n_tiles - 1);
+    const int t0 = t_begin + src * kTile;
+    const int last = min(kTile, t_end - t0) - 1;
     int64_t slot0;
     if (PAGED) {
       // scalar load: a vector load would make the compiler wait for every
@@ -227,35 +250,43 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     } else {
       slot0 = (int64_t)cb * a.seq_stride + t0;
     }
+    TileSrc ts;
     ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
     ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
+    ts.kvoff = kvoff_full;
+    ts.peoff = peoff_full;
+    if (last < kTile - 1) {  // ragged tile: rows past the end re-read the last
+      const uint32_t ln = lane_id();
+      const uint32_t r = 8u * (uint32_t)w + (ln >> 3);
+      const uint32_t rc = (uint32_t)min((int)r, last);
+      ts.kvoff = rc * kv_sb32 + (((ln & 7u) ^ lat_swz(r)) << 4);
+      ts.peoff = rc * pe_sb32 + (((ln & 7u) ^ pe_swizzle(r)) << 4);
+    }
     ts.lat = lat_buf(tile);
     ts.pe = pe_buf(tile);
     return ts;
   };
-  // ln16 = 16 * lane from the lane id of the current step (not kept live: a
-  // spilled value's scratch reload would wait for every copy in flight).
-  // Row offsets inside a tile fit 32 bits (token strides are below 2^24 bytes).
-  const uint32_t kv_sb32 = (uint32_t)a.kv_sb, pe_sb32 = (uint32_t)a.pe_sb;
-  auto copy_kv = [&](const TileSrc& ts, int r, uint32_t ln16) {  // latent row r
-    const uint32_t roff = (uint32_t)min(r, ts.last) * kv_sb32;
-    dma16(ts.kv0 + roff, ln16 ^ (lat_swizzle(r) << 4), ts.lat + r * kKvRow);
-  };
-  auto copy_pe = [&](const TileSrc& ts, int i, uint32_t ln16) {  // RoPE rows 8i .. 8i+7
-    const uint32_t r = 8 * i + (ln16 >> 7);
-    const uint32_t c = ((ln16 >> 4) & 7u) ^ pe_swizzle(r);
-    const uint32_t voff = (uint32_t)min((int)r, ts.last) * pe_sb32 + (c << 4);
-    dma16(ts.pe0, voff, ts.pe + i * 1024);
-  };
-  auto issue_copy = [&](const TileSrc& ts, int k, uint32_t ln16) {
-    if (k < KV_PW) copy_kv(ts, w * KV_PW + k, ln16);
-    else copy_pe(ts, w * PE_PW + (k - KV_PW), ln16);
+  // Copy k < 8: latent block (w, k) (the immediate offset 128 k moves the
+  // source to chunk 8k and the destination by the same amount, hence M0 =
+  // block - 128 k); copy 8: the RoPE rows.
+  auto issue_copy = [&](const TileSrc& ts, int k) {
+    const uint32_t blk = ts.lat + (uint32_t)w * 8192u + (uint32_t)k * 896u;
+    switch (k) {
+      case 0: dma16_off<0>(ts.kv0, ts.kvoff, blk); break;
+      case 1: dma16_off<128>(ts.kv0, ts.kvoff, blk); break;
+      case 2: dma16_off<256>(ts.kv0, ts.kvoff, blk); break;
+      case 3: dma16_off<384>(ts.kv0, ts.kvoff, blk); break;
+      case 4: dma16_off<512>(ts.kv0, ts.kvoff, blk); break;
+      case 5: dma16_off<640>(ts.kv0, ts.kvoff, blk); break;
+      case 6: dma16_off<768>(ts.kv0, ts.kvoff, blk); break;
+      case 7: dma16_off<896>(ts.kv0, ts.kvoff, blk); break;
+      default: dma16(ts.pe0, ts.peoff, ts.pe + (uint32_t)w * 1024u); break;
+    }
   };
   auto issue_tile = [&](int tile) {
     const TileSrc ts = tile_src(tile);
-    const uint32_t ln16 = lane_id() << 4;
 #pragma unroll
-    for (int k = 0; k < kCopies; ++k) issue_copy(ts, k, ln16);
+    for (int k = 0; k < kCopies; ++k) issue_copy(ts, k);
   };
 
   // ---- prologue ----
@@ -296,41 +327,49 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   };
   issue_tile(0);
   stage_q(0);
-  if (n_tiles > 1) {
-    issue_tile(1);
-    wait_vmcnt<kCopies>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  issue_tile(1);
+  wait_vmcnt<kCopies>();
   read_q(0);
   stage_q(1);
   wait_vmcnt<0>();
   read_q(1);
-  barrier();  // every wave has read its query block: the staging area is free
-  if (NBUF > 3 && n_tiles > 2) issue_tile(2);
+  // every wave has read its query block (the staging area is free) and its
+  // copies of tiles 0 and 1 have landed
+  barrier();
+  issue_tile(2);
 
   // ---- per-lane LDS addresses inside a tile ----
-  // The swizzles XOR only the 16-byte chunk index and buffers are 1 KiB
-  // aligned, so each fragment address is a per-lane base XOR a step constant
-  // plus an immediate offset.
-  //   K fragment of score step s, token half th: row 16 th + l%16, latent
-  //   chunk 4 s + l/16 = 16 m + ((l/16 ^ swz) ^ 4 s4) for s = 4 m + s4 < 16;
-  //   steps 16, 17: RoPE chunk 4 (s-16) + l/16.  Row r + 16 has the swizzle of r.
-  auto k_addr_fn = [&](uint32_t kb0, uint32_t pb0, int s) -> uint32_t {
-    if (s < 16) return (kb0 ^ ((uint32_t)(s & 3) << 6)) + 256u * (uint32_t)(s >> 2);
+  //   K fragment of score step s < 16, token half th: row 16 th + l%16, latent
+  //   chunk 4 s + l/16, at kb[s % 2] + 16 KiB th + 1 KiB (s / 2), where kb[1]
+  //   = kb[0] ^ 64 (the chunk's bit 2 is the step's parity, XORed into a slot
+  //   whose bit 2 also depends on the row).  Steps 16, 17: RoPE chunk
+  //   4 (s-16) + l/16 at pb0 ^ 64 (s-16) (+ 2 KiB th).
+  // Per-lane parts of the fragment addresses, the same for every tile
+  // (buffers are 1 KiB aligned, so the ring offset adds and the ^ 64 of the
+  // odd bases acts on the lane part alone).
+  uint32_t kb_lane, pb_lane, vb_lane, p_lane;
+  {
+    const uint32_t ln = lane_id();
+    const uint32_t r16 = ln & 15u;
+    kb_lane = ((r16 >> 3) << 13) + ((r16 & 7u) << 7) + (((ln >> 4) ^ lat_swz(r16)) << 4);
+    pb_lane = r16 * kPeRow + (((ln >> 4) ^ pe_swizzle(r16)) << 4);
+    const uint32_t g = ln >> 5, i = (ln & 15u) >> 2, cb2 = (ln >> 3) & 2u, a2 = (ln & 3u) >> 1;
+    vb_lane = (g << 13) + ((uint32_t)w << 11) + (i << 7) + (((cb2 | a2) ^ (6u * (i >> 1)) ^ (3u * g)) << 4) +
+              ((ln & 1u) << 3);
+    p_lane = ln << 4;
+  }
+  auto k_addr_fn = [&](uint32_t kbe, uint32_t kbo, uint32_t pb0, int s) -> uint32_t {
+    if (s < 16) return ((s & 1) ? kbo : kbe) + 1024u * (uint32_t)(s >> 1);
     return pb0 ^ ((uint32_t)(s - 16) << 6);
   };
   auto k_hi = [&](int s) -> uint32_t { return s < 16 ? 16u * kKvRow : 16u * kPeRow; };
   //   V^T fragment (column tile ct, k-step kk): the 16-lane group l/16 reads
   //   rows 16 kk + 8 (l/32) + (l%16)/4 (and + 4), columns col0 + 32 ct +
   //   16 ((l/16) % 2) + 4 (l%4) .. +3; lane l receives column col0 + 32 ct +
-  //   l%32 of those 4 rows (transposing read).  The chunk is
-  //   (col0/8 + 2 ((l/16)%2) + (l%4)/2) XOR 4 ct, col0/8 a multiple of 16.
-  auto v_base = [&](uint32_t l, uint32_t roff) -> uint32_t {
-    const uint32_t r = 8 * (l >> 5) + ((l & 15u) >> 2) + roff;
-    const uint32_t chunk = (uint32_t)(col0 >> 3) | (((l >> 4) & 1u) << 1) | ((l & 3u) >> 1);
-    return r * kKvRow + ((chunk ^ lat_swizzle(r)) << 4) + ((l & 1u) << 3);
-  };
+  //   l%32 of those 4 rows (transposing read).  Row bit 2 (the + 4) and
+  //   column-tile bit 0 both land in bit 2 of the slot, so the read is
+  //   vb[(ct % 2) ^ (row part / 4)] + 16 KiB kk + 1 KiB (ct / 2) (+ 512 for
+  //   the + 4 rows) with vb[1] = vb[0] ^ 64.
 
   f32x16 o[CT][NT];  // o[ct][n][j] = O^T[col0 + 32 ct + 8 (j/4) + 4 g2 + j%4][32 n + h32]
 #pragma unroll
@@ -347,14 +386,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   float l_sum[2] = {0.f, 0.f};              // this lane's share of sum_t exp2((s - m_ref) c2)
   const float c2 = a.scale_log2;
 
-  // Wait for this wave's copies of tile k, leaving at most `younger_max`
-  // younger tiles in flight.
-  auto wait_tile = [&](int k, int younger_max) {
-    const int later = min(younger_max, n_tiles - 1 - k);
-    if (later <= 0) wait_vmcnt<0>();
-    else if (later == 1) wait_vmcnt<kCopies>();
-    else wait_vmcnt<(NBUF > 3 ? 2 * kCopies : 0)>();
-  };
   static_assert(kCopies <= 9, "one copy every other score step");
 
   typedef f32x4 Scores[2][2];  // [token half th][head half hh]
@@ -398,27 +429,24 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   //   O *= alpha of slot pb if any wave's softmax of tile tv moved its
   //   reference max.
   auto iteration = [&](auto pv_tag, int tq, Scores& sc, int tv, int pb, int ps, bool rescale_check,
-                       bool commit, bool copy_next, const TileSrc& nts) {
+                       bool commit, const TileSrc& nts) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
-    const uint32_t ln = lane_id();
-    const uint32_t ln16 = ln << 4;
-    const uint32_t r16 = ln & 15u;
     // one byte per wave; read now, tested after the deferred MFMAs
     const uint32_t flags = DO_PV ? lds_read_u32(lds0 + kFlagOff + pb * 8) : 0u;
-    const uint32_t kb0 = lat_buf(tq) + r16 * kKvRow + (((ln >> 4) ^ lat_swizzle(r16)) << 4);
-    const uint32_t pb0 = pe_buf(tq) + r16 * kPeRow + (((ln >> 4) ^ pe_swizzle(r16)) << 4);
-    uint32_t va0 = 0, va4 = 0;
-    const uint32_t pbase = lds0 + kPOff + (uint32_t)pb * kPBuf + ln16;
+    const uint32_t kbe = lat_buf(tq) + kb_lane;
+    const uint32_t kbo = kbe ^ 64u;
+    const uint32_t pb0 = pe_buf(tq) + pb_lane;
+    uint32_t vb0 = 0, vb1 = 0;
+    const uint32_t pbase = lds0 + kPOff + (uint32_t)pb * kPBuf + p_lane;
     if (DO_PV) {
-      const uint32_t tb = lat_buf(tv);
-      va0 = tb + v_base(ln, 0);
-      va4 = tb + v_base(ln, 4);
+      vb0 = lat_buf(tv) + vb_lane;
+      vb1 = vb0 ^ 64u;
     }
     auto va_load = [&](int vi) -> bf16x8 {  // vi = 4 kk + ct
       const int ct = vi & 3, kk = vi >> 2;
-      const uint32_t x = (uint32_t)ct << 6;
-      const bf16x4 lo = lds_read_tr16((va0 ^ x) + (uint32_t)kk * 16u * kKvRow);
-      const bf16x4 hi = lds_read_tr16((va4 ^ x) + (uint32_t)kk * 16u * kKvRow);
+      const uint32_t imm = (uint32_t)kk * 16u * kKvRow + (uint32_t)(ct >> 1) * 1024u;
+      const bf16x4 lo = lds_read_tr16(((ct & 1) ? vb1 : vb0) + imm);
+      const bf16x4 hi = lds_read_tr16(((ct & 1) ? vb0 : vb1) + imm + 512u);
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto pf_load = [&](int n, int kk) -> bf16x8 {
@@ -428,7 +456,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     bf16x8 kf[D + 1][2];
 #pragma unroll
     for (int st = 0; st < D; ++st) {
-      const uint32_t ad = k_addr_fn(kb0, pb0, st);
+      const uint32_t ad = k_addr_fn(kbe, kbo, pb0, st);
       kf[st][0] = lds_read_b128(ad);
       kf[st][1] = lds_read_b128(ad + k_hi(st));
     }
@@ -458,7 +486,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // slot work of step st (two slots per step): this wave's copy i in the
     // first slot of step 2i + 1, P.V operand preloads in steps 0 .. 3
     auto slot = [&](int st, int k) {
-      if ((st & 1) == 1 && k == 0 && (st >> 1) < kCopies && copy_next) issue_copy(nts, st >> 1, ln16);
+      if (DO_PV && (st & 1) == 1 && k == 0 && (st >> 1) < kCopies) issue_copy(nts, st >> 1);
       if (DO_PV) {
         if (k == 0 && st < 2) pf[2 * st] = pf_load(2 * st, 0);
         else if (k == 1 && st < 2) pf[2 * st + 1] = pf_load(2 * st + 1, 0);
@@ -468,7 +496,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     };
 #pragma unroll
     for (int st = 0; st < 18; ++st) {
-      const uint32_t ad = st + D < 18 ? k_addr_fn(kb0, pb0, st + D) : 0u;
+      const uint32_t ad = st + D < 18 ? k_addr_fn(kbe, kbo, pb0, st + D) : 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int th = e >> 1, hh = e & 1;
@@ -583,30 +611,26 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   };
 
   // Pipeline.  Before the loop: scores and softmax of tile 0 (slot 0).
-  // Iteration k, after barrier A (tile k+1 landed; every wave's probabilities
-  // of tile k are in slot k%2; every wave is done with iteration k-1, so the
-  // latent buffer of tile k-1 and the RoPE buffer of tile k are free and the
-  // copies of tile k + NBUF - 1 go there): the P.V of tile k woven with the
-  // scores and softmax of tile k+1 into slot (k+1)%2 (whose previous
-  // contents, tile k-1's, were consumed in iteration k-1).  The last tile has
-  // no successor: its own rows are scored again and that softmax is not
-  // committed (one code path keeps the registers allocated once).
-  const TileSrc no_copy = {nullptr, nullptr, 0, 0u, 0u};
+  // Iteration k, after barrier A (tile k+1 landed: only tile k+2's copies
+  // may still be in flight; every wave's probabilities of tile k are in slot
+  // k%2; every wave is done with iteration k-1, so the latent buffer of tile
+  // k-1 and the RoPE buffer of tile k are free and the copies of tile
+  // k + NBUF - 1 go there): the P.V of tile k woven with the scores and
+  // softmax of tile k+1 into slot (k+1)%2 (whose previous contents, tile
+  // k-1's, were consumed in iteration k-1).  The last tile has no successor:
+  // its own rows are scored again and that softmax is not committed (one
+  // code path keeps the registers allocated once).
+  static_assert(NBUF == 4, "the waits count one tile of copies in flight");
   Scores sc;
-  wait_tile(0, NBUF - 2);
-  barrier();
   __builtin_amdgcn_sched_barrier(0);
-  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, false, no_copy);
+  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{});
   for (int it = 0; it < n_tiles; ++it) {
     const bool has_next = it + 1 < n_tiles;
-    if (has_next) wait_tile(it + 1, NBUF - 3);
+    wait_vmcnt<kCopies>();
     barrier();  // barrier A
     __builtin_amdgcn_sched_barrier(0);
-    const int nxt = it + NBUF - 1;
-    const bool copy_next = nxt < n_tiles;
-    const TileSrc nts = tile_src(copy_next ? nxt : it);
-    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next,
-              copy_next, nts);
+    const TileSrc nts = tile_src(it + NBUF - 1);
+    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts);
   }
 #pragma unroll
   for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the last tile
@@ -615,7 +639,10 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   float l_tot[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) l_tot[hh] = sum_xor32(sum_xor16(l_sum[hh]));
-  barrier();  // every wave is done with the tiles and the rescale factors
+  // every wave is done with the tiles and the rescale factors, and its last
+  // copies (past the last tile) have landed before the rings are reused
+  wait_vmcnt<0>();
+  barrier();
   if (q4 == 0) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {

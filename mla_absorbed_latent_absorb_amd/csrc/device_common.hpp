@@ -58,6 +58,18 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "s"(m0), "v"(voff), "s"(sbase)
                : "memory");
 }
+// The same with the instruction's immediate offset OFF, which the hardware
+// adds to both addresses: lane i reads sbase + voff + OFF and writes bytes
+// [lds_base + OFF + 16*i, +16) (checked on gfx950 with an in-bounds probe).
+template <int OFF>
+__device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF)
+               : "memory");
+}
 
 // The same with 4 bytes per lane (global_load_lds_dword): lane i writes
 // [lds_base + 4*i, +4).
