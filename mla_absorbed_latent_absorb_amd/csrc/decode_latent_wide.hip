@@ -235,24 +235,34 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     kvoff_full = r * kv_sb32 + (((ln & 7u) ^ lat_swz(r)) << 4);
     peoff_full = r * pe_sb32 + (((ln & 7u) ^ pe_swizzle(r)) << 4);
   }
+  // Contiguous cache: the source rows of the next tile to copy, advanced by
+  // one tile per call of tile_src (tiles are requested in order) and held at
+  // the last tile.
+  const char* kv_next = kv_base + ((int64_t)cb * a.seq_stride + t_begin) * a.kv_sb;
+  const char* pe_next = pe_base + ((int64_t)cb * a.seq_stride + t_begin) * a.pe_sb;
+  const uint32_t kv_step = kTile * kv_sb32, pe_step = kTile * pe_sb32;
   auto tile_src = [&](int tile) -> TileSrc {
     const int src = min(tile, n_tiles - 1);
     const int t0 = t_begin + src * kTile;
     const int last = min(kTile, t_end - t0) - 1;
-    int64_t slot0;
+    TileSrc ts;
     if (PAGED) {
       // scalar load: a vector load would make the compiler wait for every
       // tile copy in flight before using it
       const auto* table = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
           reinterpret_cast<uintptr_t>(a.block_table));
       const int blk = table[(size_t)cb * a.max_blocks + t0 / a.block_size];
-      slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
+      const int64_t slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
+      ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
+      ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
     } else {
-      slot0 = (int64_t)cb * a.seq_stride + t0;
+      ts.kv0 = uniform_ptr(kv_next);
+      ts.pe0 = uniform_ptr(pe_next);
+      if (tile < n_tiles - 1) {
+        kv_next += kv_step;
+        pe_next += pe_step;
+      }
     }
-    TileSrc ts;
-    ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
-    ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
     ts.kvoff = kvoff_full;
     ts.peoff = peoff_full;
     if (last < kTile - 1) {  // ragged tile: rows past the end re-read the last
@@ -270,16 +280,16 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // source to chunk 8k and the destination by the same amount, hence M0 =
   // block - 128 k); copy 8: the RoPE rows.
   auto issue_copy = [&](const TileSrc& ts, int k) {
-    const uint32_t blk = ts.lat + (uint32_t)w * 8192u + (uint32_t)k * 896u;
+    const uint32_t blk0 = ts.lat + (uint32_t)w * 8192u;
     switch (k) {
-      case 0: dma16_off<0>(ts.kv0, ts.kvoff, blk); break;
-      case 1: dma16_off<128>(ts.kv0, ts.kvoff, blk); break;
-      case 2: dma16_off<256>(ts.kv0, ts.kvoff, blk); break;
-      case 3: dma16_off<384>(ts.kv0, ts.kvoff, blk); break;
-      case 4: dma16_off<512>(ts.kv0, ts.kvoff, blk); break;
-      case 5: dma16_off<640>(ts.kv0, ts.kvoff, blk); break;
-      case 6: dma16_off<768>(ts.kv0, ts.kvoff, blk); break;
-      case 7: dma16_off<896>(ts.kv0, ts.kvoff, blk); break;
+      case 0: dma16_off<0, 0>(ts.kv0, ts.kvoff, blk0); break;
+      case 1: dma16_off<128, 896>(ts.kv0, ts.kvoff, blk0); break;
+      case 2: dma16_off<256, 1792>(ts.kv0, ts.kvoff, blk0); break;
+      case 3: dma16_off<384, 2688>(ts.kv0, ts.kvoff, blk0); break;
+      case 4: dma16_off<512, 3584>(ts.kv0, ts.kvoff, blk0); break;
+      case 5: dma16_off<640, 4480>(ts.kv0, ts.kvoff, blk0); break;
+      case 6: dma16_off<768, 5376>(ts.kv0, ts.kvoff, blk0); break;
+      case 7: dma16_off<896, 6272>(ts.kv0, ts.kvoff, blk0); break;
       default: dma16(ts.pe0, ts.peoff, ts.pe + (uint32_t)w * 1024u); break;
     }
   };
@@ -537,20 +547,20 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         }
       } else if (c == 1 || c == 2) {
         const int hh = c - 1;
-        mx[hh] = fmaxf(fmaxf(fmaxf(sp[0][hh][0], sp[0][hh][1]), fmaxf(sp[0][hh][2], sp[0][hh][3])),
-                       fmaxf(fmaxf(sp[1][hh][0], sp[1][hh][1]), fmaxf(sp[1][hh][2], sp[1][hh][3])));
+        mx[hh] = vmax(vmax3(vmax3(sp[0][hh][0], sp[0][hh][1], sp[0][hh][2]), sp[0][hh][3], sp[1][hh][0]),
+                      vmax3(sp[1][hh][1], sp[1][hh][2], sp[1][hh][3]));
       } else if (c == 3) {
-        mx[0] = max_xor16(mx[0]);
-        mx[1] = max_xor16(mx[1]);
+        mx[0] = vmax_xor16(mx[0]);
+        mx[1] = vmax_xor16(mx[1]);
       } else if (c == 4) {
-        mx[0] = max_xor32(mx[0]);
-        mx[1] = max_xor32(mx[1]);
+        mx[0] = vmax_xor32(mx[0]);
+        mx[1] = vmax_xor32(mx[1]);
       } else if (c == 5) {
         bool grow = false;
         float m_new[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          m_new[hh] = fmaxf(m_ref[hh], mx[hh]);
+          m_new[hh] = vmax(m_ref[hh], mx[hh]);
           grow = grow || (m_new[hh] - m_ref[hh]) * c2 > kRescaleLog2;
         }
         any_grow = __ballot(grow) != 0;
@@ -562,18 +572,15 @@ void decode_latent_wide_kernel(DecodeArgs a) {
           mb[hh] = m_use * c2;
           if (commit) m_ref[hh] = m_use;
         }
-      } else if (c >= 6 && c < 14) {
-        // two of the lane's 16 probabilities per chunk
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int e = 2 * (c - 6) + x, th = e >> 3, hh = (e >> 2) & 1, j = e & 3;
-          sp[th][hh][j] = fast_exp2(fmaf(sp[th][hh][j], c2, -mb[hh]));
-        }
-      } else if (c == 14 || c == 15) {
+      } else if (c >= 6 && c < 22) {
+        // one of the lane's 16 probabilities per chunk
+        const int e = c - 6, th = e >> 3, hh = (e >> 2) & 1, j = e & 3;
+        sp[th][hh][j] = fast_exp2(fmaf(sp[th][hh][j], c2, -mb[hh]));
+      } else if (c == 22 || c == 23) {
         // B operand of P.V (k-step th of head tile w): lane h' + 32 g' holds
         // tokens 16 th + 8 g' + i; this lane's 4 tokens 16 th + 4 q4 + j are
         // elements 4 (q4 % 2) + j of lane (16 hh + h16) + 32 (q4 / 2)
-        const int th = c - 14;
+        const int th = c - 22;
         const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u + (uint32_t)th * 1024u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -581,13 +588,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
           const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
           lds_write_b64(pw + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
         }
-      } else if (c == 16 || c == 17) {
-        const int hh = c - 16;
+      } else if (c == 24 || c == 25) {
+        const int hh = c - 24;
         const float psum = ((sp[0][hh][0] + sp[0][hh][1]) + (sp[0][hh][2] + sp[0][hh][3])) +
                            ((sp[1][hh][0] + sp[1][hh][1]) + (sp[1][hh][2] + sp[1][hh][3]));
         const float nl = fmaf(l_sum[hh], alpha[hh], psum);
         if (commit) l_sum[hh] = nl;
-      } else if (c == 18) {
+      } else if (c == 26) {
         if (q4 == 0) {
           const uint32_t ab = lds0 + kAlphaOff + (uint32_t)ps * (H * 4);
           lds_write_f32(ab + (32 * w + h16) * 4, alpha[0]);

@@ -59,15 +59,16 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory");
 }
 // The same with the instruction's immediate offset OFF, which the hardware
-// adds to both addresses: lane i reads sbase + voff + OFF and writes bytes
-// [lds_base + OFF + 16*i, +16) (checked on gfx950 with an in-bounds probe).
-template <int OFF>
+// adds to both addresses, and M0 = lds_base + MADD: lane i reads
+// sbase + voff + OFF and writes bytes [lds_base + MADD + OFF + 16*i, +16)
+// (checked on gfx950 with an in-bounds probe).
+template <int OFF, int MADD>
 __device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
                :
-               : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF)
+               : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF), "n"(MADD)
                : "memory");
 }
 
@@ -174,6 +175,20 @@ __device__ __forceinline__ float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// IEEE maximum (NaN-propagating, +0 above -0): v_maximum3_f32 on gfx950.
+// fmaxf's maxNum semantics make the compiler quiet every operand it cannot
+// prove to be a non-signalling value (results of inline asm, lane swaps)
+// with one extra instruction each; scores never hold NaN, where the two agree.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+__device__ __forceinline__ float vmax_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float vmax_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float sum_xor16(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -195,10 +210,13 @@ __device__ __forceinline__ u32x2 lds_read_u32x2(uint32_t byte_off) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two fp32 values -> bf16 pair (lo in bits 0..15), nearest even: one
+// v_cvt_pk_bf16_f32 (two scalar casts compile to two converts, a shift and an
+// OR).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // Lane index recomputed at the point of use (v_mbcnt over a full mask).  It is
