@@ -687,13 +687,21 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         lds_write_b64(stage + (uint32_t)h32 * (uint32_t)(2 * C) + (chunk << 4) + ((uint32_t)g2 << 3), v);
       }
     }
+    // all reads first, then the stores: one LDS round trip per head tile
+    constexpr int KR = (32 * RC) / 64;
+    u32x4 v[KR];
 #pragma unroll
-    for (int k = 0; k < (32 * RC) / 64; ++k) {
+    for (int k = 0; k < KR; ++k) {
       const uint32_t L = (uint32_t)(64 * k + lane);
       const uint32_t row = L / RC, ch = L % RC;
-      const u32x4 v = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
+      v[k] = lds_read_u32x4(stage + row * (uint32_t)(2 * C) + ((ch ^ (row & SWZ)) << 4));
+    }
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+      const uint32_t L = (uint32_t)(64 * k + lane);
+      const uint32_t row = L / RC, ch = L % RC;
       if ((int)(32 * n + row) < n_rows)
-        *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v;
+        *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v[k];
     }
   }
 }
