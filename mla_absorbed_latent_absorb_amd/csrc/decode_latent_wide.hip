@@ -300,9 +300,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   };
 
   // ---- prologue ----
-  // Copies in issue order: tile 0, query half 0 (heads 32w .. 32w+15), tile
-  // 1, query half 1; each query half is read back as soon as it has landed,
-  // and tile 2 goes into the staging area once every wave is done with it.
+  // Copies in issue order: query half 0 (heads 32w .. 32w+15), tile 0, query
+  // half 1, tile 1; each query half is read back as soon as it has landed (the
+  // query is on the critical path: every split of a sequence fetches the same
+  // 147 KB while the whole grid starts at once), and tile 2 goes into the
+  // staging area once every wave is done with it.  The splits of a sequence
+  // start their query rows at different heads, so they do not all ask for the
+  // same lines at the same moment (both orders measured faster).
   const uint32_t qstage = lds0 + kQStage + (uint32_t)w * kQWave;
   // Query half hh: latent row of head j (0..15) at qstage + 1024 j with
   // chunk c at slot c ^ j; RoPE rows of heads 8i .. 8i+7 at qstage + 16 KiB +
@@ -313,8 +317,12 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     const uint32_t ln = lane_id();
     const char* ql = uniform_ptr(reinterpret_cast<const char*>(a.q_lat + head0 * kDc));
     const char* qr = uniform_ptr(reinterpret_cast<const char*>(a.q_pe + head0 * kDr));
+    const uint32_t rot = (uint32_t)(split * 2) & 15u;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) dma16(ql + j * (kDc * 2), (ln ^ (uint32_t)j) << 4, qstage + j * 1024);
+    for (int jj = 0; jj < 16; ++jj) {
+      const uint32_t j = ((uint32_t)jj + rot) & 15u;
+      dma16(ql + j * (kDc * 2), (ln ^ j) << 4, qstage + j * 1024);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t j = 8 * i + (ln >> 3);
@@ -335,16 +343,16 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // the reads are complete before the staging area is overwritten
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  issue_tile(0);
   stage_q(0);
-  issue_tile(1);
+  issue_tile(0);
   wait_vmcnt<kCopies>();
   read_q(0);
   stage_q(1);
-  wait_vmcnt<0>();
+  issue_tile(1);
+  wait_vmcnt<kCopies>();
   read_q(1);
   // every wave has read its query block (the staging area is free) and its
-  // copies of tiles 0 and 1 have landed
+  // copies of tile 0 have landed; tile 1 may still be in flight
   barrier();
   issue_tile(2);
 
