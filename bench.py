@@ -515,17 +515,19 @@ def main():
     for x in reps:
         cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
                                    block_size=x.block_size, token_scale=x.token_scale)
-        steps.append((x, binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev)))
+        steps.append((x, binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev, keep_latent=False)))
 
     def run(i, ev=None):
         x, st = steps[i % R]
         binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
         if ev is not None:
             ev[0].record()
-        st.attend(x.q_pe)
+        st.decode(x.q_pe)
         if ev is not None:
             ev[1].record()
-        binding.mla_expand_v(d, st.o_lat, x.w_uv, out=st.out)
+        st.finish(x.w_uv)
+        if ev is not None:
+            ev[2].record()
 
     for i in range(args.warmup):
         run(i)
@@ -553,41 +555,20 @@ def main():
     t_step = (time.perf_counter() - t0) / args.steps
     del graph
 
-    # dominant kernel: HIP events around each decode launch (same stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    evs_dec = []
+    # dominant kernel: HIP events around each decode launch, and around the
+    # merge + W_UV launch after it (all on the stream the calls launch on)
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for i in range(args.steps):
-        x, st = steps[i % R]
-        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
-        a, b = evs[i]
-        a.record()
-        if P > 1:
-            binding.mla_decode_latent(d, st.cache, st.q_lat, x.q_pe, st.seq_lens, st.max_seq_len, P,
-                                      o_part=st.o_part, lse_part=st.lse_part)
-            b.record()
-            binding.mla_combine_splits(d, st.o_part, st.lse_part, o_lat=st.o_lat, lse=st.lse)
-        else:
-            binding.mla_decode_latent(d, st.cache, st.q_lat, x.q_pe, st.seq_lens, st.max_seq_len, 1,
-                                      o_lat=st.o_lat, lse=st.lse)
-            b.record()
-        binding.mla_expand_v(d, st.o_lat, x.w_uv, out=st.out)
-        evs_dec.append((a, b))
+        run(i, evs[i])
     torch.cuda.synchronize()
-    t_dec = sum(a.elapsed_time(b) for a, b in evs_dec) / len(evs_dec) * 1e-3
-
-    # decode + combine (the attention part of the step)
-    evs_att = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        run(i, evs_att[i])
-    torch.cuda.synchronize()
-    t_att = sum(a.elapsed_time(b) for a, b in evs_att) / len(evs_att) * 1e-3
+    t_dec = sum(a.elapsed_time(b) for a, b, _ in evs) / len(evs) * 1e-3
+    t_tail = sum(b.elapsed_time(c) for _, b, c in evs) / len(evs) * 1e-3
 
     lens_sum = int(x0.seq_lens.to(torch.int64).sum().item())
     flops_core = core_flops(x0.batch, x0.heads, lens_sum)
     flops_step = flops_core + proj_flops(x0.batch, x0.heads)
     gbs_step = cache_bytes / t_step / 1e9
     gbs_dec = cache_bytes / t_dec / 1e9
-    gbs_att = cache_bytes / t_att / 1e9
     traffic = traffic_from_counters(wl.name)
 
     result = {
@@ -599,7 +580,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
         "ms_per_step_eager": round(t_step_eager * 1e3, 5),
-        "step_timing": "one HIP graph replay holding the K steps (four launches each)",
+        "step_timing": "one HIP graph replay holding the K steps (three launches each: absorb_q, decode_latent, "
+                       "combine_expand_v or expand_v)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -612,9 +594,7 @@ def main():
                      "frac": round(gbs_dec / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernel": "mla_decode_latent",
         "decode_us": round(t_dec * 1e6, 3),
-        "decode_plus_combine_us": round(t_att * 1e6, 3),
-        "attention_gbs": round(gbs_att, 2),
-        "attention_hbm_frac": round(gbs_att / HBM_PEAK_GBS, 4),
+        "merge_expand_us": round(t_tail * 1e6, 3),
         "tflops_step": round(flops_step / t_step / 1e12, 3),
         "tflops_decode": round(flops_core / t_dec / 1e12, 3),
         "decode_mfma_frac": round(flops_core / t_dec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),

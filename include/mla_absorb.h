@@ -12,7 +12,8 @@
  *   mla_combine_splits  log-sum-exp merge of split-KV partial results
  *   mla_expand_v        out[b,h,:] = W_UV[h] . o_lat[b,h,:]                 (value absorption)
  *
- * and mla_cache_append, which writes new tokens (latent row + rotated RoPE
+ * (mla_combine_expand_v runs the last two in one launch), and
+ * mla_cache_append, which writes new tokens (latent row + rotated RoPE
  * key, bf16 or E4M3 with a per-token scale) into the cache that decode reads,
  * and mla_decode_step_fused, the three decode stages in one launch for short
  * contexts, and mla_naive_decode, the expand-every-step baseline.
@@ -233,6 +234,24 @@ mla_status mla_combine_splits(const mla_dims *dims, const void *o_part, const fl
  */
 mla_status mla_expand_v(const mla_dims *dims, const void *o_lat, const void *w_uv, void *out,
                         void *stream);
+
+/*
+ * Split-KV merge and value absorption in one launch ([AUDIT] §2.3: W_UV is
+ * applied after the latent aggregation): the result of mla_combine_splits
+ * followed by mla_expand_v, with the same arithmetic (the merged row is
+ * rounded to bf16 before the W_UV product), so out, o_lat and lse equal the
+ * two calls' bit for bit.
+ *   o_part, lse_part, num_splits  as mla_combine_splits
+ *   w_uv   device bf16 [H, 128, 512]
+ *   out    device bf16 [B, H, 128] (output)
+ *   o_lat  device bf16 [B, H, 512] (output, may be NULL)
+ *   lse    device fp32 [B, H] (output, may be NULL)
+ * One workgroup per (head, 16 sequences): W_UV[h] and the partial rows are
+ * read once, and o_lat need not make a round trip through memory.
+ */
+mla_status mla_combine_expand_v(const mla_dims *dims, const void *o_part, const float *lse_part,
+                                int32_t num_splits, const void *w_uv, void *out, void *o_lat, float *lse,
+                                void *stream);
 
 /*
  * Fused decode step for short contexts: mla_absorb_q, mla_decode_latent with

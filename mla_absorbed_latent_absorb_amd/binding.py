@@ -24,7 +24,7 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
             "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused", "mla_naive_workspace_bytes",
-            "mla_naive_decode", "mla_prefill_latent"]
+            "mla_naive_decode", "mla_prefill_latent", "mla_combine_expand_v"]
 
 
 class MlaError(RuntimeError):
@@ -84,6 +84,8 @@ def load():
                                       P, P, P, P, P]
     lib.mla_combine_splits.restype = st
     lib.mla_combine_splits.argtypes = [D, P, P, ctypes.c_int32, P, P, P]
+    lib.mla_combine_expand_v.restype = st
+    lib.mla_combine_expand_v.argtypes = [D, P, P, ctypes.c_int32, P, P, P, P, P]
     lib.mla_expand_v.restype = st
     lib.mla_expand_v.argtypes = [D, P, P, P, P]
     lib.mla_cache_append.restype = st
@@ -306,6 +308,28 @@ def mla_expand_v(d, o_lat, w_uv, out=None, stream=None):
     return out
 
 
+def mla_combine_expand_v(d, o_part, lse_part, w_uv, out=None, o_lat=None, lse=None, stream=None):
+    """Split merge + value absorption in one launch -> out (bf16 [B, H, 128]).
+    o_lat / lse are written when given (else not at all)."""
+    B, H = d.batch, d.num_heads
+    P = o_part.shape[1]
+    dev = o_part.device
+    _expect(o_part, "o_part", torch.bfloat16, (B, P, H, d.kv_lora_rank))
+    _expect(lse_part, "lse_part", torch.float32, (B, P, H), dev)
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, d.v_head_dim, d.kv_lora_rank), dev)
+    if out is None:
+        out = torch.empty((B, H, d.v_head_dim), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), dev)
+    if o_lat is not None:
+        _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_combine_expand_v(ctypes.byref(d), _ptr(o_part), _ptr(lse_part), int(P), _ptr(w_uv), _ptr(out),
+                                       _ptr(o_lat) if o_lat is not None else None,
+                                       _ptr(lse) if lse is not None else None, _stream(stream)))
+    return out
+
+
 def mla_decode_step_fused(d, cache, q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, out=None, o_lat=None,
                           lse=None, want_latent=False, stream=None):
     """The three decode stages in one launch (short contexts).  Returns out,
@@ -389,11 +413,15 @@ def mla_cache_append(d, cache, kv_in, positions, rope_base=10000.0, stream=None)
 
 
 class DecodeStep:
-    """The four calls of one absorbed decode step with preallocated buffers
-    (so a timed or captured step allocates nothing)."""
+    """One absorbed decode step with preallocated buffers (so a timed or
+    captured step allocates nothing): mla_absorb_q, mla_decode_latent, then
+    mla_expand_v (one split) or mla_combine_expand_v (split-KV).  With
+    keep_latent the merged o_lat and lse are written too (the step's output is
+    `out` either way)."""
 
-    def __init__(self, d, cache, seq_lens, max_seq_len, num_splits, device):
+    def __init__(self, d, cache, seq_lens, max_seq_len, num_splits, device, keep_latent=True):
         B, H = d.batch, d.num_heads
+        self.keep_latent = bool(keep_latent)
         self.d, self.cache, self.seq_lens = d, cache, seq_lens
         self.max_seq_len, self.num_splits = int(max_seq_len), int(num_splits)
         bf, f32 = torch.bfloat16, torch.float32
@@ -417,8 +445,27 @@ class DecodeStep:
             mla_decode_latent(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len, 1,
                               o_lat=self.o_lat, lse=self.lse, stream=stream)
 
+    def decode(self, q_pe, stream=None):
+        """mla_decode_latent alone: partials (split-KV) or o_lat / lse."""
+        if self.num_splits > 1:
+            mla_decode_latent(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len,
+                              self.num_splits, o_part=self.o_part, lse_part=self.lse_part, stream=stream)
+        else:
+            mla_decode_latent(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len, 1,
+                              o_lat=self.o_lat, lse=self.lse, stream=stream)
+
+    def finish(self, w_uv, stream=None):
+        """What follows mla_decode_latent: the merge (if split) and W_UV."""
+        if self.num_splits > 1:
+            keep = self.keep_latent
+            mla_combine_expand_v(self.d, self.o_part, self.lse_part, w_uv, out=self.out,
+                                 o_lat=self.o_lat if keep else None, lse=self.lse if keep else None,
+                                 stream=stream)
+        else:
+            mla_expand_v(self.d, self.o_lat, w_uv, out=self.out, stream=stream)
+
     def __call__(self, q_nope, q_pe, w_uk, w_uv, stream=None):
         mla_absorb_q(self.d, q_nope, w_uk, q_lat=self.q_lat, stream=stream)
-        self.attend(q_pe, stream=stream)
-        mla_expand_v(self.d, self.o_lat, w_uv, out=self.out, stream=stream)
+        self.decode(q_pe, stream=stream)
+        self.finish(w_uv, stream=stream)
         return self.out

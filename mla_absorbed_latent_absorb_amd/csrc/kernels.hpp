@@ -55,6 +55,18 @@ struct CombineArgs {
   int32_t num_splits;
 };
 
+struct CombineExpandArgs {
+  const uint16_t* o_part; // [B, P, H, 512] bf16
+  const float* lse_part; // [B, P, H]
+  const uint16_t* w_uv;  // [H, 128, 512] bf16
+  uint16_t* out;         // [B, H, 128] bf16
+  uint16_t* o_lat;       // [B, H, 512] bf16 or null
+  float* lse;            // [B, H] or null
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_splits;
+};
+
 struct AppendArgs {
   const uint16_t* kv_in;      // [B, num_new, in_stride] bf16: 512 latent, then 64 unrotated key
   int64_t in_stride;          // elements between consecutive input rows
@@ -126,6 +138,8 @@ hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// combine + expand_v in one launch
+hipError_t launch_combine_expand(const CombineExpandArgs& a, hipStream_t stream);
 hipError_t launch_decode_step_fused(const FusedStepArgs& a, bool fp8, hipStream_t stream);
 // Naive decode: expansion GEMM into a.ws, then attention over the expanded rows.
 hipError_t launch_naive_decode(const NaiveArgs& a, bool fp8, hipStream_t stream);

@@ -276,6 +276,26 @@ mla_status mla_combine_splits(const mla_dims* dims, const void* o_part, const fl
   return launch_result(mla::launch_combine(a, static_cast<hipStream_t>(stream)), where);
 }
 
+mla_status mla_combine_expand_v(const mla_dims* dims, const void* o_part, const float* lse_part, int32_t num_splits,
+                                const void* w_uv, void* out, void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_combine_expand_v";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
+  REQUIRE_PTR(o_part, "o_part", where);
+  if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+  REQUIRE_PTR(w_uv, "w_uv", where);
+  REQUIRE_PTR(out, "out", where);
+  if (o_lat != nullptr && (reinterpret_cast<uintptr_t>(o_lat) & 15u))
+    return fail(MLA_ERR_ALIGN, "o_lat is not 16-byte aligned (%s)", where);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  mla::CombineExpandArgs a{static_cast<const uint16_t*>(o_part), lse_part, static_cast<const uint16_t*>(w_uv),
+                           static_cast<uint16_t*>(out), static_cast<uint16_t*>(o_lat), lse, dims->batch,
+                           dims->num_heads, num_splits};
+  return launch_result(mla::launch_combine_expand(a, static_cast<hipStream_t>(stream)), where);
+}
+
 mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
                              const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_part,
                              float* lse_part, void* o_lat, float* lse, void* stream) {

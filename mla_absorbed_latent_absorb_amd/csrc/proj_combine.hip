@@ -4,6 +4,7 @@
 //   "DeepSeek MLA 吸收式缓存：真实权重执行与 FlashMLA 架构边界" §2.2)
 // expand_v: out[b,h,j] = sum_c W_UV[h,j,c] o_lat[b,h,c]       (value absorption, §2.3)
 // combine : LSE = ln sum_i exp(lse_i); o = sum_i exp(lse_i - LSE) o_i
+// combine_expand: combine, then expand_v, in one launch
 //
 // Both projections are per-head batched GEMMs that are bound by reading the
 // weights once (16 MiB each for 128 heads); two workgroups per head, every
@@ -219,12 +220,92 @@ __global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: one wave per (sequence, head); lane l handles latent columns
-// 8 l .. 8 l + 7 of the bf16 partial rows.  The rows of the first 8 splits
-// and the split lse values are all requested before any of them is used (one
-// memory round trip); lane i holds split i's lse and weight, broadcast with
-// shuffles.  Splits past the first 8 (P > 8) are read in further groups of 8.
+// Split merge of one (sequence, head) row by one wave; lane l handles latent
+// columns 8 l .. 8 l + 7 of the bf16 partial rows.  The rows of the first 8
+// splits and the split lse values are all requested before any of them is
+// used (one memory round trip); lane i holds split i's lse and weight, read
+// by the other lanes with readlane; maxima and sums over the wave use DPP and
+// permlane swaps.  Splits past the first 8 (P > 8) are read in
+// further groups of 8.  combine_row_finish returns the lane's 8 merged
+// columns as bf16 and the row's lse (every lane).  combine_kernel and
+// combine_expand_kernel both merge through these functions, so their o_lat
+// bits agree.
 // ---------------------------------------------------------------------------
+struct CombineRow {
+  const float* lse_row;
+  const uint16_t* prow;
+  size_t split_stride;
+  float li0;
+  u32x4 v[8];
+};
+
+// Issue: lse of split `lane` (lanes < P, up to 64) and the first 8 rows.
+__device__ __forceinline__ CombineRow combine_row_issue(const uint16_t* o_part, const float* lse_part, int num_heads,
+                                                        int P, int b, int h, int lane) {
+  CombineRow r;
+  r.lse_row = lse_part + (size_t)b * P * num_heads + h;
+  r.prow = o_part + ((size_t)b * P * num_heads + h) * kDc + lane * 8;
+  r.split_stride = (size_t)num_heads * kDc;
+  // Loads are unconditional (splits past P re-read the last one; those
+  // values are never used): conditional loads make the compiler copy the
+  // results, which waits for them before the next row's loads are issued.
+  const float li = r.lse_row[(size_t)min(lane, P - 1) * num_heads];
+  r.li0 = lane < P ? li : -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r.v[j] = *reinterpret_cast<const u32x4*>(r.prow + (size_t)min(j, P - 1) * r.split_stride);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 combine_row_finish(CombineRow& r, int num_heads, int P, int lane, float& lse_out) {
+  float m = r.li0;
+  for (int i = 64 + lane; i < P; i += 64) m = fmaxf(m, r.lse_row[(size_t)i * num_heads]);
+  m = wave_max(m);
+
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  auto accumulate = [&](float wl, int n) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < n) {
+        const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          acc0[2 * e] += wi * __uint_as_float(r.v[j][e] << 16);
+          acc0[2 * e + 1] += wi * __uint_as_float(r.v[j][e] & 0xffff0000u);
+          acc1[2 * e] += wi * __uint_as_float(r.v[j][2 + e] << 16);
+          acc1[2 * e + 1] += wi * __uint_as_float(r.v[j][2 + e] & 0xffff0000u);
+        }
+      }
+    }
+  };
+  if (m != -INFINITY) {
+    // weight of split lane (0 for empty splits and lanes past P)
+    const float w0 = r.li0 == -INFINITY ? 0.f : __expf(r.li0 - m);
+    tot = wave_sum(w0);
+    accumulate(w0, min(P, 8));
+    for (int i0 = 8; i0 < P; i0 += 8) {
+      const int n = min(8, P - i0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < n) r.v[j] = *reinterpret_cast<const u32x4*>(r.prow + (size_t)(i0 + j) * r.split_stride);
+      // weights of splits i0 .. i0+7 on lanes 0..7 (the lse of splits >= 64 re-read here)
+      const int si = i0 + (lane & 7);
+      const float li = si < P ? r.lse_row[(size_t)si * num_heads] : -INFINITY;
+      const float wl = li == -INFINITY ? 0.f : __expf(li - m);
+      if (i0 >= 64) {
+        // splits 64.. were not in the lane-wise total above
+        tot += wave_sum(lane < 8 && si < P ? wl : 0.f);
+      }
+      accumulate(wl, n);
+    }
+  }
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  lse_out = tot > 0.f ? m + __logf(tot) : -INFINITY;
+  return u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
+               pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+}
+
+// combine: one wave per (sequence, head).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // Sequences map to XCDs the way the decode kernel's splits do, so a
   // sequence's partial rows may still be in that XCD's L2.
@@ -233,73 +314,95 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int b = wid / a.num_heads;
   const int h = wid - b * a.num_heads;
   const int lane = threadIdx.x & 63;
-  const int P = a.num_splits;
-  const float* lse_row = a.lse_part + (size_t)b * P * a.num_heads + h;
-  const uint16_t* prow = a.o_part + ((size_t)b * P * a.num_heads + h) * kDc + lane * 8;
-  const size_t split_stride = (size_t)a.num_heads * kDc;
+  float lse;
+  CombineRow r = combine_row_issue(a.o_part, a.lse_part, a.num_heads, a.num_splits, b, h, lane);
+  const u32x4 o = combine_row_finish(r, a.num_heads, a.num_splits, lane, lse);
+  *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + h) * kDc + lane * 8) = o;
+  if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.num_heads + h] = lse;
+}
 
-  // issue: lse of split `lane` (lanes < P, up to 64) and the first 8 rows
-  const float li0 = lane < P ? lse_row[(size_t)lane * a.num_heads] : -INFINITY;
-  u32x4 v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < P) v[j] = *reinterpret_cast<const u32x4*>(prow + (size_t)j * split_stride);
+// ---------------------------------------------------------------------------
+// combine_expand: the split merge and value absorption of one head for 16
+// sequences in one launch: out[b][h][:] = W_UV[h] . merge_i(o_part[b][i][h]).
+// Workgroup = (head h, sequences 16 bg .. +15), 16 waves in two roles, so
+// that no wave waits for loads it does not need:
+//   - waves 0 .. 7 merge sequences 16 bg + 2 w, + 1 with combine_row_issue /
+//     _finish (the same arithmetic as combine_kernel; both rows' loads are
+//     issued first) into rows of a 16-row bf16 tile in LDS (chunk ^ b % 16),
+//     also stored as o_lat / lse if asked for;
+//   - waves 8 .. 15 copy W_UV[h] (128 rows of 1 KiB) direct-to-LDS, 16 rows
+//     each (chunk ^ j % 16).
+//   Then D[j][b] = W . O^T as in expand_v_kernel (wave w < 8: rows 16 w ..
+//   +15, the same MFMA order), so out matches the two-launch path bit for bit.
+// The head's sequence groups are consecutive items on one XCD, which then
+// fetches W_UV[h] once.
+// ---------------------------------------------------------------------------
+constexpr int kCeRows = 16;                  // sequences per workgroup
+constexpr int kCeW = kDv * kDc * 2;          // 128 KiB
+constexpr int kCeO = kCeRows * kDc * 2;      // 16 KiB
 
-  float m = li0;
-  for (int i = 64 + lane; i < P; i += 64) m = fmaxf(m, lse_row[(size_t)i * a.num_heads]);
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+__global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kCeW + kCeO];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t wl = lds0, ol = lds0 + kCeW;
+  const int groups = (a.batch + kCeRows - 1) / kCeRows;
+  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
+  const int h = item / groups, bg = item - h * groups;
+  const int w = wave_id();
+  const int lane = threadIdx.x & 63;
+  const int nl = lane & 15, g = lane >> 4;
 
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  auto accumulate = [&](int i0, float wl, int n) {
+  if (w < 8) {
+    // rows 2 w, 2 w + 1 (sequences past the batch repeat the last one and
+    // are not stored)
+    int b[2];
+    CombineRow row[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < n) {
-        const float wi = __shfl(wl, j);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          acc0[2 * e] += wi * __uint_as_float(v[j][e] << 16);
-          acc0[2 * e + 1] += wi * __uint_as_float(v[j][e] & 0xffff0000u);
-          acc1[2 * e] += wi * __uint_as_float(v[j][2 + e] << 16);
-          acc1[2 * e + 1] += wi * __uint_as_float(v[j][2 + e] & 0xffff0000u);
-        }
-      }
+    for (int i = 0; i < 2; ++i) {
+      b[i] = min(kCeRows * bg + 2 * w + i, a.batch - 1);
+      row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, a.num_splits, b[i], h, lane);
     }
-    (void)i0;
-  };
-  if (m != -INFINITY) {
-    // weight of split lane (0 for empty splits and lanes past P)
-    const float w0 = li0 == -INFINITY ? 0.f : __expf(li0 - m);
-    float ws = w0;
 #pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) ws += __shfl_xor(ws, k);
-    tot = ws;
-    accumulate(0, w0, min(P, 8));
-    for (int i0 = 8; i0 < P; i0 += 8) {
-      const int n = min(8, P - i0);
+    for (int i = 0; i < 2; ++i) {
+      const int r = 2 * w + i;
+      const bool store = kCeRows * bg + r < a.batch;
+      float lse;
+      const u32x4 o = combine_row_finish(row[i], a.num_heads, a.num_splits, lane, lse);
+      lds_write_u32x4(ol + (uint32_t)r * 1024u + (((uint32_t)lane ^ ((uint32_t)r & 15u)) << 4), o);
+      if (store && a.o_lat != nullptr)
+        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b[i] * a.num_heads + h) * kDc + lane * 8) = o;
+      if (store && a.lse != nullptr && lane == 0) a.lse[(size_t)b[i] * a.num_heads + h] = lse;
+    }
+  } else {
+    // W_UV[h] rows 16 (w - 8) .. +15: copy k = row k, chunk slot ^ (k % 16)
+    const uint32_t ln = lane_id();
+    const char* wsrc = reinterpret_cast<const char*>(a.w_uv + (size_t)h * kDv * kDc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < n) v[j] = *reinterpret_cast<const u32x4*>(prow + (size_t)(i0 + j) * split_stride);
-      // weights of splits i0 .. i0+7 on lanes 0..7 (the lse of splits >= 64 re-read here)
-      const int si = i0 + (lane & 7);
-      const float li = si < P ? lse_row[(size_t)si * a.num_heads] : -INFINITY;
-      const float wl = li == -INFINITY ? 0.f : __expf(li - m);
-      if (i0 >= 64) {
-        // splits 64.. were not in the lane-wise total above
-        float wsum = lane < 8 && si < P ? wl : 0.f;
-#pragma unroll
-        for (int k = 32; k >= 1; k >>= 1) wsum += __shfl_xor(wsum, k);
-        tot += wsum;
-      }
-      accumulate(i0, wl, n);
+    for (int i = 0; i < 16; ++i) {
+      const int k = 16 * (w - 8) + i;
+      dma16(uniform_ptr(wsrc + (size_t)k * (kDc * 2)), (ln ^ (uint32_t)(k & 15)) * 16, wl + k * 1024);
     }
   }
-  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-  const u32x4 o = {pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
-                   pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
-  *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + h) * kDc + lane * 8) = o;
-  if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.num_heads + h] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+  wait_vmcnt<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier();
+  if (w >= kDv / 16) return;
+
+  const uint32_t jrow = 16 * w + nl;  // A row of this lane
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const uint32_t chunk = (uint32_t)(4 * s + g);
+    const bf16x8 aw = lds_read_b128(wl + jrow * 1024 + ((chunk ^ (jrow & 15u)) << 4));
+    const bf16x8 bo = lds_read_b128(ol + (uint32_t)nl * 1024 + ((chunk ^ ((uint32_t)nl & 15u)) << 4));
+    acc = mfma16(aw, bo, acc);
+  }
+  // D[j = 16 w + 4 g + r][b = 16 bg + nl]: four consecutive output columns
+  const int bo = kCeRows * bg + nl;
+  if (bo < a.batch) {
+    const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(a.out + ((size_t)bo * a.num_heads + h) * kDv + 16 * w + 4 * g) = v;
+  }
 }
 
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
@@ -309,6 +412,12 @@ hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
 
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(expand_v_kernel, dim3(a.num_heads * (kDv / kExpRows)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_expand(const CombineExpandArgs& a, hipStream_t stream) {
+  const int groups = (a.batch + kCeRows - 1) / kCeRows;
+  hipLaunchKernelGGL(combine_expand_kernel, dim3(a.num_heads * groups), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

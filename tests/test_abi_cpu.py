@@ -130,6 +130,17 @@ def test_combine_and_expand_validation(lib):
     assert lib.mla_combine_splits(ctypes.byref(d), None, P(16), 2, P(16), P(16), None) == 1
     assert lib.mla_expand_v(ctypes.byref(d), P(16), None, P(16), None) == 1
     assert "w_uv" in lib.mla_last_error().decode()
+    ce = lib.mla_combine_expand_v
+    assert ce(ctypes.byref(d), P(16), P(16), 0, P(16), P(16), None, None, None) == 4
+    assert ce(ctypes.byref(d), None, P(16), 2, P(16), P(16), None, None, None) == 1
+    assert ce(ctypes.byref(d), P(16), None, 2, P(16), P(16), None, None, None) == 1
+    assert "lse_part" in lib.mla_last_error().decode()
+    assert ce(ctypes.byref(d), P(16), P(16), 2, None, P(16), None, None, None) == 1
+    assert "w_uv" in lib.mla_last_error().decode()
+    assert ce(ctypes.byref(d), P(16), P(16), 2, P(16), None, None, None, None) == 1
+    assert ce(ctypes.byref(d), P(16), P(16), 2, P(16), P(16), P(24), None, None) == 6  # o_lat misaligned
+    assert ce(ctypes.byref(d), P(16), P(16), 2, P(16), P(16), None, P(18), None) == 6  # lse misaligned
+    assert "mla_combine_expand_v" in lib.mla_last_error().decode()
 
 
 def test_recommended_splits(lib):
