@@ -198,29 +198,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Whole-wave reductions without LDS: DPP within rows of 16 lanes (pairs
-// xor 1, xor 2, then the half-row and row mirrors), then the two permlane
-// swaps.  Every lane ends with the same value (each step combines two
-// operands with a commutative op).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm(1, 0, 3, 2)
-  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm(2, 3, 0, 1)
-  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
-  return max_xor32(max_xor16(x));
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x += dpp_f32<0xB1>(x);
-  x += dpp_f32<0x4E>(x);
-  x += dpp_f32<0x141>(x);
-  x += dpp_f32<0x140>(x);
-  return sum_xor32(sum_xor16(x));
-}
-
 __device__ __forceinline__ void lds_write_u8(uint32_t byte_off, uint32_t v) {
   *reinterpret_cast<__attribute__((address_space(3))) uint8_t*>((uintptr_t)byte_off) = (uint8_t)v;
 }
