@@ -108,7 +108,7 @@ __device__ __forceinline__ uint32_t lat_swz(uint32_t r) {
 
 }  // namespace
 
-template <int NBUF, bool PAGED>
+template <int NBUF, bool PAGED, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_latent_wide_kernel(DecodeArgs a) {
   static_assert(NBUF >= 3, "a tile's latent rows stay live for two iterations");
@@ -120,13 +120,23 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   constexpr int KV_PW = kTile / NW;       // latent rows copied per wave and tile
   constexpr int PE_PW = 4 / NW;           // RoPE copies (8 rows each) per wave
   constexpr int kCopies = KV_PW + PE_PW;  // copies per wave and tile
-  constexpr int NPE = NBUF - 1;           // RoPE ring length
+  // E4M3 cache (FP8): raw codes stream into a ring of 2 raw tiles and each
+  // wave decodes the 8 rows it copied into a ring of 3 bf16 tiles and 2 RoPE
+  // buffers (the LDS holds no fourth bf16 tile beside the raw ring).
+  constexpr int NLAT = FP8 ? 3 : NBUF;    // bf16 latent ring length
+  constexpr int NPE = FP8 ? 2 : NBUF - 1; // RoPE ring length
+  constexpr int NRAW = FP8 ? 2 : 0;       // raw E4M3 ring length
+  // raw tile, per wave: latent codes of rows 8w .. 8w+7 (8 x 512 B), their
+  // RoPE codes (8 x 64 B) and scales (8 x 4 B, then copies of the last)
+  constexpr int kRawWave = 8 * kDc + 8 * kDr + 256;
+  constexpr int kCopies8 = 4 + 2 + 1;     // E4M3 copies per wave and tile
   constexpr int kLatBytes = kTile * kKvRow;
   constexpr int kPeBytes = kTile * kPeRow;
   constexpr int kPeRing = 0;                    // RoPE ring, then the latent ring
   constexpr int kLatRing = kPeRing + NPE * kPeBytes;
   constexpr int kPBuf = NW * 2048;              // one tile's probabilities, [head tile][k-step] 1 KiB
-  constexpr int kPOff = kLatRing + NBUF * kLatBytes;
+  constexpr int kRawRing = kLatRing + NLAT * kLatBytes;
+  constexpr int kPOff = kRawRing + NRAW * NW * kRawWave;
   constexpr int kAlphaOff = kPOff + 2 * kPBuf;  // [2][H] rescale factors, then 1/l
   constexpr int kFlagOff = kAlphaOff + 2 * H * 4;  // [2][8] byte per wave: its softmax rescaled
   constexpr int kSmem = kFlagOff + 64;
@@ -134,9 +144,10 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // query staging (prologue only): per wave 16 latent rows (16 KiB) + 16
   // RoPE rows (2 KiB), from latent buffer 2 on (latent buffers 2 .. 3 and
   // the probability slots, all unused until tile 2 is issued)
-  constexpr int kQStage = kLatRing + 2 * kLatBytes;
+  constexpr int kQStage = FP8 ? kLatRing : kLatRing + 2 * kLatBytes;
   constexpr int kQWave = 16 * 1024 + 2048;
-  static_assert(NBUF == 4 && kQStage + NW * kQWave <= kAlphaOff, "query staging must fit before the factors");
+  static_assert(NBUF == 4 && kQStage + NW * kQWave <= (FP8 ? kRawRing : kAlphaOff),
+                "query staging must fit before the factors (E4M3: before the raw ring)");
   static_assert(NW * 32 * C * 2 <= kPOff, "epilogue staging must fit in the rings");
   static_assert(kLatBytes % 1024 == 0 && kPeBytes % 1024 == 0 && kLatRing % 1024 == 0 && kPOff % 1024 == 0,
                 "buffers must stay 1 KiB aligned");
@@ -222,8 +233,15 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     uint32_t peoff;   // per-lane source offset of the wave's RoPE copy
     uint32_t lat;     // LDS latent buffer
     uint32_t pe;      // LDS RoPE buffer
+    const char* sc0;  // E4M3: token scale of the source tile's first token
+    uint32_t raw;     // E4M3: this wave's region of the raw tile
+    int last;         // last valid row of the source tile
   };
-  auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NBUF) * kLatBytes; };
+  auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NLAT) * kLatBytes; };
+  // E4M3: this wave's region of the raw tile
+  auto raw_buf = [&](int tile) -> uint32_t {
+    return lds0 + kRawRing + (uint32_t)((tile & 1) * NW + w) * (uint32_t)kRawWave;
+  };
   auto pe_buf = [&](int tile) -> uint32_t { return lds0 + kPeRing + (uint32_t)(tile % NPE) * kPeBytes; };
   // Row offsets inside a tile fit 32 bits (token strides are below 2^24 bytes).
   const uint32_t kv_sb32 = (uint32_t)a.kv_sb, pe_sb32 = (uint32_t)a.pe_sb;
@@ -241,6 +259,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   const char* kv_next = kv_base + ((int64_t)cb * a.seq_stride + t_begin) * a.kv_sb;
   const char* pe_next = pe_base + ((int64_t)cb * a.seq_stride + t_begin) * a.pe_sb;
   const uint32_t kv_step = kTile * kv_sb32, pe_step = kTile * pe_sb32;
+  const char* sc_next = FP8 ? reinterpret_cast<const char*>(a.token_scale + (int64_t)cb * a.seq_stride + t_begin) : nullptr;
   auto tile_src = [&](int tile) -> TileSrc {
     const int src = min(tile, n_tiles - 1);
     const int t0 = t_begin + src * kTile;
@@ -255,14 +274,18 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       const int64_t slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
       ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
       ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
+      if (FP8) ts.sc0 = uniform_ptr(reinterpret_cast<const char*>(a.token_scale + slot0));
     } else {
       ts.kv0 = uniform_ptr(kv_next);
       ts.pe0 = uniform_ptr(pe_next);
+      if (FP8) ts.sc0 = uniform_ptr(sc_next);
       if (tile < n_tiles - 1) {
         kv_next += kv_step;
         pe_next += pe_step;
+        if (FP8) sc_next += kTile * 4;
       }
     }
+    ts.last = last;
     ts.kvoff = kvoff_full;
     ts.peoff = peoff_full;
     if (last < kTile - 1) {  // ragged tile: rows past the end re-read the last
@@ -274,6 +297,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     }
     ts.lat = lat_buf(tile);
     ts.pe = pe_buf(tile);
+    if (FP8) ts.raw = raw_buf(tile);
     return ts;
   };
   // Copy k < 8: latent block (w, k) (the immediate offset 128 k moves the
@@ -292,6 +316,48 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       case 7: dma16_off<896, 6272>(ts.kv0, ts.kvoff, blk0); break;
       default: dma16(ts.pe0, ts.peoff, ts.pe + (uint32_t)w * 1024u); break;
     }
+  };
+  // E4M3 copy k of this wave (rows 8w .. 8w+7 of the tile; rows past the end
+  // re-read the last): k < 4 latent rows 8w + 2k, +1 (16 B per lane); k = 4, 5
+  // RoPE rows 8w + 4(k-4) .. +3 (4 B per lane); k = 6 the 8 scales.
+  auto issue_copy8 = [&](const TileSrc& ts, int k) {
+    const uint32_t ln = lane_id();
+    if (k < 4) {
+      const uint32_t r = (uint32_t)min(8 * w + 2 * k + (int)(ln >> 5), ts.last);
+      dma16(ts.kv0, r * kv_sb32 + ((ln & 31u) << 4), ts.raw + (uint32_t)k * 1024u);
+    } else if (k < 6) {
+      const uint32_t r = (uint32_t)min(8 * w + 4 * (k - 4) + (int)(ln >> 4), ts.last);
+      dma4(ts.pe0, r * pe_sb32 + ((ln & 15u) << 2), ts.raw + (uint32_t)(8 * kDc + (k - 4) * 256));
+    } else {
+      const uint32_t r = (uint32_t)min(8 * w + min((int)ln, 7), ts.last);
+      dma4(ts.sc0, r * 4u, ts.raw + (uint32_t)(8 * kDc + 8 * kDr));
+    }
+  };
+  // E4M3: decode this wave's 8 rows of a raw tile (code times its token's
+  // scale in fp32, rounded to bf16) into the tile's bf16 latent and RoPE
+  // buffers.  Lane l: row 8w + l/8, 16-byte chunks (l % 8) + 8k.
+  auto expand = [&](int tile) {
+    const uint32_t rw = raw_buf(tile), lat = lat_buf(tile), pe = pe_buf(tile);
+    const uint32_t ln = lane_id();
+    const uint32_t r8 = ln >> 3, c8 = ln & 7u, r = 8u * (uint32_t)w + r8;
+    const float sc = lds_read_f32(rw + (uint32_t)(8 * kDc + 8 * kDr) + r8 * 4u);
+    auto dec = [&](u32x2 v) -> u32x4 {
+      u32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
+        out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
+      }
+      return out;
+    };
+    const uint32_t slot = (c8 ^ lat_swz(r)) << 4;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u32x2 v = lds_read_u32x2(rw + r8 * (uint32_t)kDc + (8u * (uint32_t)k + c8) * 8u);
+      lds_write_u32x4(lat + (8u * (uint32_t)w + (uint32_t)k) * 1024u + r8 * 128u + slot, dec(v));
+    }
+    const u32x2 v = lds_read_u32x2(rw + (uint32_t)(8 * kDc) + r8 * (uint32_t)kDr + c8 * 8u);
+    lds_write_u32x4(pe + r * (uint32_t)kPeRow + ((c8 ^ pe_swizzle(r)) << 4), dec(v));
   };
   auto issue_tile = [&](int tile) {
     const TileSrc ts = tile_src(tile);
@@ -343,18 +409,45 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // the reads are complete before the staging area is overwritten
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  stage_q(0);
-  issue_tile(0);
-  wait_vmcnt<kCopies>();
-  read_q(0);
-  stage_q(1);
-  issue_tile(1);
-  wait_vmcnt<kCopies>();
-  read_q(1);
-  // every wave has read its query block (the staging area is free) and its
-  // copies of tile 0 have landed; tile 1 may still be in flight
-  barrier();
-  issue_tile(2);
+  if constexpr (FP8) {
+    // E4M3: raw tiles 0 and 1 travel with the query halves (the raw ring is
+    // apart from the staging area); once every wave has read its query block,
+    // each wave decodes its rows of tiles 0 and 1 and requests raw tile 2
+    // into the raw buffer of tile 0, which its own decode has just read.
+    stage_q(0);
+    const TileSrc ts0 = tile_src(0);
+    const TileSrc ts1 = tile_src(1);
+#pragma unroll
+    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts0, k);
+#pragma unroll
+    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts1, k);
+    wait_vmcnt<2 * kCopies8>();
+    read_q(0);
+    stage_q(1);
+    wait_vmcnt<0>();
+    read_q(1);
+    barrier();
+    expand(0);
+    expand(1);
+    const TileSrc ts2 = tile_src(2);
+#pragma unroll
+    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts2, k);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();  // the bf16 tiles 0 and 1 are complete
+  } else {
+    stage_q(0);
+    issue_tile(0);
+    wait_vmcnt<kCopies>();
+    read_q(0);
+    stage_q(1);
+    issue_tile(1);
+    wait_vmcnt<kCopies>();
+    read_q(1);
+    // every wave has read its query block (the staging area is free) and its
+    // copies of tile 0 have landed; tile 1 may still be in flight
+    barrier();
+    issue_tile(2);
+  }
 
   // ---- per-lane LDS addresses inside a tile ----
   //   K fragment of score step s < 16, token half th: row 16 th + l%16, latent
@@ -504,7 +597,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // slot work of step st (two slots per step): this wave's copy i in the
     // first slot of step 2i + 1, P.V operand preloads in steps 0 .. 3
     auto slot = [&](int st, int k) {
-      if (DO_PV && (st & 1) == 1 && k == 0 && (st >> 1) < kCopies) issue_copy(nts, st >> 1);
+      if (DO_PV && (st & 1) == 1 && k == 0) {
+        if constexpr (FP8) {
+          if ((st >> 1) < kCopies8) issue_copy8(nts, st >> 1);
+        } else if ((st >> 1) < kCopies) {
+          issue_copy(nts, st >> 1);
+        }
+      }
       if (DO_PV) {
         if (k == 0 && st < 2) pf[2 * st] = pf_load(2 * st, 0);
         else if (k == 1 && st < 2) pf[2 * st + 1] = pf_load(2 * st + 1, 0);
@@ -641,11 +740,28 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{});
   for (int it = 0; it < n_tiles; ++it) {
     const bool has_next = it + 1 < n_tiles;
-    wait_vmcnt<kCopies>();
+    if constexpr (FP8) {
+      // E4M3: tile it + 1 was decoded (by every wave) in iteration it - 1
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      wait_vmcnt<kCopies>();
+    }
     barrier();  // barrier A
     __builtin_amdgcn_sched_barrier(0);
-    const TileSrc nts = tile_src(it + NBUF - 1);
+    const TileSrc nts = tile_src(it + 3);
     iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts);
+    if constexpr (FP8) {
+      // Decode this wave's rows of tile it + 2 (its raw copies, requested in
+      // iteration it - 1, have landed; those of tile it + 3 may be in
+      // flight) into the bf16 buffers of tiles it - 1 (free since barrier A)
+      // and it (RoPE rows, read by the scores of iteration it - 1).  Past the
+      // last tile the source is the last tile, so the bytes written equal
+      // the ones already there.
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kCopies8>();
+      expand(it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the last tile
@@ -657,6 +773,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // every wave is done with the tiles and the rescale factors, and its last
   // copies (past the last tile) have landed before the rings are reused
   wait_vmcnt<0>();
+  if constexpr (FP8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
   if (q4 == 0) {
 #pragma unroll
@@ -715,14 +832,20 @@ void decode_latent_wide_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream) {
-  if (a.fp8 || a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1)))
+  if (a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1 || a.fp8)))
     return hipErrorInvalidValue;
   const int groups = (a.q_per_seq + a.q_group - 1) / a.q_group;
   const int grid = (a.q_group > 1 ? (a.batch / a.q_per_seq) * groups : a.batch) * a.num_splits;
-  if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((decode_latent_wide_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a);
+  if (a.fp8) {
+    if (a.block_table != nullptr) {
+      hipLaunchKernelGGL((decode_latent_wide_kernel<4, true, true>), dim3(grid), dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_latent_wide_kernel<4, false, true>), dim3(grid), dim3(256), 0, stream, a);
+    }
+  } else if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, true, false>), dim3(grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_latent_wide_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, false, false>), dim3(grid), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
