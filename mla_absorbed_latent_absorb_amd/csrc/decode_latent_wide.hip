@@ -126,8 +126,11 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   constexpr int NLAT = FP8 ? 3 : NBUF;    // bf16 latent ring length
   constexpr int NPE = FP8 ? 2 : NBUF - 1; // RoPE ring length
   constexpr int NRAW = FP8 ? 2 : 0;       // raw E4M3 ring length
-  // raw tile, per wave: latent codes of rows 8w .. 8w+7 (8 x 512 B), their
-  // RoPE codes (8 x 64 B) and scales (8 x 4 B, then copies of the last)
+  // raw tile, per wave: latent codes of rows 8w .. 8w+7 (8 x 512 B) as four
+  // 1 KiB column blocks (16-byte chunk j of row r at (j / 8) KiB + 128 r +
+  // 16 (j % 8)), their RoPE codes (8 x 64 B) as two 256 B halves (byte b of
+  // row r at 4 KiB + 256 (b / 32) + 32 r + b % 32), and scales (8 x 4 B,
+  // then copies)
   constexpr int kRawWave = 8 * kDc + 8 * kDr + 256;
   constexpr int kCopies8 = 4 + 2 + 1;     // E4M3 copies per wave and tile
   constexpr int kLatBytes = kTile * kKvRow;
@@ -235,7 +238,9 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     uint32_t pe;      // LDS RoPE buffer
     const char* sc0;  // E4M3: token scale of the source tile's first token
     uint32_t raw;     // E4M3: this wave's region of the raw tile
-    int last;         // last valid row of the source tile
+    uint32_t roff8;   // E4M3: per-lane row part of the latent source offset (row 8w + l/8, clamped)
+    uint32_t poff8;   // E4M3: the same for the RoPE codes
+    uint32_t soff8;   // E4M3: per-lane scale offset (row 8w + l%8, clamped)
   };
   auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NLAT) * kLatBytes; };
   // E4M3: this wave's region of the raw tile
@@ -285,7 +290,15 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         if (FP8) sc_next += kTile * 4;
       }
     }
-    ts.last = last;
+    if (FP8) {
+      // rows past the end re-read the last
+      const uint32_t ln = lane_id();
+      const uint32_t rc = (uint32_t)min(8 * w + (int)(ln >> 3), last);
+      const uint32_t rs = (uint32_t)min(8 * w + (int)(ln & 7u), last);
+      ts.roff8 = rc * kv_sb32 + ((ln & 7u) << 4);
+      ts.poff8 = rc * pe_sb32 + ((ln & 7u) << 2);
+      ts.soff8 = rs * 4u;
+    }
     ts.kvoff = kvoff_full;
     ts.peoff = peoff_full;
     if (last < kTile - 1) {  // ragged tile: rows past the end re-read the last
@@ -317,47 +330,60 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       default: dma16(ts.pe0, ts.peoff, ts.pe + (uint32_t)w * 1024u); break;
     }
   };
-  // E4M3 copy k of this wave (rows 8w .. 8w+7 of the tile; rows past the end
-  // re-read the last): k < 4 latent rows 8w + 2k, +1 (16 B per lane); k = 4, 5
-  // RoPE rows 8w + 4(k-4) .. +3 (4 B per lane); k = 6 the 8 scales.
+  // E4M3 copy k of this wave (rows 8w .. 8w+7 of the tile): k < 4 latent
+  // column block k (16 B per lane: row l/8, chunk 8k + l%8); k = 4, 5 RoPE
+  // bytes 32(k-4) .. +31 (4 B per lane: row l/8); k = 6 the 8 scales.  The
+  // immediate offset moves the source and the destination by the same
+  // amount, so one per-lane offset serves every copy of a kind.
   auto issue_copy8 = [&](const TileSrc& ts, int k) {
-    const uint32_t ln = lane_id();
-    if (k < 4) {
-      const uint32_t r = (uint32_t)min(8 * w + 2 * k + (int)(ln >> 5), ts.last);
-      dma16(ts.kv0, r * kv_sb32 + ((ln & 31u) << 4), ts.raw + (uint32_t)k * 1024u);
-    } else if (k < 6) {
-      const uint32_t r = (uint32_t)min(8 * w + 4 * (k - 4) + (int)(ln >> 4), ts.last);
-      dma4(ts.pe0, r * pe_sb32 + ((ln & 15u) << 2), ts.raw + (uint32_t)(8 * kDc + (k - 4) * 256));
-    } else {
-      const uint32_t r = (uint32_t)min(8 * w + min((int)ln, 7), ts.last);
-      dma4(ts.sc0, r * 4u, ts.raw + (uint32_t)(8 * kDc + 8 * kDr));
+    switch (k) {
+      case 0: dma16_off<0, 0>(ts.kv0, ts.roff8, ts.raw); break;
+      case 1: dma16_off<128, 896>(ts.kv0, ts.roff8, ts.raw); break;
+      case 2: dma16_off<256, 1792>(ts.kv0, ts.roff8, ts.raw); break;
+      case 3: dma16_off<384, 2688>(ts.kv0, ts.roff8, ts.raw); break;
+      case 4: dma4_off<0, 4096>(ts.pe0, ts.poff8, ts.raw); break;
+      case 5: dma4_off<32, 4096 + 224>(ts.pe0, ts.poff8, ts.raw); break;
+      default: dma4(ts.sc0, ts.soff8, ts.raw + (uint32_t)(8 * kDc + 8 * kDr)); break;
     }
   };
   // E4M3: decode this wave's 8 rows of a raw tile (code times its token's
   // scale in fp32, rounded to bf16) into the tile's bf16 latent and RoPE
   // buffers.  Lane l: row 8w + l/8, 16-byte chunks (l % 8) + 8k.
-  auto expand = [&](int tile) {
-    const uint32_t rw = raw_buf(tile), lat = lat_buf(tile), pe = pe_buf(tile);
-    const uint32_t ln = lane_id();
-    const uint32_t r8 = ln >> 3, c8 = ln & 7u, r = 8u * (uint32_t)w + r8;
-    const float sc = lds_read_f32(rw + (uint32_t)(8 * kDc + 8 * kDr) + r8 * 4u);
-    auto dec = [&](u32x2 v) -> u32x4 {
-      u32x4 out;
+  // Per-lane parts of the decode addresses (lane l: row 8w + l/8, bf16
+  // chunks 8i + l%8 of the latent row for i < 8, RoPE chunk l%8 for i = 8),
+  // computed once where they are used; chunk i adds an immediate.
+  struct XAddr {
+    uint32_t src, src_pe, dst, dst_pe, sc;
+  };
+  auto x_addr = [&](int tile) -> XAddr {
+    const uint32_t ln = lane_id(), r8 = ln >> 3, c8 = ln & 7u, r = 8u * (uint32_t)w + r8;
+    const uint32_t rw = raw_buf(tile);
+    XAddr x;
+    x.src = rw + r8 * 128u + c8 * 8u;
+    x.src_pe = rw + (uint32_t)(8 * kDc) + (c8 >> 2) * 256u + r8 * 32u + (c8 & 3u) * 8u;
+    x.dst = lat_buf(tile) + 8u * (uint32_t)w * 1024u + r8 * 128u + ((c8 ^ lat_swz(r)) << 4);
+    x.dst_pe = pe_buf(tile) + r * (uint32_t)kPeRow + ((c8 ^ pe_swizzle(r)) << 4);
+    x.sc = rw + (uint32_t)(8 * kDc + 8 * kDr) + r8 * 4u;
+    return x;
+  };
+  auto x_src = [&](const XAddr& x, int i) -> uint32_t {
+    return i < 8 ? x.src + (uint32_t)(i >> 1) * 1024u + (uint32_t)(i & 1) * 64u : x.src_pe;
+  };
+  auto x_dst = [&](const XAddr& x, int i) -> uint32_t { return i < 8 ? x.dst + (uint32_t)i * 1024u : x.dst_pe; };
+  auto x_dec = [&](u32x2 v, float sc) -> u32x4 {
+    u32x4 out;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
-        out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
-      }
-      return out;
-    };
-    const uint32_t slot = (c8 ^ lat_swz(r)) << 4;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x2 v = lds_read_u32x2(rw + r8 * (uint32_t)kDc + (8u * (uint32_t)k + c8) * 8u);
-      lds_write_u32x4(lat + (8u * (uint32_t)w + (uint32_t)k) * 1024u + r8 * 128u + slot, dec(v));
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
+      out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
     }
-    const u32x2 v = lds_read_u32x2(rw + (uint32_t)(8 * kDc) + r8 * (uint32_t)kDr + c8 * 8u);
-    lds_write_u32x4(pe + r * (uint32_t)kPeRow + ((c8 ^ pe_swizzle(r)) << 4), dec(v));
+    return out;
+  };
+  auto expand = [&](int tile) {
+    const XAddr x = x_addr(tile);
+    const float sc = lds_read_f32(x.sc);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) lds_write_u32x4(x_dst(x, i), x_dec(lds_read_u32x2(x_src(x, i)), sc));
   };
   auto issue_tile = [&](int tile) {
     const TileSrc ts = tile_src(tile);
@@ -540,7 +566,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   //   O *= alpha of slot pb if any wave's softmax of tile tv moved its
   //   reference max.
   auto iteration = [&](auto pv_tag, int tq, Scores& sc, int tv, int pb, int ps, bool rescale_check,
-                       bool commit, const TileSrc& nts) {
+                       bool commit, const TileSrc& nts, int tx) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
     // one byte per wave; read now, tested after the deferred MFMAs
     const uint32_t flags = DO_PV ? lds_read_u32(lds0 + kFlagOff + pb * 8) : 0u;
@@ -710,6 +736,11 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         if (lane == 0) lds_write_u8(lds0 + kFlagOff + ps * 8 + w, any_grow ? 1u : 0u);
       }
     };
+    // E4M3: this wave's rows of tile tx are decoded in 9 chunks, one after
+    // every third P.V MFMA, each chunk's LDS read issued a chunk ahead.
+    u32x2 xr[2];
+    float xsc = 0.f;
+    XAddr xa{};
 #pragma unroll
     for (int m = 0; m < 28; ++m) {
       if (DO_PV) {
@@ -720,6 +751,24 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         if (m >= 12 && m < 16) pf[n] = pf_load(n, 1);
       }
       softmax_chunk(m);
+      if constexpr (FP8) {
+        if (DO_PV) {
+          if (m == 0) {
+            // raw tile tx was requested an iteration ago; only tile tx + 1's
+            // copies (issued in the score phase) may still be in flight
+            wait_vmcnt<kCopies8>();
+            xa = x_addr(tx);
+            xsc = lds_read_f32(xa.sc);
+            xr[0] = lds_read_u32x2(x_src(xa, 0));
+          }
+          if (m % 3 == 1 && m / 3 < 9) {
+            const int i = m / 3;
+            const u32x2 cur = xr[i & 1];
+            if (i + 1 < 9) xr[(i + 1) & 1] = lds_read_u32x2(x_src(xa, i + 1));
+            lds_write_u32x4(x_dst(xa, i), x_dec(cur, xsc));
+          }
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -737,7 +786,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   static_assert(NBUF == 4, "the waits count one tile of copies in flight");
   Scores sc;
   __builtin_amdgcn_sched_barrier(0);
-  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{});
+  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{}, 0);
   for (int it = 0; it < n_tiles; ++it) {
     const bool has_next = it + 1 < n_tiles;
     if constexpr (FP8) {
@@ -749,19 +798,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     barrier();  // barrier A
     __builtin_amdgcn_sched_barrier(0);
     const TileSrc nts = tile_src(it + 3);
-    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts);
-    if constexpr (FP8) {
-      // Decode this wave's rows of tile it + 2 (its raw copies, requested in
-      // iteration it - 1, have landed; those of tile it + 3 may be in
-      // flight) into the bf16 buffers of tiles it - 1 (free since barrier A)
-      // and it (RoPE rows, read by the scores of iteration it - 1).  Past the
-      // last tile the source is the last tile, so the bytes written equal
-      // the ones already there.
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<kCopies8>();
-      expand(it + 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    // E4M3: the P.V phase also decodes this wave's rows of tile it + 2 (its
+    // raw copies, requested in iteration it - 1, have landed; those of tile
+    // it + 3 may be in flight) into the bf16 buffers of tiles it - 1 (free
+    // since barrier A) and it (RoPE rows, read by the scores of iteration
+    // it - 1).  Past the last tile the source is the last tile, so the bytes
+    // written equal the ones already there.
+    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts, it + 2);
   }
 #pragma unroll
   for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the last tile

@@ -82,6 +82,18 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// The same with the immediate offset OFF (added to both addresses, as for
+// dma16_off) and M0 = lds_base + MADD.
+template <int OFF, int MADD>
+__device__ __forceinline__ void dma4_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 offset:%3"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF), "n"(MADD)
+               : "memory");
+}
+
 // Two OCP E4M3 (e4m3fn) codes, bytes 2*HI and 2*HI+1 of a 32-bit word, to
 // fp32 (exact).
 template <bool HI>
