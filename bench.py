@@ -116,9 +116,9 @@ COPY_ELEMS = 1 << 28          # float32 elements of the calibration copy (1 GiB 
 PMC_COMMANDS = [
     "export TMPDIR=/tmp",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $PWD/gpurun_out/pmc_fetch -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill --no-fp8",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $PWD/gpurun_out/pmc_write -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill --no-fp8",
     "python bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
     "gpurun_out/pmc_write/run_counter_collection.csv",
 ]
@@ -334,6 +334,48 @@ def bench_prefill(dev):
     return res
 
 
+def bench_fp8(dev):
+    """The E4M3 long-context workload (V3 shape, B=64, T=32,768, OCP E4M3 cache
+    with a per-token fp32 scale): mla_decode_latent alone, alternating two
+    input replicas (2.4 GB, beyond the Infinity Cache), graph-replayed;
+    latent-cache GB/s (576 code bytes + 4 scale bytes per token) and TFLOP/s
+    (2 * H * (576 + 512) per cached token, on bf16 MFMAs after the decode)."""
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    wl = datagen.WORKLOADS["v3_b64_s32768_fp8"]
+    reps = [datagen.make_inputs(wl, device=dev) for _ in range(2)]
+    x0 = reps[0]
+    d = binding.dims(x0.batch, x0.heads, x0.scale)
+    P = binding.mla_recommended_splits(d, x0.max_seq_len, torch.cuda.get_device_properties(dev).multi_processor_count)
+    steps = []
+    for x in reps:
+        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, token_scale=x.token_scale)
+        st = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev, keep_latent=False)
+        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
+        steps.append((x, st))
+    k = [0]
+
+    def call():
+        x, st = steps[k[0] % 2]
+        k[0] += 1
+        st.decode(x.q_pe)
+
+    call()
+    torch.cuda.synchronize()
+    t = graph_time_per_call(call, 4, 3)
+    lens_sum = int(x0.seq_lens.to(torch.int64).sum().item())
+    nbytes = x0.cache_bytes()
+    flops = core_flops(x0.batch, x0.heads, lens_sum)
+    gbs, tf = nbytes / t / 1e9, flops / t / 1e12
+    out = {"workload": wl.name, "kernel": "mla_decode_latent", "splits": P, "decode_us": round(t * 1e6, 1),
+           "cache_bytes": nbytes, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "tflops": round(tf, 1), "mfma_frac_bf16": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+    del steps, reps
+    torch.cuda.empty_cache()
+    return out
+
+
 FUSED_MAX_CONTEXT = 2048   # the fused one-launch step is timed on short contexts only
 
 
@@ -461,6 +503,7 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--no-naive", action="store_true", help="skip the naive-decode baseline and context sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3 long-context decode measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
@@ -604,6 +647,8 @@ def main():
     }
     if x0.max_seq_len <= FUSED_MAX_CONTEXT:
         result["fused_step"] = bench_fused_step(x0, d, dev, args.steps)
+    if not args.no_fp8 and wl.name != "v3_b64_s32768_fp8":
+        result["fp8_long_context"] = bench_fp8(dev)
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev)
     if not args.no_naive:

@@ -33,6 +33,12 @@
 //     barrier per tile.
 //   - The running max of a head moves only when it grows by more than
 //     2^kRescaleLog2 in the exp2 domain, so O is rarely rescaled.
+//   - E4M3 cache (FP8): each wave copies the raw codes, RoPE codes and
+//     per-token scales of its own 8 rows of a tile into a ring of 2 raw
+//     tiles, and decodes them (code times scale in fp32, rounded to bf16)
+//     into a ring of 3 bf16 tiles and 2 RoPE buffers, in chunks spread over
+//     the P.V MFMAs of the iteration two tiles earlier; the matrix products
+//     are then those of a bf16 cache.
 #include <type_traits>
 
 #include "device_common.hpp"
