@@ -874,8 +874,11 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     for (int k = 0; k < KR; ++k) {
       const uint32_t L = (uint32_t)(64 * k + lane);
       const uint32_t row = L / RC, ch = L % RC;
+      // Non-temporal stores: every workgroup writes its 128 KiB of partials at
+      // the same moment and nothing here reads them again; streaming them
+      // past the caches measured 4.5 us faster per V3 launch than plain stores.
       if ((int)(32 * n + row) < n_rows)
-        *reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8) = v[k];
+        __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(out_rows + (size_t)(32 * n + row) * kDc + col0 + ch * 8));
     }
   }
 }
