@@ -151,8 +151,10 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   constexpr int kSmem = kFlagOff + 64;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   // query staging (prologue only): per wave 16 latent rows (16 KiB) + 16
-  // RoPE rows (2 KiB), from latent buffer 2 on (latent buffers 2 .. 3 and
-  // the probability slots, all unused until tile 2 is issued)
+  // RoPE rows (2 KiB).  bf16: from latent buffer 2 on (latent buffers 2 .. 3
+  // and the probability slots, all unused until tile 2 is issued); E4M3:
+  // from latent buffer 0 on (the bf16 ring is written only after every
+  // wave has read its query block; the raw ring lies past it)
   constexpr int kQStage = FP8 ? kLatRing : kLatRing + 2 * kLatBytes;
   constexpr int kQWave = 16 * 1024 + 2048;
   static_assert(NBUF == 4 && kQStage + NW * kQWave <= (FP8 ? kRawRing : kAlphaOff),
