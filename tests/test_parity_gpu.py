@@ -333,3 +333,33 @@ def test_fp8_decode_matches_bf16_decode_of_the_decoded_cache():
     torch.cuda.synchronize()
     assert rel_err(f64(o8), f64(o16)) <= 1e-2
     assert float(torch.max(torch.abs(l8 - l16))) <= 1e-2
+
+
+# lengths 0 (o = 0, lse = -inf), 1, a ragged 33 and one above max_seq_len
+# (clamped to it) in one batch; with 3 splits some splits are empty
+EDGE_CASES = [("v3_b32_s4096", 128, 1), ("v3_b32_s4096", 128, 3), ("v3_b64_s32768_fp8", 128, 1),
+              ("v3_b64_s32768_fp8", 128, 3), ("v3_b32_s4096", 16, 2), ("v3_b64_s32768_fp8", 32, 1)]
+
+
+@pytest.mark.parametrize("workload,H,P", EDGE_CASES)
+def test_decode_lengths_zero_one_ragged_and_clamped(workload, H, P):
+    S = 100
+    announce(f"decode lengths 0/1/33/clamped {workload} H={H} P={P}")
+    x = _inputs(workload, batch=4, seq_len=S, heads=H)
+    lens = torch.tensor([0, 1, 33, S + 100], dtype=torch.int32, device=DEV)
+    d = binding.dims(4, H, x.scale)
+    q_lat = datagen.random_latent_queries(4, H, seed=7, device=DEV)
+    cache = _cache(x)
+    if P == 1:
+        o_lat, lse = binding.mla_decode_latent(d, cache, q_lat, x.q_pe, lens, S, 1)
+    else:
+        o_part, lse_part = binding.mla_decode_latent(d, cache, q_lat, x.q_pe, lens, S, P)
+        o_lat, lse = binding.mla_combine_splits(d, o_part, lse_part)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=np.array([0, 1, 33, S]), scale=x.scale,
+                                        **cache_args(x))
+    got, gl = f64(o_lat), lse.cpu().numpy()
+    assert np.all(got[0] == 0) and np.isneginf(gl[0]).all()
+    for b in (1, 2, 3):
+        assert rel_err(got[b], ref_o[b]) <= TOL_BF16, b
+        assert np.max(np.abs(gl[b] - ref_l[b])) <= TOL_BF16, b
