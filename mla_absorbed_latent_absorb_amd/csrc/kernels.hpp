@@ -65,6 +65,7 @@ struct CombineExpandArgs {
   int32_t batch;
   int32_t num_heads;
   int32_t num_splits;
+  int32_t rows;          // sequences per workgroup: 4, 8 or 16 (set by the launcher)
 };
 
 struct AppendArgs {

@@ -347,12 +347,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // ---------------------------------------------------------------------------
 // combine_expand: the split merge and value absorption of one head for 16
 // sequences in one launch: out[b][h][:] = W_UV[h] . merge_i(o_part[b][i][h]).
-// Workgroup = (head h, sequences 16 bg .. +15), 16 waves in two roles, so
-// that no wave waits for loads it does not need:
-//   - waves 0 .. 7 merge sequences 16 bg + 2 w, + 1 with combine_row_issue /
+// Workgroup = (head h, sequences R bg .. R bg + R - 1), R = 4, 8 or 16 (fewer
+// when batch x heads is small, so the launch still spans the chip), 16 waves
+// in two roles, so that no wave waits for loads it does not need:
+//   - waves w < R / 2 merge sequences R bg + 2 w, + 1 with combine_row_issue /
 //     _finish (the same arithmetic as combine_kernel; both rows' loads are
 //     issued first) into rows of a 16-row bf16 tile in LDS (chunk ^ b % 16),
-//     also stored as o_lat / lse if asked for;
+//     also stored as o_lat / lse if asked for (tile rows past R are not
+//     written: the MFMA columns they feed are not stored);
 //   - waves 8 .. 15 copy W_UV[h] (128 rows of 1 KiB) direct-to-LDS, 16 rows
 //     each (chunk ^ j % 16).
 //   Then D[j][b] = W . O^T as in expand_v_kernel (wave w < 8: rows 16 w ..
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 // The head's sequence groups are consecutive items on one XCD, which then
 // fetches W_UV[h] once.
 // ---------------------------------------------------------------------------
-constexpr int kCeRows = 16;                  // sequences per workgroup
+constexpr int kCeRows = 16;                  // most sequences per workgroup
 constexpr int kCeW = kDv * kDc * 2;          // 128 KiB
 constexpr int kCeO = kCeRows * kDc * 2;      // 16 KiB
 
@@ -368,27 +370,28 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
   __shared__ __attribute__((aligned(1024))) char smem[kCeW + kCeO];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t wl = lds0, ol = lds0 + kCeW;
-  const int groups = (a.batch + kCeRows - 1) / kCeRows;
+  const int R = a.rows;
+  const int groups = (a.batch + R - 1) / R;
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
   const int h = item / groups, bg = item - h * groups;
   const int w = wave_id();
   const int lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
 
-  if (w < 8) {
+  if (2 * w < R) {
     // rows 2 w, 2 w + 1 (sequences past the batch repeat the last one and
     // are not stored)
     int b[2];
     CombineRow row[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      b[i] = min(kCeRows * bg + 2 * w + i, a.batch - 1);
+      b[i] = min(R * bg + 2 * w + i, a.batch - 1);
       row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, a.num_splits, b[i], h, lane);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 2 * w + i;
-      const bool store = kCeRows * bg + r < a.batch;
+      const bool store = R * bg + r < a.batch;
       float lse;
       const u32x4 o = combine_row_finish(row[i], a.num_heads, a.num_splits, lane, lse);
       lds_write_u32x4(ol + (uint32_t)r * 1024u + (((uint32_t)lane ^ ((uint32_t)r & 15u)) << 4), o);
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
         *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b[i] * a.num_heads + h) * kDc + lane * 8) = o;
       if (store && a.lse != nullptr && lane == 0) a.lse[(size_t)b[i] * a.num_heads + h] = lse;
     }
-  } else {
+  } else if (w >= 8) {
     // W_UV[h] rows 16 (w - 8) .. +15: copy k = row k, chunk slot ^ (k % 16)
     const uint32_t ln = lane_id();
     const char* wsrc = reinterpret_cast<const char*>(a.w_uv + (size_t)h * kDv * kDc);
@@ -421,8 +424,8 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
     acc = mfma16(aw, bo, acc);
   }
   // D[j = 16 w + 4 g + r][b = 16 bg + nl]: four consecutive output columns
-  const int bo = kCeRows * bg + nl;
-  if (bo < a.batch) {
+  const int bo = R * bg + nl;
+  if (nl < R && bo < a.batch) {
     const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     *reinterpret_cast<u32x2*>(a.out + ((size_t)bo * a.num_heads + h) * kDv + 16 * w + 4 * g) = v;
   }
@@ -438,8 +441,12 @@ hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine_expand(const CombineExpandArgs& a, hipStream_t stream) {
-  const int groups = (a.batch + kCeRows - 1) / kCeRows;
+hipError_t launch_combine_expand(const CombineExpandArgs& a_in, hipStream_t stream) {
+  CombineExpandArgs a = a_in;
+  // sequences per workgroup: 16 while the grid has >= 256 workgroups, else fewer
+  const int64_t rows_total = (int64_t)a.batch * a.num_heads;
+  a.rows = rows_total >= 256 * kCeRows ? kCeRows : (rows_total >= 256 * 8 ? 8 : 4);
+  const int groups = (a.batch + a.rows - 1) / a.rows;
   hipLaunchKernelGGL(combine_expand_kernel, dim3(a.num_heads * groups), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
