@@ -260,7 +260,7 @@ def bench_naive(x0, d, dev, absorbed_step_s):
 
 
 def bench_crossover(dev):
-    """Naive vs absorbed (four calls) vs fused one-launch step against context
+    """Naive vs absorbed (three launches) vs fused one-launch step against context
     length at the V2-Lite shape with one sequence (H=16), the setting of the
     pages' naive-vs-absorbed latency comparison; GPU time per step from graph
     replays."""
