@@ -174,6 +174,10 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  *           by its own softmax sum) and lse_part (device fp32 [B, P, H]); an
  *           empty split gets o = 0 and lse = -inf.  o_lat / lse must be NULL;
  *           merge with mla_combine_splits.
+ * Precision choices (differences from a design with fp32 partials and an
+ * fp8 query): the partials are bf16, since each split's o_i is a normalised
+ * average with the relative rounding error of the bf16 o_lat, and there is
+ * no query scale argument, since the queries stay bf16 for every cache dtype.
  * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): each tile of cached rows
  * is decoded (value = e4m3(code) * token_scale[slot], in fp32) and rounded to
  * bf16 before the same bf16 matrix products as a bf16 cache; the queries stay
@@ -214,7 +218,10 @@ mla_status mla_prefill_latent(const mla_dims *dims, const mla_cache *cache, cons
                               void *o_part, float *lse_part, void *o_lat, float *lse, void *stream);
 
 /*
- * Split-KV merge: LSE = ln sum_i exp(lse_part[b,i,h]),
+ * Split-KV merge ([G5SPEC] Appendix B: the cache is read concurrently by
+ * several workers and their attention results combined; the merge is the
+ * log-sum-exp identity of softmax over a union of token ranges):
+ * LSE = ln sum_i exp(lse_part[b,i,h]),
  * o_lat[b,h] = sum_i exp(lse_part[b,i,h] - LSE) * o_part[b,i,h]; splits with
  * lse = -inf carry no weight.
  *   o_part device bf16 [B, P, H, 512], lse_part device fp32 [B, P, H]
@@ -299,32 +306,6 @@ mla_status mla_naive_decode(const mla_dims *dims, const mla_cache *cache, const 
                             void *workspace, size_t workspace_bytes, void *out, void *stream);
 
 /*
- * Cache append: writes num_new new tokens/*
- * Cache append: writes num_new new tokens/*
- * Naive decode, the baseline the absorbed path is compared with ([MLA80] §4
- * path A and §5: the base decode re-applies the up-projections to the whole
- * latent cache every step; [AUDIT] §2: per-head expanded keys and values).
- * Every step expands each cached token t < seq_lens[b] into
- *   k_nope[t,h] = W_UK[h] c_t,  v[t,h] = W_UV[h] c_t      (bf16, in workspace)
- * and runs multi-head attention with keys [k_nope[t,h] | kR_t] and values
- * v[t,h]: out[b,h] = sum_t softmax_t(softmax_scale * (q_nope . k_nope +
- * q_pe . kR_t)) v[t,h].  Same result as the absorbed path up to rounding.
- *   q_nope, q_pe, w_uk, w_uv, seq_lens, max_seq_len, cache: as in
- *     mla_absorb_q / mla_decode_latent / mla_expand_v
- *   workspace  device, at least mla_naive_workspace_bytes() bytes: the
- *              expanded rows [B, max_seq_len, H, 256] bf16 (k_nope | v),
- *              owned by the caller and overwritten
- *   out        device bf16 [B, H, 128] (output)
- * Two launches (an expansion GEMM on 32x32x16 bf16 MFMAs, then attention).
- * batch must be at most 65535.
- */
-mla_status mla_naive_workspace_bytes(const mla_dims *dims, int32_t max_seq_len, size_t *bytes);
-mla_status mla_naive_decode(const mla_dims *dims, const mla_cache *cache, const void *q_nope, const void *q_pe,
-                            const void *w_uk, const void *w_uv, const int32_t *seq_lens, int32_t max_seq_len,
-                            void *workspace, size_t workspace_bytes, void *out, void *stream);
-
-/*
- * Cache append: writes num_new new tokens/*
  * Cache append: writes num_new new tokens of every sequence into the latent
  * cache.  Each input row is the token's fused down-projection output: 512
  * latent values, then the 64-wide decoupled RoPE key BEFORE rotation ([AUDIT]
@@ -363,7 +344,6 @@ mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const 
                             const int32_t *positions, int32_t num_new, float rope_base, void *stream);
 
 /*
- * Recommended num_splits for mla_decode_latent/*
  * Recommended num_splits for mla_decode_latent on a device with `num_cus`
  * compute units: enough workgroups to fill the chip, each split at least
  * max_seq_len / 32 tokens, kept within [32, 256] (measured on MI355X: with few

@@ -29,6 +29,32 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
 
 
+def _prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return re.findall(r"^(?:mla_status|int32_t|const char \*)\s*(mla_[a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def test_header_compiles_cleanly_as_c_and_cpp(tmp_path):
+    """The public header is valid C and C++ under -Wall -Wextra -Werror
+    (no stray comment openers, no duplicate or conflicting prototypes)."""
+    import shutil
+    import subprocess
+    for compiler, lang in (("gcc", "c"), ("g++", "c++")):
+        if shutil.which(compiler) is None:
+            pytest.skip(f"{compiler} not available")
+        src = tmp_path / f"use_header.{'c' if lang == 'c' else 'cpp'}"
+        src.write_text('#include "mla_absorb.h"\nint main(void) { return (int)MLA_OK; }\n')
+        res = subprocess.run([compiler, "-Wall", "-Wextra", "-Werror", "-Wcomment", "-I", os.path.dirname(HEADER),
+                              "-x", lang, "-fsyntax-only", str(src)], capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
+
+
+def test_each_prototype_declared_once():
+    protos = _prototypes()
+    assert len(protos) == len(set(protos)), sorted(p for p in protos if protos.count(p) > 1)
+    assert set(protos) == set(declared_functions())
+
+
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert len(names) >= 9
