@@ -178,11 +178,13 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  * fp8 query): the partials are bf16, since each split's o_i is a normalised
  * average with the relative rounding error of the bf16 o_lat, and there is
  * no query scale argument, since the queries stay bf16 for every cache dtype.
- * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): each tile of cached rows
- * is decoded (value = e4m3(code) * token_scale[slot], in fp32) and rounded to
- * bf16 before the same bf16 matrix products as a bf16 cache; the queries stay
- * bf16.  token_scale must then be non-NULL (4-byte aligned), else
- * MLA_ERR_NULL; a bf16 cache must pass token_scale = NULL (MLA_ERR_BUFFER).
+ * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): the codes enter the bf16
+ * matrix products exactly (every E4M3 value is a bf16 value) and the token
+ * scale in fp32: s_t = softmax_scale * token_scale[slot] * (q . code_t), and
+ * the probability multiplying code_t in P.V is p_t * token_scale[slot],
+ * rounded to bf16 as p_t alone is for a bf16 cache.  The queries stay bf16.
+ * token_scale must then be non-NULL (4-byte aligned), else MLA_ERR_NULL; a
+ * bf16 cache must pass token_scale = NULL (MLA_ERR_BUFFER).
  */
 mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
                              const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,

@@ -46,8 +46,11 @@ void decode_latent_kernel(DecodeArgs a) {
   constexpr int C = 512 / NW;             // latent columns owned by a wave
   static_assert(kTile % NW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
   // E4M3 tiles (FP8): the raw tile (latent rows, RoPE rows, per-token scales)
-  // streams into a ring of raw buffers and is expanded once per tile into a
-  // single bf16 tile in the layout the bf16 path reads.  Copies per wave and
+  // streams into a ring of raw buffers and its codes are widened once per
+  // tile into a single bf16 tile in the layout the bf16 path reads (exact:
+  // every E4M3 value is a bf16 value).  The token scale s_t enters in fp32:
+  // score = s_t (q . code_t), and P.V multiplies code_t by p_t s_t, rounded
+  // to bf16 as p_t alone would be.  Copies per wave and
   // tile: KV8 latent copies (2 rows each) plus E8 extras (RoPE halves, the
   // scales, or a dummy copy so that every wave issues the same number).
   constexpr int KV8 = 16 / NW;
@@ -219,9 +222,8 @@ void decode_latent_kernel(DecodeArgs a) {
   };
 
   // Expand raw tile `buf` into the bf16 tile: 32 rows x 72 chunks of 8
-  // elements (64 latent + 8 RoPE), each value decoded (OCP E4M3) and
-  // multiplied by its token's scale, then rounded to bf16 into the swizzled
-  // bf16 layout.
+  // elements (64 latent + 8 RoPE), each code decoded (OCP E4M3) to bf16 into
+  // the swizzled bf16 layout.
   auto expand_tile = [&](int buf) {
     const uint32_t raw = lds0 + buf * kRawTileBytes;
     const uint32_t bt = lds0 + kBf16Off;
@@ -240,12 +242,11 @@ void decode_latent_kernel(DecodeArgs a) {
           dst = bt + kPeRegion + r * kPeRow + (((c - 64u) ^ pe_swizzle(r)) << 4);
         }
         const u32x2 v = lds_read_u32x2(src);
-        const float sc = lds_read_f32(raw + kRawScaleOff + r * 4u);
         u32x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
-          out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
+          out[e] = pack_bf16x2(f[0], f[1]);
         }
         lds_write_u32x4(dst, out);
       }
@@ -395,6 +396,18 @@ void decode_latent_kernel(DecodeArgs a) {
 #pragma unroll
     for (int cb = 0; cb < kVPre; ++cb) va[cb] = va_load(cb);
 
+    // E4M3: q . code_t -> q . k_t with the scales of this lane's tokens
+    // 4 g4 + j and 16 + 4 g4 + j (raw tile `buf` holds tile it until the next
+    // iteration refills it)
+    f32x4 tsA = {}, tsB = {};
+    if constexpr (FP8) {
+      const uint32_t sr = lds0 + buf * kRawTileBytes + kRawScaleOff + (uint32_t)g4 * 16u;
+      tsA = lds_read_f32x4(sr);
+      tsB = lds_read_f32x4(sr + 64u);
+      s0 *= tsA;
+      s1 *= tsB;
+    }
+
     // ---- mask the ragged tail ----
     const int t0 = t_begin + it * kTile;
     const int nvalid = min(kTile, t_end - t0);
@@ -429,8 +442,15 @@ void decode_latent_kernel(DecodeArgs a) {
     l_sum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     // B operand of P.V for head 16 w + hl: element i <-> token
     // i<4 ? 4 g4 + i : 16 + 4 g4 + (i-4)
-    const u32x4 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    // E4M3: P.V multiplies the codes, so the probability carries the token scale
+    float pv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pv[j] = FP8 ? p[j] * tsA[j] : p[j];
+      pv[4 + j] = FP8 ? p[4 + j] * tsB[j] : p[4 + j];
+    }
+    const u32x4 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                      pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
     lds_write_u32x4(lds0 + kPOff + w * 1024 + lane * 16, pk);
     if (g4 == 0) lds_write_f32(lds0 + kAlphaOff + h * 4, alpha);
     if (lane == 0) lds_write_u8(lds0 + kFlagOff + w, any_grow ? 1u : 0u);

@@ -35,10 +35,13 @@
 //     2^kRescaleLog2 in the exp2 domain, so O is rarely rescaled.
 //   - E4M3 cache (FP8): each wave copies the raw codes, RoPE codes and
 //     per-token scales of its own 8 rows of a tile into a ring of 2 raw
-//     tiles, and decodes them (code times scale in fp32, rounded to bf16)
-//     into a ring of 3 bf16 tiles and 2 RoPE buffers, in chunks spread over
-//     the P.V MFMAs of the iteration two tiles earlier; the matrix products
-//     are then those of a bf16 cache.
+//     tiles, and widens the codes to bf16 (exact: every E4M3 value is a bf16
+//     value) into a ring of 3 bf16 tiles and 2 RoPE buffers, in chunks spread
+//     over the P.V MFMAs of the iteration two tiles earlier, with the rows'
+//     scales into a ring of 2 scale rows.  The token scale s_t then enters
+//     in fp32: score = s_t (q . code_t), and the probability that multiplies
+//     code_t in P.V is p_t s_t, rounded to bf16 as p_t alone would be.  So
+//     the E4M3 path rounds exactly where the bf16 path does.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -148,7 +151,8 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   constexpr int kPOff = kRawRing + NRAW * NW * kRawWave;
   constexpr int kAlphaOff = kPOff + 2 * kPBuf;  // [2][H] rescale factors, then 1/l
   constexpr int kFlagOff = kAlphaOff + 2 * H * 4;  // [2][8] byte per wave: its softmax rescaled
-  constexpr int kSmem = kFlagOff + 64;
+  constexpr int kScaleOff = kFlagOff + 64;         // E4M3: [2][32] fp32 token scales, ring by tile parity
+  constexpr int kSmem = kScaleOff + (FP8 ? 2 * kTile * 4 : 0);
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   // query staging (prologue only): per wave 16 latent rows (16 KiB) + 16
   // RoPE rows (2 KiB).  bf16: from latent buffer 2 on (latent buffers 2 .. 3
@@ -378,20 +382,28 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     return i < 8 ? x.src + (uint32_t)(i >> 1) * 1024u + (uint32_t)(i & 1) * 64u : x.src_pe;
   };
   auto x_dst = [&](const XAddr& x, int i) -> uint32_t { return i < 8 ? x.dst + (uint32_t)i * 1024u : x.dst_pe; };
-  auto x_dec = [&](u32x2 v, float sc) -> u32x4 {
+  // eight codes -> eight bf16 values (exact)
+  auto x_dec = [&](u32x2 v) -> u32x4 {
     u32x4 out;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
-      out[e] = pack_bf16x2(f[0] * sc, f[1] * sc);
+      out[e] = pack_bf16x2(f[0], f[1]);
     }
     return out;
   };
+  // scale row of a tile: the 32 token scales by tile parity (written by the
+  // wave that widens each row, read by every wave's softmax of that tile)
+  auto scale_row = [&](int tile) -> uint32_t { return lds0 + kScaleOff + (uint32_t)(tile & 1) * (kTile * 4); };
+  auto x_scale = [&](int tile, float sc) {
+    const uint32_t ln = lane_id();
+    if ((ln & 7u) == 0) lds_write_f32(scale_row(tile) + (8u * (uint32_t)w + (ln >> 3)) * 4u, sc);
+  };
   auto expand = [&](int tile) {
     const XAddr x = x_addr(tile);
-    const float sc = lds_read_f32(x.sc);
+    x_scale(tile, lds_read_f32(x.sc));
 #pragma unroll
-    for (int i = 0; i < 9; ++i) lds_write_u32x4(x_dst(x, i), x_dec(lds_read_u32x2(x_src(x, i)), sc));
+    for (int i = 0; i < 9; ++i) lds_write_u32x4(x_dst(x, i), x_dec(lds_read_u32x2(x_src(x, i))));
   };
   auto issue_tile = [&](int tile) {
     const TileSrc ts = tile_src(tile);
@@ -578,6 +590,15 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
     // one byte per wave; read now, tested after the deferred MFMAs
     const uint32_t flags = DO_PV ? lds_read_u32(lds0 + kFlagOff + pb * 8) : 0u;
+    // E4M3: scales of this lane's tokens 16 th + 4 q4 + j of tile tq, read
+    // from LDS where they are used (kept in registers they would spill)
+    auto tok_scale = [&](int th) -> f32x4 {
+      return lds_read_f32x4(scale_row(tq) + (uint32_t)(lane_id() >> 4) * 16u + (uint32_t)th * 64u);
+    };
+    // The E4M3 variant holds more state across the softmax (decode addresses
+    // and codes), so it recomputes the lane's indices where they are used.
+    auto lane_h16 = [&]() -> int { return FP8 ? (int)(lane_id() & 15u) : h16; };
+    auto lane_q4 = [&]() -> int { return FP8 ? (int)(lane_id() >> 4) : q4; };
     const uint32_t kbe = lat_buf(tq) + kb_lane;
     const uint32_t kbo = kbe ^ 64u;
     const uint32_t pb0 = pe_buf(tq) + pb_lane;
@@ -675,6 +696,17 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         drain_v(sp[0][1], false);
         drain_v(sp[1][0], false);
         drain_v(sp[1][1], false);
+        if constexpr (FP8) {
+          // q . code_t -> q . k_t (token scale in fp32)
+#pragma unroll
+          for (int th = 0; th < 2; ++th) {
+            const f32x4 ts = tok_scale(th);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) sp[th][hh][j] *= ts[j];
+          }
+        }
         // ragged tail (and, in a query group, tokens past each half's own
         // query): tokens 16 th + 4 q4 + j at or past the half's count
         if (min(nvalid_h[0], nvalid_h[1]) < kTile) {
@@ -684,7 +716,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (16 * th + 4 * q4 + j >= nvalid_h[hh]) sp[th][hh][j] = -INFINITY;
+                if (16 * th + 4 * lane_q4() + j >= nvalid_h[hh]) sp[th][hh][j] = -INFINITY;
         }
       } else if (c == 1 || c == 2) {
         const int hh = c - 1;
@@ -722,12 +754,18 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         // tokens 16 th + 8 g' + i; this lane's 4 tokens 16 th + 4 q4 + j are
         // elements 4 (q4 % 2) + j of lane (16 hh + h16) + 32 (q4 / 2)
         const int th = c - 22;
+        f32x4 ts = {};
+        if constexpr (FP8) ts = tok_scale(th);
         const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u + (uint32_t)th * 1024u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const u32x2 pk = {pack_bf16x2(sp[th][hh][0], sp[th][hh][1]), pack_bf16x2(sp[th][hh][2], sp[th][hh][3])};
-          const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
-          lds_write_b64(pw + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
+          // E4M3: P.V multiplies the codes, so the probability carries the token scale
+          f32x4 pv = {sp[th][hh][0], sp[th][hh][1], sp[th][hh][2], sp[th][hh][3]};
+          if constexpr (FP8) pv *= ts;
+          const u32x2 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          const int lq4 = lane_q4();
+          const uint32_t dl = (uint32_t)(16 * hh + lane_h16() + 32 * (lq4 >> 1));
+          lds_write_b64(pw + dl * 16u + (uint32_t)(lq4 & 1) * 8u, pk);
         }
       } else if (c == 24 || c == 25) {
         const int hh = c - 24;
@@ -736,10 +774,11 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         const float nl = fmaf(l_sum[hh], alpha[hh], psum);
         if (commit) l_sum[hh] = nl;
       } else if (c == 26) {
-        if (q4 == 0) {
+        if (lane_q4() == 0) {
           const uint32_t ab = lds0 + kAlphaOff + (uint32_t)ps * (H * 4);
-          lds_write_f32(ab + (32 * w + h16) * 4, alpha[0]);
-          lds_write_f32(ab + (32 * w + 16 + h16) * 4, alpha[1]);
+          const int lh = lane_h16();
+          lds_write_f32(ab + (32 * w + lh) * 4, alpha[0]);
+          lds_write_f32(ab + (32 * w + 16 + lh) * 4, alpha[1]);
         }
         if (lane == 0) lds_write_u8(lds0 + kFlagOff + ps * 8 + w, any_grow ? 1u : 0u);
       }
@@ -768,12 +807,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
             xa = x_addr(tx);
             xsc = lds_read_f32(xa.sc);
             xr[0] = lds_read_u32x2(x_src(xa, 0));
+            x_scale(tx, xsc);
           }
           if (m % 3 == 1 && m / 3 < 9) {
             const int i = m / 3;
             const u32x2 cur = xr[i & 1];
             if (i + 1 < 9) xr[(i + 1) & 1] = lds_read_u32x2(x_src(xa, i + 1));
-            lds_write_u32x4(x_dst(xa, i), x_dec(cur, xsc));
+            lds_write_u32x4(x_dst(xa, i), x_dec(cur));
           }
         }
       }

@@ -282,3 +282,72 @@ def random_projection_rows(batch, num_new, seed, device="cpu", width=D_K):
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     return _normal(gen, (batch, num_new, width), 1.0, dev).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------
+# Dominant ("sink" / outlier) tokens.  Real attention often has a few cached
+# tokens whose scores stand far above the rest for every head; an online
+# softmax that meets one late must move its running max and rescale what it
+# has accumulated.  These draws plant such tokens: the RoPE query of every head
+# shares one unit direction u, and a planted token's RoPE key points along u
+# with a chosen length, so its score rises by a chosen amount for every head.
+# ---------------------------------------------------------------------------
+
+def sink_direction(seed, device="cpu"):
+    """A unit vector u in the 64-wide RoPE space (float32)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    u = _normal(gen, (D_R,), 1.0, dev)
+    return u / u.norm()
+
+
+def aligned_rope_queries(shape, u, seed, device="cpu"):
+    """RoPE queries [*shape, 64] bfloat16 of the form r u + n: weight
+    r ~ U[0.5, 1.5] along the shared direction u, plus n ~ N(0, 1) with its
+    component along u removed.  A planted token whose key has length g along u
+    adds about r * g * scale to this query's score."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    u = u.to(device=dev, dtype=torch.float32)
+    r = torch.rand(tuple(shape) + (1,), generator=gen, device=dev) + 0.5
+    n = _normal(gen, tuple(shape) + (D_R,), 1.0, dev)
+    n = n - (n @ u).unsqueeze(-1) * u
+    return (r * u + n).to(torch.bfloat16)
+
+
+def plant_sink_tokens(x, sinks, u, seed):
+    """Overwrite cached tokens of DecodeInputs x with dominant tokens, in place.
+
+    sinks: iterable of (b, t, jump): sequence b, position t, and jump in
+    natural-log units.  Token (b, t) gets a fresh row: 512 latent values and a
+    64-wide RoPE key ~ N(0, 1), then the key's component along u is set to
+    jump / x.scale, so for a query r u + n (aligned_rope_queries) its score
+    gains about r * jump.  The row is stored like every other row of x (bf16,
+    or E4M3 codes with a fresh per-token scale) at the slot of (b, t) in x's
+    layout (contiguous slot b * seq_stride + t, or through the block table).
+    """
+    dev = x.kv_rows.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    u = u.to(device=dev, dtype=torch.float32)
+    fp8 = x.workload.dtype == "fp8_e4m3"
+    for b, t, jump in sinks:
+        if x.block_table is not None:
+            slot = int(x.block_table[b, t // x.block_size].item()) * x.block_size + t % x.block_size
+        else:
+            slot = b * x.seq_stride + t
+        row = _normal(gen, (1, D_K), 1.0, dev)
+        k = row[0, D_C:]
+        k -= (k @ u) * u
+        k += (float(jump) / x.scale) * u
+        if fp8:
+            codes, sc = _to_e4m3(row)
+            x.kv_rows[slot] = codes[0, :D_C]
+            x.pe_rows[slot] = codes[0, D_C:]
+            x.token_scale[slot] = sc[0]
+        else:
+            vals = row.to(torch.bfloat16)
+            x.kv_rows[slot] = vals[0, :D_C]
+            x.pe_rows[slot] = vals[0, D_C:]

@@ -57,3 +57,59 @@ def sample_batch(B, k=4):
     if B <= k:
         return list(range(B))
     return sorted(set([0, B - 1] + list(np.linspace(0, B - 1, k).round().astype(int))))
+
+
+# ---------------------------------------------------------------------------
+# Guarded outputs: every output buffer handed to the library sits between two
+# guard regions, and the buffer and the guards start filled with a 16-bit
+# pattern that is a NaN both as bf16 (0xFFC1) and as fp32 (0xFFC1FFC1).  After
+# the call, the guards must still hold the pattern (nothing was written outside
+# the output), and an output element the kernels failed to write stays NaN,
+# which fails every comparison.
+# ---------------------------------------------------------------------------
+GUARD_BYTES = 64 * 1024
+_PATTERN16 = -63  # int16 view of 0xFFC1
+
+
+class Guarded:
+    def __init__(self, shape, dtype, device):
+        elem = torch.empty((), dtype=dtype).element_size()
+        self.nbytes = int(np.prod(shape)) * elem
+        total = GUARD_BYTES + self.nbytes + GUARD_BYTES
+        self.buf = torch.full((total // 2,), _PATTERN16, dtype=torch.int16, device=device)
+        raw = self.buf.view(torch.uint8)
+        self.tensor = raw[GUARD_BYTES:GUARD_BYTES + self.nbytes].view(dtype).view(shape)
+        self.shape = tuple(shape)
+
+    def guards_intact(self):
+        raw = self.buf.view(torch.uint8)
+        head = raw[:GUARD_BYTES].view(torch.int16)
+        tail = raw[GUARD_BYTES + self.nbytes:].view(torch.int16)
+        return bool((head == _PATTERN16).all().item()) and bool((tail == _PATTERN16).all().item())
+
+
+def guarded(device, *specs):
+    """Guarded buffers for (shape, dtype) specs; returns the list of Guarded."""
+    return [Guarded(shape, dtype, device) for shape, dtype in specs]
+
+
+def assert_guards(*gs):
+    for i, g in enumerate(gs):
+        assert g.guards_intact(), f"write outside output {i} of shape {g.shape}"
+
+
+def oracle_prefill_rows(x, q_lat, q_pe, q_start, max_len, rows):
+    """Oracle o_lat / lse of prefill query rows (b, i): latent attention of
+    query i of sequence b over its causal prefix, tokens 0 .. q_start[b] + i
+    (clamped to max_len)."""
+    args = cache_args(x)
+    ql, qp = f64(q_lat), f64(q_pe)
+    os_, ls_ = [], []
+    for b, i in rows:
+        T = min(int(q_start[b]) + i + 1, max_len)
+        slots = oracle.token_slots(b, T, args["seq_stride"], args["block_table"], args["block_size"])
+        c, k_r = oracle.load_rows(args["kv_codes"], args["pe_codes"], slots, args["dtype"], args["token_scale"])
+        o, l = oracle.latent_attention(ql[b, i], qp[b, i], c, k_r, x.scale)
+        os_.append(o)
+        ls_.append(l)
+    return np.stack(os_), np.stack(ls_)

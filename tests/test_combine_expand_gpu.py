@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import TOL_BF16, f64, rel_err
+from tests.gpu_helpers import TOL_BF16, assert_guards, f64, guarded, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -36,11 +36,13 @@ def test_combine_expand_matches_two_calls_and_oracle(B, P, H):
     d = binding.dims(B, H, 0.07)
     o_ref, l_ref = binding.mla_combine_splits(d, o_part, lse_part)
     out_ref = binding.mla_expand_v(d, o_ref, w_uv)
-    o_lat = torch.full_like(o_ref, 7.0)
-    lse = torch.full_like(l_ref, 7.0)
-    out = binding.mla_combine_expand_v(d, o_part, lse_part, w_uv, o_lat=o_lat, lse=lse)
-    out_nolat = binding.mla_combine_expand_v(d, o_part, lse_part, w_uv)
+    gout, go, gl, gout2 = guarded(DEV, ((B, H, 128), torch.bfloat16), ((B, H, 512), torch.bfloat16),
+                                  ((B, H), torch.float32), ((B, H, 128), torch.bfloat16))
+    o_lat, lse = go.tensor, gl.tensor
+    out = binding.mla_combine_expand_v(d, o_part, lse_part, w_uv, out=gout.tensor, o_lat=o_lat, lse=lse)
+    out_nolat = binding.mla_combine_expand_v(d, o_part, lse_part, w_uv, out=gout2.tensor)
     torch.cuda.synchronize()
+    assert_guards(gout, go, gl, gout2)
     assert torch.equal(out, out_ref) and torch.equal(out_nolat, out_ref)
     assert torch.equal(o_lat, o_ref)
     assert torch.equal(lse, l_ref)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import TOL_BF16, TOL_FP8, cache_args, f64, rel_err
+from tests.gpu_helpers import TOL_BF16, TOL_FP8, assert_guards, cache_args, f64, guarded, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,13 @@ def _run(x, check_all=True):
     d = binding.dims(x.batch, x.heads, x.scale)
     cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
                                block_size=x.block_size, token_scale=x.token_scale)
+    B, H = x.batch, x.heads
+    gout, go, gl = guarded(DEV, ((B, H, 128), torch.bfloat16), ((B, H, 512), torch.bfloat16), ((B, H), torch.float32))
     out, o_lat, lse = binding.mla_decode_step_fused(d, cache, x.q_nope, x.q_pe, x.w_uk, x.w_uv, x.seq_lens,
-                                                    x.max_seq_len, want_latent=True)
+                                                    x.max_seq_len, out=gout.tensor, o_lat=go.tensor, lse=gl.tensor,
+                                                    want_latent=True)
     torch.cuda.synchronize()
+    assert_guards(gout, go, gl)
     ref = oracle.absorbed_decode(f64(x.q_nope), f64(x.q_pe), f64(x.w_uk), f64(x.w_uv),
                                  seq_lens=x.seq_lens.cpu().numpy(), scale=x.scale, **cache_args(x))
     tol = TOL_FP8 if x.workload.dtype == "fp8_e4m3" else TOL_BF16

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import TOL_BF16, TOL_FP8, bits16, cache_args, f64, rel_err
+from tests.gpu_helpers import TOL_BF16, TOL_FP8, assert_guards, bits16, cache_args, f64, guarded, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -67,13 +67,20 @@ def test_prefill_against_oracle(workload, B, S, H, L, starts, P):
     max_len = x.max_seq_len
     cache = _cache(x)
     if P == 1:
-        o_lat, lse = binding.mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_len)
+        go, gl = guarded(DEV, ((B, L, H, 512), torch.bfloat16), ((B, L, H), torch.float32))
+        o_lat, lse = binding.mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_len, o_lat=go.tensor,
+                                                lse=gl.tensor)
+        gs = (go, gl)
     else:
-        o_part, lse_part = binding.mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_len, num_splits=P)
+        gp, glp = guarded(DEV, ((B * L, P, H, 512), torch.bfloat16), ((B * L, P, H), torch.float32))
+        o_part, lse_part = binding.mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_len, num_splits=P,
+                                                      o_part=gp.tensor, lse_part=glp.tensor)
         dr = binding.dims(B * L, H, x.scale)
         o_lat, lse = binding.mla_combine_splits(dr, o_part, lse_part)
         o_lat, lse = o_lat.view(B, L, H, 512), lse.view(B, L, H)
+        gs = (gp, glp)
     torch.cuda.synchronize()
+    assert_guards(*gs)
     rows = [(b, i) for b in range(B) for i in range(L)]
     ro, rl = _oracle_rows(x, q_lat, q_pe, starts, max_len, rows)
     got_o = f64(o_lat).reshape(B * L, H, 512)
