@@ -192,6 +192,24 @@ mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const
                              float *lse, void *stream);
 
 /*
+ * mla_decode_latent followed by mla_combine_splits, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split partials live in a device
+ * array of the library (48 MiB per GPU, held until the process ends), so the
+ * call allocates nothing; the caller passes inputs and outputs only.
+ *   arguments as mla_decode_latent; o_lat device bf16 [B, H, 512] and lse
+ *   device fp32 [B, H] are always written (num_splits == 1: directly).
+ * Errors: MLA_ERR_BUFFER when batch * num_splits * num_heads partial rows
+ * (1,024 + 4 bytes each) exceed the array; MLA_ERR_HIP if its device address
+ * cannot be obtained.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap on one GPU (other streams, other threads) race; serialise them.
+ * Results equal mla_decode_latent + mla_combine_splits bit for bit.
+ */
+mla_status mla_decode_latent_noalloc(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
+                                     const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,
+                                     int32_t num_splits, void *o_lat, float *lse, void *stream);
+
+/*
  * Absorbed chunked prefill ([MLA80] §2 cache test and §5: prefill, then
  * decode against the cache; [AUDIT] §2.2-§2.4: absorbed scores and latent
  * aggregation; [G5SPEC] use case 2: prefill is compute-bound): num_q query

@@ -24,7 +24,7 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
             "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused", "mla_naive_workspace_bytes",
-            "mla_naive_decode", "mla_prefill_latent", "mla_combine_expand_v"]
+            "mla_naive_decode", "mla_prefill_latent", "mla_combine_expand_v", "mla_decode_latent_noalloc"]
 
 
 class MlaError(RuntimeError):
@@ -82,6 +82,9 @@ def load():
     lib.mla_decode_latent.restype = st
     lib.mla_decode_latent.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, ctypes.c_int32,
                                       P, P, P, P, P]
+    lib.mla_decode_latent_noalloc.restype = st
+    lib.mla_decode_latent_noalloc.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                              P, P, P]
     lib.mla_combine_splits.restype = st
     lib.mla_combine_splits.argtypes = [D, P, P, ctypes.c_int32, P, P, P]
     lib.mla_combine_expand_v.restype = st
@@ -239,6 +242,23 @@ def mla_decode_latent(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_splits=1
                                     _ptr(o_lat) if num_splits == 1 else None,
                                     _ptr(lse) if num_splits == 1 else None, _stream(stream)))
     return (o_lat, lse) if num_splits == 1 else (o_part, lse_part)
+
+
+def mla_decode_latent_noalloc(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_splits, o_lat, lse, stream=None):
+    """Split-KV latent attention and merge with the partials in the library's
+    device scratch: writes o_lat [B, H, 512] bf16 and lse [B, H] fp32, which
+    the caller provides (nothing is allocated here or in the library)."""
+    B, H = d.batch, d.num_heads
+    dev = q_lat.device
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, d.kv_lora_rank))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_decode_latent_noalloc(ctypes.byref(d), ctypes.byref(cache), _ptr(q_lat), _ptr(q_pe),
+                                            _ptr(seq_lens), int(max_seq_len), int(num_splits), _ptr(o_lat), _ptr(lse),
+                                            _stream(stream)))
+    return o_lat, lse
 
 
 def mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_seq_len, num_splits=1, o_part=None, lse_part=None,

@@ -133,6 +133,11 @@ struct NaiveArgs {
   uint16_t* out;              // [B, H, 128] bf16
 };
 
+// Device scratch of mla_decode_latent_noalloc (split partials), per GPU.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+// Device address of this GPU's scratch array (looked up once per device).
+hipError_t scratch_region(void** ptr);
+
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
 // 128 heads, bf16 cache: 32-head waves with P.V woven into the next tile's scores.
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);

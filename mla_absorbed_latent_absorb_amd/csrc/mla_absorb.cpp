@@ -304,6 +304,41 @@ mla_status mla_decode_latent(const mla_dims* dims, const mla_cache* cache, const
                                lse_part, o_lat, lse, stream);
 }
 
+mla_status mla_decode_latent_noalloc(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
+                                     const int32_t* seq_lens, int32_t max_seq_len, int32_t num_splits, void* o_lat,
+                                     float* lse, void* stream) {
+  const char* where = "mla_decode_latent_noalloc";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1) return fail(MLA_ERR_BAD_LENGTH, "num_splits %d < 1 (%s)", num_splits, where);
+  REQUIRE_PTR(o_lat, "o_lat", where);
+  if (lse == nullptr) return fail(MLA_ERR_NULL, "lse is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  if (num_splits == 1)  // no partials: straight to o_lat / lse
+    return latent_attention_rows(where, dims, cache, q_lat, q_pe, seq_lens, nullptr, 1, max_seq_len, 1, nullptr,
+                                 nullptr, o_lat, lse, stream);
+  // partials [B, P, H, 512] bf16, then lse [B, P, H] fp32 (256-byte aligned)
+  const size_t rows = (size_t)dims->batch * (size_t)num_splits * (size_t)dims->num_heads;
+  const size_t part_bytes = ((rows * dims->kv_lora_rank * 2 + 255) / 256) * 256;
+  const size_t need = part_bytes + rows * 4;
+  if (need > mla::kScratchBytes)
+    return fail(MLA_ERR_BUFFER,
+                "batch * num_splits * num_heads = %zu needs %zu bytes of split partials, above the %zu-byte "
+                "device scratch of %s (use fewer splits, or mla_decode_latent with caller buffers)",
+                rows, need, mla::kScratchBytes, where);
+  void* base = nullptr;
+  const hipError_t e = mla::scratch_region(&base);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "device scratch lookup failed: %s (%s)", hipGetErrorString(e), where);
+  void* o_part = base;
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(base) + part_bytes);
+  st = latent_attention_rows(where, dims, cache, q_lat, q_pe, seq_lens, nullptr, 1, max_seq_len, num_splits, o_part,
+                             lse_part, nullptr, nullptr, stream);
+  if (st != MLA_OK) return st;
+  mla::CombineArgs c{static_cast<const uint16_t*>(o_part), lse_part, static_cast<uint16_t*>(o_lat), lse, dims->batch,
+                     dims->num_heads, num_splits};
+  return launch_result(mla::launch_combine(c, static_cast<hipStream_t>(stream)), where);
+}
+
 mla_status mla_prefill_latent(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
                               const int32_t* q_start, int32_t num_q, int32_t max_seq_len, int32_t num_splits,
                               void* o_part, float* lse_part, void* o_lat, float* lse, void* stream) {
