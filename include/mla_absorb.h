@@ -364,6 +364,71 @@ mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const 
                             const int32_t *positions, int32_t num_new, float rope_base, void *stream);
 
 /*
+ * Length-aware split plan for a decode step whose sequences have different
+ * lengths ("DeepSeek-V2-Lite 真实权重执行审计" §3.3 names a paged cache with
+ * per-sequence lengths as a production requirement; "G5 MLA KV 访存建模设计规格"
+ * Appendix B reads the cache concurrently in parts whose results are then
+ * combined).  Host-only; launches nothing.
+ *
+ * The uniform rule of mla_decode_latent cuts every sequence at multiples of
+ * ceil(max_seq_len / P), so the launch lasts as long as the longest chunk
+ * while short sequences leave workgroups idle.  This plan instead cuts each
+ * sequence into near-equal runs of whole 32-token tiles, with the fewest
+ * tiles per run such that all runs fit the device at once (num_cus times
+ * the resident workgroups per CU: 1 at 128 heads, 2 at 64, 4 at 16 or 32)
+ * and no run is shorter than max(32, min(256, max_seq_len / 32)) tokens.
+ * Every sequence gets at least one item (an empty sequence one item with no
+ * tiles); items of a sequence are consecutive.
+ *
+ *   host_seq_lens  HOST int32 [batch], clamped to [0, max_seq_len]
+ *   capacity       rows of `items` the caller provides (the plan never
+ *                  needs more than max(batch, num_cus * 4) rows)
+ *   items          HOST int32 [capacity, 3], written: (sequence, first tile,
+ *                  tile count) per work item; item i covers tokens
+ *                  [32 * first, min(32 * (first + count), seq_lens[seq]))
+ *   seq_first      HOST int32 [batch + 1], written: sequence b's items are
+ *                  seq_first[b] .. seq_first[b + 1] - 1 (the merge map)
+ *   num_items      written: number of items
+ * MLA_ERR_BUFFER if the plan needs more than `capacity` items.
+ */
+mla_status mla_plan_decode_splits(const mla_dims *dims, const int32_t *host_seq_lens, int32_t max_seq_len,
+                                  int32_t num_cus, int32_t capacity, int32_t *items, int32_t *seq_first,
+                                  int32_t *num_items);
+
+/*
+ * Latent attention (as mla_decode_latent) over the work items of a plan
+ * (mla_plan_decode_splits, copied to the device by the caller): one
+ * workgroup per item, whose partial (o_i, lse_i) over its token range goes to
+ * row i of the partial arrays.
+ *   items     device int32 [num_items, 3] (sequence, first 32-token tile,
+ *             tile count); an item naming a sequence outside [0, batch), a
+ *             negative or out-of-range first tile, or no tiles covers no
+ *             tokens (o = 0, lse = -inf); ranges end at seq_lens[seq]
+ *   o_part    device bf16 [num_items, H, 512], lse_part device fp32
+ *             [num_items, H] (outputs)
+ *   other arguments as mla_decode_latent.
+ */
+mla_status mla_decode_latent_planned(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
+                                     const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,
+                                     const int32_t *items, int32_t num_items, void *o_part, float *lse_part,
+                                     void *stream);
+
+/*
+ * The merges of mla_combine_splits / mla_combine_expand_v over planned
+ * partials: sequence b merges partial rows seq_first[b] .. seq_first[b+1]-1
+ * (in that order).  seq_first: device int32 [batch + 1]; a sequence whose
+ * range is empty or leaves [0, num_items) merges to o = 0, lse = -inf (and
+ * out = 0).  o_part [num_items, H, 512] bf16, lse_part [num_items, H] fp32;
+ * outputs as in mla_combine_splits / mla_combine_expand_v.
+ */
+mla_status mla_combine_splits_planned(const mla_dims *dims, const void *o_part, const float *lse_part,
+                                      const int32_t *seq_first, int32_t num_items, void *o_lat, float *lse,
+                                      void *stream);
+mla_status mla_combine_expand_v_planned(const mla_dims *dims, const void *o_part, const float *lse_part,
+                                        const int32_t *seq_first, int32_t num_items, const void *w_uv, void *out,
+                                        void *o_lat, float *lse, void *stream);
+
+/*
  * Recommended num_splits for mla_decode_latent on a device with `num_cus`
  * compute units: enough workgroups to fill the chip, each split at least
  * max_seq_len / 32 tokens, kept within [32, 256] (measured on MI355X: with few

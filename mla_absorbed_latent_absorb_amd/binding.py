@@ -24,7 +24,9 @@ _STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL", 2: "MLA_ERR_MISSING_DIM", 3: "MLA_ERR
 EXPORTED = ["mla_last_error", "mla_version", "mla_kv_cache_bytes", "mla_decode_kv_read_bytes",
             "mla_absorb_q", "mla_decode_latent", "mla_combine_splits", "mla_expand_v",
             "mla_recommended_splits", "mla_cache_append", "mla_decode_step_fused", "mla_naive_workspace_bytes",
-            "mla_naive_decode", "mla_prefill_latent", "mla_combine_expand_v", "mla_decode_latent_noalloc"]
+            "mla_naive_decode", "mla_prefill_latent", "mla_combine_expand_v", "mla_decode_latent_noalloc",
+            "mla_plan_decode_splits", "mla_decode_latent_planned", "mla_combine_splits_planned",
+            "mla_combine_expand_v_planned"]
 
 
 class MlaError(RuntimeError):
@@ -85,6 +87,15 @@ def load():
     lib.mla_decode_latent_noalloc.restype = st
     lib.mla_decode_latent_noalloc.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, ctypes.c_int32,
                                               P, P, P]
+    lib.mla_plan_decode_splits.restype = st
+    lib.mla_plan_decode_splits.argtypes = [D, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.mla_decode_latent_planned.restype = st
+    lib.mla_decode_latent_planned.argtypes = [D, ctypes.POINTER(MlaCache), P, P, P, ctypes.c_int32, P,
+                                              ctypes.c_int32, P, P, P]
+    lib.mla_combine_splits_planned.restype = st
+    lib.mla_combine_splits_planned.argtypes = [D, P, P, P, ctypes.c_int32, P, P, P]
+    lib.mla_combine_expand_v_planned.restype = st
+    lib.mla_combine_expand_v_planned.argtypes = [D, P, P, P, ctypes.c_int32, P, P, P, P, P]
     lib.mla_combine_splits.restype = st
     lib.mla_combine_splits.argtypes = [D, P, P, ctypes.c_int32, P, P, P]
     lib.mla_combine_expand_v.restype = st
@@ -259,6 +270,97 @@ def mla_decode_latent_noalloc(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_
                                             _ptr(seq_lens), int(max_seq_len), int(num_splits), _ptr(o_lat), _ptr(lse),
                                             _stream(stream)))
     return o_lat, lse
+
+
+class SplitPlan:
+    """A length-aware split plan (mla_plan_decode_splits) on the host and its
+    device copy: items [n, 3] and seq_first [B + 1] int32."""
+
+    def __init__(self, items, seq_first, device):
+        self.items_host, self.seq_first_host = items, seq_first
+        self.num_items = int(items.shape[0])
+        self.items = items.to(device)
+        self.seq_first = seq_first.to(device)
+
+
+def mla_plan_decode_splits(d, host_seq_lens, max_seq_len, num_cus, device=None):
+    """Plan on the host from host lengths; with `device`, also copy it there."""
+    B = d.batch
+    lens = torch.as_tensor([int(v) for v in host_seq_lens], dtype=torch.int32)
+    if lens.numel() != B:
+        raise ValueError(f"host_seq_lens must have {B} entries")
+    cap = max(B, 4 * int(num_cus))
+    items = torch.empty((cap, 3), dtype=torch.int32)
+    first = torch.empty((B + 1,), dtype=torch.int32)
+    n = ctypes.c_int32(0)
+    _check(load().mla_plan_decode_splits(ctypes.byref(d), ctypes.c_void_p(lens.data_ptr()), int(max_seq_len),
+                                         int(num_cus), cap, ctypes.c_void_p(items.data_ptr()),
+                                         ctypes.c_void_p(first.data_ptr()), ctypes.byref(n)))
+    items = items[:n.value].clone()
+    if device is None:
+        return items, first
+    return SplitPlan(items, first, device)
+
+
+def mla_decode_latent_planned(d, cache, q_lat, q_pe, seq_lens, max_seq_len, plan, o_part=None, lse_part=None,
+                              stream=None):
+    """Latent attention over the items of a SplitPlan -> partials
+    (o_part [n, H, 512] bf16, lse_part [n, H] fp32)."""
+    B, H, n = d.batch, d.num_heads, plan.num_items
+    dev = q_lat.device
+    _expect(q_lat, "q_lat", torch.bfloat16, (B, H, d.kv_lora_rank))
+    _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
+    _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _expect(plan.items, "plan.items", torch.int32, (n, 3), dev)
+    if o_part is None:
+        o_part = torch.empty((n, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((n, H), dtype=torch.float32, device=dev)
+    _expect(o_part, "o_part", torch.bfloat16, (n, H, d.kv_lora_rank), dev)
+    _expect(lse_part, "lse_part", torch.float32, (n, H), dev)
+    _check(load().mla_decode_latent_planned(ctypes.byref(d), ctypes.byref(cache), _ptr(q_lat), _ptr(q_pe),
+                                            _ptr(seq_lens), int(max_seq_len), _ptr(plan.items), n, _ptr(o_part),
+                                            _ptr(lse_part), _stream(stream)))
+    return o_part, lse_part
+
+
+def mla_combine_splits_planned(d, o_part, lse_part, plan, o_lat=None, lse=None, stream=None):
+    """Merge planned partials per sequence -> (o_lat bf16, lse fp32)."""
+    B, H, n = d.batch, d.num_heads, plan.num_items
+    dev = o_part.device
+    _expect(o_part, "o_part", torch.bfloat16, (n, H, d.kv_lora_rank))
+    _expect(lse_part, "lse_part", torch.float32, (n, H), dev)
+    _expect(plan.seq_first, "plan.seq_first", torch.int32, (B + 1,), dev)
+    if o_lat is None:
+        o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_combine_splits_planned(ctypes.byref(d), _ptr(o_part), _ptr(lse_part), _ptr(plan.seq_first), n,
+                                             _ptr(o_lat), _ptr(lse), _stream(stream)))
+    return o_lat, lse
+
+
+def mla_combine_expand_v_planned(d, o_part, lse_part, plan, w_uv, out=None, o_lat=None, lse=None, stream=None):
+    """Planned merge + value absorption in one launch -> out (bf16 [B, H, 128])."""
+    B, H, n = d.batch, d.num_heads, plan.num_items
+    dev = o_part.device
+    _expect(o_part, "o_part", torch.bfloat16, (n, H, d.kv_lora_rank))
+    _expect(lse_part, "lse_part", torch.float32, (n, H), dev)
+    _expect(plan.seq_first, "plan.seq_first", torch.int32, (B + 1,), dev)
+    _expect(w_uv, "w_uv", torch.bfloat16, (H, d.v_head_dim, d.kv_lora_rank), dev)
+    if out is None:
+        out = torch.empty((B, H, d.v_head_dim), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", torch.bfloat16, (B, H, d.v_head_dim), dev)
+    if o_lat is not None:
+        _expect(o_lat, "o_lat", torch.bfloat16, (B, H, d.kv_lora_rank), dev)
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (B, H), dev)
+    _check(load().mla_combine_expand_v_planned(ctypes.byref(d), _ptr(o_part), _ptr(lse_part), _ptr(plan.seq_first),
+                                               n, _ptr(w_uv), _ptr(out), _ptr(o_lat) if o_lat is not None else None,
+                                               _ptr(lse) if lse is not None else None, _stream(stream)))
+    return out
 
 
 def mla_prefill_latent(d, cache, q_lat, q_pe, q_start, max_seq_len, num_splits=1, o_part=None, lse_part=None,

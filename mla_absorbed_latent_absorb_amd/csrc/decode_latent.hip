@@ -78,8 +78,12 @@ void decode_latent_kernel(DecodeArgs a) {
   const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   // query row: its queries and outputs.  Prefill rows run last query first:
   // the longest causal prefixes start earliest, so the launch ends balanced.
-  const int qrow = item / a.num_splits;
-  const int split = item - qrow * a.num_splits;
+  // A planned decode reads its sequence and token range from the plan and
+  // writes the partial of its item.
+  const bool planned = a.items != nullptr;
+  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len) : PlanItem{0, 0, 0};
+  const int qrow = planned ? pl.seq : item / a.num_splits;
+  const int split = planned ? item : item - qrow * a.num_splits;
   const int b = a.q_start == nullptr ? qrow : a.batch - 1 - qrow;
   const int cb = b / a.q_per_seq;      // the sequence whose cached rows it reads
   const int h = w * 16 + hl;  // head whose scores this lane computes
@@ -87,9 +91,10 @@ void decode_latent_kernel(DecodeArgs a) {
   // decode: the sequence's length; prefill: causal, tokens up to the query's own position
   int T = a.q_start == nullptr ? a.seq_lens[b] : max(a.q_start[cb], 0) + (b - cb * a.q_per_seq) + 1;
   T = T < 0 ? 0 : (T > a.max_seq_len ? a.max_seq_len : T);
-  const int t_begin = split * a.chunk;
-  const int t_end = min(T, t_begin + a.chunk);
-  const bool final_out = a.num_splits == 1;
+  const int t_begin = planned ? pl.t_begin : split * a.chunk;
+  const int t_end = min(T, planned ? pl.t_end : t_begin + a.chunk);
+  const bool final_out = !planned && a.num_splits == 1;
+  const size_t part = planned ? (size_t)item : (size_t)b * a.num_splits + split;  // partial slot
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const int col0 = w * C;     // first latent column of this wave's P.V share
 
@@ -98,12 +103,12 @@ void decode_latent_kernel(DecodeArgs a) {
     for (int r = 0; r < 16; ++r) {
       const size_t row = (size_t)(w * 16 + r);
       uint16_t* dst = final_out ? a.o_lat + ((size_t)b * a.num_heads + row) * kDc
-                                : a.o_part + (((size_t)b * a.num_splits + split) * a.num_heads + row) * kDc;
+                                : a.o_part + (part * a.num_heads + row) * kDc;
       *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
     }
     if (g4 == 0) {
       if (final_out) a.lse[(size_t)b * a.num_heads + h] = -INFINITY;
-      else a.lse_part[((size_t)b * a.num_splits + split) * a.num_heads + h] = -INFINITY;
+      else a.lse_part[part * a.num_heads + h] = -INFINITY;
     }
     return;
   }
@@ -507,7 +512,7 @@ void decode_latent_kernel(DecodeArgs a) {
   if (g4 == 0) {
     lds_write_f32(lds0 + kAlphaOff + h * 4, 1.0f / l_tot);
     if (final_out) a.lse[(size_t)b * a.num_heads + h] = lse_val;
-    else a.lse_part[((size_t)b * a.num_splits + split) * a.num_heads + h] = lse_val;
+    else a.lse_part[part * a.num_heads + h] = lse_val;
   }
   barrier();
   float inv[NW];
@@ -519,7 +524,7 @@ void decode_latent_kernel(DecodeArgs a) {
   // XOR-swizzled by row, and store whole row segments of C columns: to o_lat
   // (one split) or to the split's bf16 partial rows.
   uint16_t* const out_rows = final_out ? a.o_lat + (size_t)b * a.num_heads * kDc
-                                       : a.o_part + ((size_t)b * a.num_splits + split) * a.num_heads * kDc;
+                                       : a.o_part + part * a.num_heads * kDc;
   const uint32_t stage = lds0 + (uint32_t)w * (uint32_t)(C * 32);
   constexpr int RC = C / 8;                  // 16-byte chunks per bf16 row
   constexpr uint32_t SWZ = RC >= 16 ? 15u : (uint32_t)(RC - 1);
@@ -556,7 +561,7 @@ static hipError_t launch_nw(const DecodeArgs& a, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = a.batch * a.num_splits;
+  const int grid = a.items != nullptr ? a.num_items : a.batch * a.num_splits;
   if (a.fp8) {
     switch (a.num_heads) {
       case 16: return launch_nw<1, 4, true>(a, grid, stream);

@@ -182,8 +182,12 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   // query row: its queries and outputs.  Prefill rows run last query first:
   // the longest causal prefixes start earliest, so the launch ends balanced.
-  const int qrow = item / a.num_splits;
-  const int split = item - qrow * a.num_splits;
+  // A planned decode reads its sequence and token range from the plan and
+  // writes the partial of its item.
+  const bool planned = a.items != nullptr;
+  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len) : PlanItem{0, 0, 0};
+  const int qrow = planned ? pl.seq : item / a.num_splits;
+  const int split = planned ? item : item - qrow * a.num_splits;
   // Workgroup rows: decode, one sequence (128 heads); prefill, one query (128
   // heads), or with fewer heads a group of QG = 128 / H consecutive queries of
   // one sequence (row r = query r / H, head r % H; one split).
@@ -205,8 +209,8 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     return t < 0 ? 0 : (t > a.max_seq_len ? a.max_seq_len : t);
   };
   const int T = length_of(i0 + nq - 1);
-  const int t_begin = split * a.chunk;
-  const int t_end = min(T, t_begin + a.chunk);
+  const int t_begin = planned ? pl.t_begin : split * a.chunk;
+  const int t_end = min(T, planned ? pl.t_end : t_begin + a.chunk);
   // query of each 16-row half of this wave (rows 32w + 16hh .. +15) and its tokens
   int qo[2], t_end_h[2];
 #pragma unroll
@@ -214,11 +218,11 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     qo[hh] = min((32 * w + 16 * hh) / Hq, nq - 1);
     t_end_h[hh] = QG > 1 ? min(length_of(i0 + qo[hh]), t_begin + a.chunk) : t_end;
   }
-  const bool final_out = a.num_splits == 1;
+  const bool final_out = !planned && a.num_splits == 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  uint16_t* const out_rows = final_out ? a.o_lat + row0 * Hq * kDc
-                                       : a.o_part + ((size_t)b * a.num_splits + split) * Hq * kDc;
-  float* const lse_out = final_out ? a.lse + row0 * Hq : a.lse_part + ((size_t)b * a.num_splits + split) * Hq;
+  const size_t part = planned ? (size_t)item : (size_t)b * a.num_splits + split;  // partial slot
+  uint16_t* const out_rows = final_out ? a.o_lat + row0 * Hq * kDc : a.o_part + part * Hq * kDc;
+  float* const lse_out = final_out ? a.lse + row0 * Hq : a.lse_part + part * Hq;
 
   if (t_begin >= t_end) {
     // No tokens in this range: zero weight (o = 0, lse = -inf).
@@ -929,7 +933,8 @@ hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1 || a.fp8)))
     return hipErrorInvalidValue;
   const int groups = (a.q_per_seq + a.q_group - 1) / a.q_group;
-  const int grid = (a.q_group > 1 ? (a.batch / a.q_per_seq) * groups : a.batch) * a.num_splits;
+  const int grid = a.items != nullptr ? a.num_items
+                                      : (a.q_group > 1 ? (a.batch / a.q_per_seq) * groups : a.batch) * a.num_splits;
   if (a.fp8) {
     if (a.block_table != nullptr) {
       hipLaunchKernelGGL((decode_latent_wide_kernel<4, true, true>), dim3(grid), dim3(256), 0, stream, a);

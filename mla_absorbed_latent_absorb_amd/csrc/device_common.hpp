@@ -163,6 +163,34 @@ __device__ __forceinline__ f32x4 lds_read_f32x4(uint32_t byte_off) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>((uintptr_t)byte_off);
 }
 
+// Scalar (wave-uniform) load of an int32 through the constant address space:
+// a vector load would make the compiler wait for every copy in flight.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p, size_t i) {
+  return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
+// Work item of a planned decode: (sequence, first 32-token tile, tile count).
+// A malformed item (sequence outside [0, batch), negative tile index, no
+// tiles) covers no tokens; ranges are clamped to max_tiles.
+struct PlanItem {
+  int seq;       // valid sequence (0 for a malformed item)
+  int t_begin;   // first token
+  int t_end;     // one past the last token (before clamping to the sequence length)
+};
+__device__ __forceinline__ PlanItem plan_item(const int32_t* items, int item, int batch, int max_seq_len) {
+  const int s = scalar_load(items, 3 * (size_t)item);
+  const int f = scalar_load(items, 3 * (size_t)item + 1);
+  const int n = scalar_load(items, 3 * (size_t)item + 2);
+  const int max_tiles = (max_seq_len + 31) / 32;
+  PlanItem p{0, 0, 0};
+  if (s >= 0 && s < batch && f >= 0 && f < max_tiles && n >= 1) {
+    p.seq = s;
+    p.t_begin = 32 * f;
+    p.t_end = 32 * (f + min(n, max_tiles - f));
+  }
+  return p;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by id.  This maps the
 // launch index so that consecutive work items (e.g. the splits of one
 // sequence, which read the same query block) run on the same XCD and share

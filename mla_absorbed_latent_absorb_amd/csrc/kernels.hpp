@@ -27,6 +27,9 @@ struct DecodeArgs {
   int32_t batch;              // query rows (decode: sequences; prefill: sequences * L)
   int32_t num_heads;
   int32_t num_splits;
+  const int32_t* items;       // planned decode: [num_items, 3] (sequence, first 32-token tile,
+                              // tile count) per workgroup, partials per item; null: uniform splits
+  int32_t num_items;
   int32_t chunk;              // tokens per split, multiple of 32
   int32_t max_seq_len;
   float scale;                // softmax scale
@@ -46,13 +49,14 @@ struct ProjArgs {
 };
 
 struct CombineArgs {
-  const uint16_t* o_part; // [B, P, H, 512] bf16
-  const float* lse_part; // [B, P, H]
+  const uint16_t* o_part; // [B, P, H, 512] bf16 (planned: [num_items, H, 512])
+  const float* lse_part; // [B, P, H] (planned: [num_items, H])
   uint16_t* o_lat;       // [B, H, 512]
   float* lse;            // [B, H] or null
   int32_t batch;
   int32_t num_heads;
-  int32_t num_splits;
+  int32_t num_splits;    // uniform splits per sequence (planned: num_items)
+  const int32_t* seq_first;  // planned: [B + 1] first item of each sequence; null: uniform
 };
 
 struct CombineExpandArgs {
@@ -64,8 +68,9 @@ struct CombineExpandArgs {
   float* lse;            // [B, H] or null
   int32_t batch;
   int32_t num_heads;
-  int32_t num_splits;
+  int32_t num_splits;    // uniform splits per sequence (planned: num_items)
   int32_t rows;          // sequences per workgroup: 4, 8 or 16 (set by the launcher)
+  const int32_t* seq_first;  // planned: [B + 1] first item of each sequence; null: uniform
 };
 
 struct AppendArgs {

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -139,7 +140,8 @@ mla_status check_read_cache(const mla_dims* dims, const mla_cache* cache, int32_
 mla_status latent_attention_rows(const char* where, const mla_dims* dims, const mla_cache* cache, const void* q_lat,
                                  const void* q_pe, const int32_t* seq_lens, const int32_t* q_start,
                                  int32_t q_per_seq, int32_t max_seq_len, int32_t num_splits, void* o_part,
-                                 float* lse_part, void* o_lat, float* lse, void* stream) {
+                                 float* lse_part, void* o_lat, float* lse, void* stream,
+                                 const int32_t* items = nullptr, int32_t num_items = 0) {
   mla_status st = check_dims(dims, where);
   if (st != MLA_OK) return st;
   if (cache == nullptr) return fail(MLA_ERR_NULL, "cache is NULL (%s)", where);
@@ -195,7 +197,20 @@ mla_status latent_attention_rows(const char* where, const mla_dims* dims, const 
   a.lse_part = lse_part;
   a.o_lat = static_cast<uint16_t*>(o_lat);
   a.lse = lse;
+  a.items = items;
+  a.num_items = num_items;
   return launch_result(mla::launch_decode_latent(a, static_cast<hipStream_t>(stream)), where);
+}
+
+// Workgroups of the decode kernel resident per CU: 8 waves of 16 heads at
+// most (the 128-head kernel holds a whole CU).
+int wg_per_cu(int num_heads) { return num_heads >= 128 ? 1 : (num_heads >= 64 ? 2 : 4); }
+
+// Shortest split: 1/32 of the context, within [32, 256] tokens (each split
+// pays a fixed prologue and epilogue and one more partial to merge).
+int64_t min_split_tokens(int32_t max_seq_len) {
+  int64_t m = max_seq_len / 32;
+  return m < 32 ? 32 : (m > 256 ? 256 : m);
 }
 
 }  // namespace
@@ -534,16 +549,131 @@ mla_status mla_cache_append(const mla_dims* dims, const mla_cache* cache, const 
   return launch_result(mla::launch_cache_append(a, fp8, static_cast<hipStream_t>(stream)), where);
 }
 
+mla_status mla_plan_decode_splits(const mla_dims* dims, const int32_t* host_seq_lens, int32_t max_seq_len,
+                                  int32_t num_cus, int32_t capacity, int32_t* items, int32_t* seq_first,
+                                  int32_t* num_items) {
+  const char* where = "mla_plan_decode_splits";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (host_seq_lens == nullptr) return fail(MLA_ERR_NULL, "host_seq_lens is NULL (%s)", where);
+  if (items == nullptr || seq_first == nullptr || num_items == nullptr)
+    return fail(MLA_ERR_NULL, "items / seq_first / num_items is NULL (%s)", where);
+  if (max_seq_len < 1) return fail(MLA_ERR_BAD_LENGTH, "max_seq_len %d < 1 (%s)", max_seq_len, where);
+  if (num_cus < 1) return fail(MLA_ERR_BAD_LENGTH, "num_cus %d < 1 (%s)", num_cus, where);
+  const int B = dims->batch;
+  // 32-token tiles per sequence (lengths clamped to [0, max_seq_len] as the kernels do)
+  int64_t max_tiles = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t t = host_seq_lens[b] < 0 ? 0 : (host_seq_lens[b] > max_seq_len ? max_seq_len : host_seq_lens[b]);
+    max_tiles = std::max<int64_t>(max_tiles, (t + 31) / 32);
+  }
+  auto tiles_of = [&](int b) -> int64_t {
+    const int64_t t = host_seq_lens[b] < 0 ? 0 : (host_seq_lens[b] > max_seq_len ? max_seq_len : host_seq_lens[b]);
+    return (t + 31) / 32;
+  };
+  auto items_for = [&](int64_t per) -> int64_t {  // items when no item exceeds `per` tiles
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b) n += std::max<int64_t>(1, (tiles_of(b) + per - 1) / per);
+    return n;
+  };
+  // The longest item sets the launch time: the fewest tiles per item such
+  // that every item runs at once (at most one resident workgroup slot each),
+  // and no shorter than the shortest useful split.
+  const int64_t slots = std::max<int64_t>((int64_t)num_cus * wg_per_cu(dims->num_heads), B);
+  int64_t lo = std::max<int64_t>(1, (min_split_tokens(max_seq_len) + 31) / 32), hi = std::max<int64_t>(lo, max_tiles);
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (items_for(mid) <= slots) hi = mid;
+    else lo = mid + 1;
+  }
+  const int64_t per = lo;
+  const int64_t total = items_for(per);
+  if (total > capacity)
+    return fail(MLA_ERR_BUFFER, "the plan has %lld items, above capacity %d (%s)", (long long)total, capacity, where);
+  // each sequence's tiles in near-equal consecutive items (sizes differ by at most one tile)
+  int32_t k = 0;
+  for (int b = 0; b < B; ++b) {
+    seq_first[b] = k;
+    const int64_t tiles = tiles_of(b);
+    const int64_t n = std::max<int64_t>(1, (tiles + per - 1) / per);
+    int64_t first = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t cnt = tiles / n + (i < tiles % n ? 1 : 0);
+      items[3 * k] = b;
+      items[3 * k + 1] = (int32_t)first;
+      items[3 * k + 2] = (int32_t)cnt;
+      first += cnt;
+      ++k;
+    }
+  }
+  seq_first[B] = k;
+  *num_items = k;
+  return ok();
+}
+
+mla_status mla_decode_latent_planned(const mla_dims* dims, const mla_cache* cache, const void* q_lat, const void* q_pe,
+                                     const int32_t* seq_lens, int32_t max_seq_len, const int32_t* items,
+                                     int32_t num_items, void* o_part, float* lse_part, void* stream) {
+  const char* where = "mla_decode_latent_planned";
+  if (items == nullptr) return fail(MLA_ERR_NULL, "items is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(items) & 3u) return fail(MLA_ERR_ALIGN, "items is not 4-byte aligned (%s)", where);
+  if (num_items < 1 || num_items > (1 << 30))
+    return fail(MLA_ERR_BAD_LENGTH, "num_items %d outside [1, 2^30] (%s)", num_items, where);
+  // num_splits > 1 selects the partial outputs in the shared checks
+  return latent_attention_rows(where, dims, cache, q_lat, q_pe, seq_lens, nullptr, 1, max_seq_len, 2, o_part,
+                               lse_part, nullptr, nullptr, stream, items, num_items);
+}
+
+mla_status mla_combine_splits_planned(const mla_dims* dims, const void* o_part, const float* lse_part,
+                                      const int32_t* seq_first, int32_t num_items, void* o_lat, float* lse,
+                                      void* stream) {
+  const char* where = "mla_combine_splits_planned";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (num_items < 1) return fail(MLA_ERR_BAD_LENGTH, "num_items %d < 1 (%s)", num_items, where);
+  REQUIRE_PTR(o_part, "o_part", where);
+  if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+  if (seq_first == nullptr) return fail(MLA_ERR_NULL, "seq_first is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(seq_first) & 3u)
+    return fail(MLA_ERR_ALIGN, "seq_first is not 4-byte aligned (%s)", where);
+  REQUIRE_PTR(o_lat, "o_lat", where);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  mla::CombineArgs a{static_cast<const uint16_t*>(o_part), lse_part, static_cast<uint16_t*>(o_lat), lse, dims->batch,
+                     dims->num_heads, num_items, seq_first};
+  return launch_result(mla::launch_combine(a, static_cast<hipStream_t>(stream)), where);
+}
+
+mla_status mla_combine_expand_v_planned(const mla_dims* dims, const void* o_part, const float* lse_part,
+                                        const int32_t* seq_first, int32_t num_items, const void* w_uv, void* out,
+                                        void* o_lat, float* lse, void* stream) {
+  const char* where = "mla_combine_expand_v_planned";
+  mla_status st = check_dims(dims, where);
+  if (st != MLA_OK) return st;
+  if (num_items < 1) return fail(MLA_ERR_BAD_LENGTH, "num_items %d < 1 (%s)", num_items, where);
+  REQUIRE_PTR(o_part, "o_part", where);
+  if (lse_part == nullptr) return fail(MLA_ERR_NULL, "lse_part is NULL (%s)", where);
+  if (seq_first == nullptr) return fail(MLA_ERR_NULL, "seq_first is NULL (%s)", where);
+  if (reinterpret_cast<uintptr_t>(seq_first) & 3u)
+    return fail(MLA_ERR_ALIGN, "seq_first is not 4-byte aligned (%s)", where);
+  REQUIRE_PTR(w_uv, "w_uv", where);
+  REQUIRE_PTR(out, "out", where);
+  if (o_lat != nullptr && (reinterpret_cast<uintptr_t>(o_lat) & 15u))
+    return fail(MLA_ERR_ALIGN, "o_lat is not 16-byte aligned (%s)", where);
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(MLA_ERR_ALIGN, "lse is not 4-byte aligned (%s)", where);
+  mla::CombineExpandArgs a{static_cast<const uint16_t*>(o_part), lse_part, static_cast<const uint16_t*>(w_uv),
+                           static_cast<uint16_t*>(out), static_cast<uint16_t*>(o_lat), lse, dims->batch,
+                           dims->num_heads, num_items, 0, seq_first};
+  return launch_result(mla::launch_combine_expand(a, static_cast<hipStream_t>(stream)), where);
+}
+
 int32_t mla_recommended_splits(const mla_dims* dims, int32_t max_seq_len, int32_t num_cus) {
   if (dims == nullptr || dims->batch <= 0 || dims->num_heads <= 0 || max_seq_len <= 0 || num_cus <= 0) return 1;
-  // workgroups resident per CU: 8 waves of 16 heads at most
-  const int wg_per_cu = dims->num_heads >= 128 ? 1 : (dims->num_heads >= 64 ? 2 : 4);
-  const int64_t want = (int64_t)num_cus * wg_per_cu;
+  const int64_t want = (int64_t)num_cus * wg_per_cu(dims->num_heads);
   int64_t p = (want + dims->batch - 1) / dims->batch;
-  // shortest split: 1/32 of the context, within [32, 256] tokens (each split
-  // pays a fixed prologue and epilogue; short splits keep few sequences busy)
-  int64_t min_tokens = max_seq_len / 32;
-  min_tokens = min_tokens < 32 ? 32 : (min_tokens > 256 ? 256 : min_tokens);
+  // short splits keep few sequences busy, but each pays a fixed cost
+  const int64_t min_tokens = min_split_tokens(max_seq_len);
   const int64_t max_p = (max_seq_len + min_tokens - 1) / min_tokens;
   if (p > max_p) p = max_p;
   if (p < 1) p = 1;

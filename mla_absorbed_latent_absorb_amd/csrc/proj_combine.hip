@@ -262,12 +262,27 @@ struct CombineRow {
   u32x4 v[8];
 };
 
+// Partial rows of one sequence: splits first .. first + P - 1 of the partial
+// arrays (uniform splits: first = b * P).  A planned merge reads them from the
+// per-sequence map seq_first; a malformed range (no splits, or outside the
+// num_items partials) is reported as invalid and merges to o = 0, lse = -inf.
+struct SplitRange {
+  int first, P;
+  bool valid;
+};
+__device__ __forceinline__ SplitRange split_range(const int32_t* seq_first, int num_splits, int b) {
+  if (seq_first == nullptr) return SplitRange{b * num_splits, num_splits, true};
+  const int f = scalar_load(seq_first, (size_t)b), e = scalar_load(seq_first, (size_t)b + 1);
+  if (f < 0 || e <= f || e > num_splits) return SplitRange{0, 1, false};  // loads stay in bounds, result masked
+  return SplitRange{f, e - f, true};
+}
+
 // Issue: lse of split `lane` (lanes < P, up to 64) and the first 8 rows.
 __device__ __forceinline__ CombineRow combine_row_issue(const uint16_t* o_part, const float* lse_part, int num_heads,
-                                                        int P, int b, int h, int lane) {
+                                                        int P, int first, int h, int lane) {
   CombineRow r;
-  r.lse_row = lse_part + (size_t)b * P * num_heads + h;
-  r.prow = o_part + ((size_t)b * P * num_heads + h) * kDc + lane * 8;
+  r.lse_row = lse_part + (size_t)first * num_heads + h;
+  r.prow = o_part + ((size_t)first * num_heads + h) * kDc + lane * 8;
   r.split_stride = (size_t)num_heads * kDc;
   // Loads are unconditional (splits past P re-read the last one; those
   // values are never used): conditional loads make the compiler copy the
@@ -338,8 +353,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int h = wid - b * a.num_heads;
   const int lane = threadIdx.x & 63;
   float lse;
-  CombineRow r = combine_row_issue(a.o_part, a.lse_part, a.num_heads, a.num_splits, b, h, lane);
-  const u32x4 o = combine_row_finish(r, a.num_heads, a.num_splits, lane, lse);
+  const SplitRange sr = split_range(a.seq_first, a.num_splits, b);
+  CombineRow r = combine_row_issue(a.o_part, a.lse_part, a.num_heads, sr.P, sr.first, h, lane);
+  u32x4 o = combine_row_finish(r, a.num_heads, sr.P, lane, lse);
+  if (!sr.valid) {
+    o = u32x4{0u, 0u, 0u, 0u};
+    lse = -INFINITY;
+  }
   *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b * a.num_heads + h) * kDc + lane * 8) = o;
   if (a.lse != nullptr && lane == 0) a.lse[(size_t)b * a.num_heads + h] = lse;
 }
@@ -382,18 +402,24 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
     // rows 2 w, 2 w + 1 (sequences past the batch repeat the last one and
     // are not stored)
     int b[2];
+    SplitRange sr[2];
     CombineRow row[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       b[i] = min(R * bg + 2 * w + i, a.batch - 1);
-      row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, a.num_splits, b[i], h, lane);
+      sr[i] = split_range(a.seq_first, a.num_splits, b[i]);
+      row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, sr[i].P, sr[i].first, h, lane);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 2 * w + i;
       const bool store = R * bg + r < a.batch;
       float lse;
-      const u32x4 o = combine_row_finish(row[i], a.num_heads, a.num_splits, lane, lse);
+      u32x4 o = combine_row_finish(row[i], a.num_heads, sr[i].P, lane, lse);
+      if (!sr[i].valid) {
+        o = u32x4{0u, 0u, 0u, 0u};
+        lse = -INFINITY;
+      }
       lds_write_u32x4(ol + (uint32_t)r * 1024u + (((uint32_t)lane ^ ((uint32_t)r & 15u)) << 4), o);
       if (store && a.o_lat != nullptr)
         *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b[i] * a.num_heads + h) * kDc + lane * 8) = o;
