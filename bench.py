@@ -1,19 +1,32 @@
 """Benchmark of one absorbed-MLA decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b32_s4096]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_b32_s4096] [--only]
 
 A step is the whole decode path of one layer for one batch: mla_absorb_q,
-mla_decode_latent (split-KV), mla_combine_splits and mla_expand_v, on seeded
-synthetic inputs already resident in HBM, issued as one HIP graph replay per
-step (the eager, call-by-call time is reported beside it).  Inputs are rotated over several
-replicas per step so the working set exceeds the 256 MB Infinity Cache and
-every step streams its latent cache from HBM.
+mla_decode_latent (split-KV; variable-length batches through the
+length-aware plan of mla_plan_decode_splits) and the merge + W_UV
+(mla_combine_expand_v), on seeded synthetic inputs already resident in HBM,
+rotated over enough replicas that every step streams its latent cache from
+HBM (the working set exceeds the 256 MB Infinity Cache).
 
 Prints one JSON line:
-  value           latent-KV GB/s over the whole step (cache bytes / step time)
+  value           latent-KV GB/s of the headline workload (V3, B=32, 4096
+                  tokens) over the whole step: W untimed steps, then the K
+                  steps as one HIP graph replay between two synchronisations
+  step_us_stats   per-step time over 7 more replays, each timed with HIP
+                  events at its ends: median / p10 / p90
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
-                  bytes per launch / its mean duration from HIP events around
-                  each launch, against 8 TB/s
+                  bytes per launch / its mean launch duration from HIP events
+                  around each launch (queued behind a GPU-side spin so no host
+                  gap falls inside), against 8 TB/s; traffic from the
+                  committed rocprofv3 byte counters
+  sclk            the shader clock sampled while the step runs
+  configs         every workload (the 26-token V2-Lite step, V2-Lite B=64,
+                  V3 B=32, paged V3 B=128 with varied lengths, E4M3 V3 B=64
+                  at 32,768 tokens): step and decode-kernel time statistics,
+                  and GB/s, TFLOP/s and tokens/s each with its fraction of the
+                  roofline (max of cache bytes / 8 TB/s and core FLOPs /
+                  2.5 PFLOP/s bf16)
   fused_step      (contexts up to 2048) mla_decode_step_fused, the same step
                   in one launch, GPU time per step from graph replays
   prefill         mla_prefill_latent on prompt / chunk shapes, TFLOP/s against
@@ -25,8 +38,9 @@ Prints one JSON line:
   append          mla_cache_append on the same shape (timed apart from the
                   step): one token per sequence, and the whole history in one
                   call against the HBM roofline (input read + cache write bytes)
-  cpu_baseline    the float64 oracle on the host cores, on a bounded sample of
-                  the same workload, in the same unit
+  cpu_baseline    the float64 oracle on all host cores, on a bounded sample of
+                  the same workload, in the same unit (cpu_baseline_1core: one
+                  core)
 """
 
 import argparse
@@ -116,9 +130,9 @@ COPY_ELEMS = 1 << 28          # float32 elements of the calibration copy (1 GiB 
 PMC_COMMANDS = [
     "export TMPDIR=/tmp",
     "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $PWD/gpurun_out/pmc_fetch -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill --no-fp8",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --only --no-cpu-baseline --no-append --no-naive --no-prefill",
     "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $PWD/gpurun_out/pmc_write -o run --output-format csv "
-    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --no-cpu-baseline --no-append --no-naive --no-prefill --no-fp8",
+    "-- python -u $PWD/bench.py --copy-calibration --steps 10 --warmup 2 --only --no-cpu-baseline --no-append --no-naive --no-prefill",
     "python bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
     "gpurun_out/pmc_write/run_counter_collection.csv",
 ]
@@ -334,48 +348,6 @@ def bench_prefill(dev):
     return res
 
 
-def bench_fp8(dev):
-    """The E4M3 long-context workload (V3 shape, B=64, T=32,768, OCP E4M3 cache
-    with a per-token fp32 scale): mla_decode_latent alone, alternating two
-    input replicas (2.4 GB, beyond the Infinity Cache), graph-replayed;
-    latent-cache GB/s (576 code bytes + 4 scale bytes per token) and TFLOP/s
-    (2 * H * (576 + 512) per cached token, on bf16 MFMAs after the decode)."""
-    import torch
-    from mla_absorbed_latent_absorb_amd import binding, datagen
-
-    wl = datagen.WORKLOADS["v3_b64_s32768_fp8"]
-    reps = [datagen.make_inputs(wl, device=dev) for _ in range(2)]
-    x0 = reps[0]
-    d = binding.dims(x0.batch, x0.heads, x0.scale)
-    P = binding.mla_recommended_splits(d, x0.max_seq_len, torch.cuda.get_device_properties(dev).multi_processor_count)
-    steps = []
-    for x in reps:
-        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, token_scale=x.token_scale)
-        st = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev, keep_latent=False)
-        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
-        steps.append((x, st))
-    k = [0]
-
-    def call():
-        x, st = steps[k[0] % 2]
-        k[0] += 1
-        st.decode(x.q_pe)
-
-    call()
-    torch.cuda.synchronize()
-    t = graph_time_per_call(call, 4, 3)
-    lens_sum = int(x0.seq_lens.to(torch.int64).sum().item())
-    nbytes = x0.cache_bytes()
-    flops = core_flops(x0.batch, x0.heads, lens_sum)
-    gbs, tf = nbytes / t / 1e9, flops / t / 1e12
-    out = {"workload": wl.name, "kernel": "mla_decode_latent", "splits": P, "decode_us": round(t * 1e6, 1),
-           "cache_bytes": nbytes, "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-           "tflops": round(tf, 1), "mfma_frac_bf16": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
-    del steps, reps
-    torch.cuda.empty_cache()
-    return out
-
-
 FUSED_MAX_CONTEXT = 2048   # the fused one-launch step is timed on short contexts only
 
 
@@ -491,19 +463,265 @@ def bench_append(x0, d, dev, steps):
     }
 
 
+def _stats(xs):
+    """median / p10 / p90 / mean of a list of durations (seconds) in us."""
+    import numpy as np
+    v = np.asarray(xs, dtype=np.float64) * 1e6
+    return {"median": round(float(np.median(v)), 3), "p10": round(float(np.percentile(v, 10)), 3),
+            "p90": round(float(np.percentile(v, 90)), 3), "mean": round(float(v.mean()), 3), "n": int(v.size)}
+
+
+class SclkSampler:
+    """Samples the GPU's current shader clock (the level the driver marks in
+    pp_dpm_sclk) in a thread while the timed work runs."""
+
+    def __init__(self):
+        import glob
+        self.path = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))), None)
+        self.samples = []
+        self._stop = False
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.strip().endswith("*"):
+                        return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is not None:
+            def loop():
+                while not self._stop:
+                    v = self._read()
+                    if v is not None:
+                        self.samples.append(v)
+                    time.sleep(0.002)
+            self._t = threading.Thread(target=loop, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self.path is not None:
+            self._t.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples)
+        busy = v[v > 500]   # levels below 500 MHz are idle moments between replays
+        if busy.size == 0:
+            busy = v
+        return {"median_mhz": int(np.median(busy)), "min_mhz": int(busy.min()), "max_mhz": int(busy.max()),
+                "samples": int(v.size), "source": "pp_dpm_sclk (current level) sampled every 2 ms during graph "
+                                                  "replays of the step"}
+
+
+def _queue_ahead(us):
+    """Hold the stream in a GPU-side spin for about `us` microseconds so the
+    launches queued behind it run back to back (events then time GPU work,
+    not host launch gaps)."""
+    import torch
+    global _SLEEP_CYCLES_PER_US
+    if _SLEEP_CYCLES_PER_US is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1000000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = 1000000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
+    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US))
+
+
+_SLEEP_CYCLES_PER_US = None
+
+# the five workloads of the decode benchmark (headline: v3_b32_s4096)
+CONFIGS = ["v2lite_b1_s26", "v2lite_b64_s4096", "v3_b32_s4096", "v3_b128_paged", "v3_b64_s32768_fp8"]
+
+
+def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=False):
+    """Time the whole decode step of one workload on inputs resident in HBM.
+
+    Step: mla_absorb_q, then the latent attention (split-KV with the library's
+    recommended split count; variable-length batches through the length-aware
+    plan, mla_plan_decode_splits, computed on the host from the host lengths
+    as an input of the step like seq_lens), then the merge + W_UV
+    (mla_combine_expand_v[_planned]) or W_UV alone (one split).  Input replicas
+    rotate so the working set exceeds the 256 MB Infinity Cache.
+
+      headline      `steps` steps as ONE HIP graph replay between two
+                    synchronisations (host clock)
+      step_us       per-step time of >= 5 more replays (HIP events at the
+                    start and end of each replay): median / p10 / p90
+      decode_us     mla_decode_latent[_planned] launches, HIP events around each
+                    launch on its stream, launches queued behind a GPU-side
+                    spin so no host gap falls between the events
+      merge_expand_us  the launch after it, timed the same way
+    """
+    import torch
+    from mla_absorbed_latent_absorb_amd import binding, datagen
+
+    props = torch.cuda.get_device_properties(dev)
+    wl = datagen.WORKLOADS[name]
+    x0 = datagen.make_inputs(wl, device=dev)
+    cache_bytes = x0.cache_bytes()
+    R = replicas or min(64, max(2, math.ceil(512e6 / cache_bytes) + 1))
+    reps = [x0] + [datagen.make_inputs(wl, device=dev) for _ in range(R - 1)]
+    d = binding.dims(x0.batch, x0.heads, x0.scale)
+    lens_host = x0.seq_lens.cpu().tolist()
+    planned = wl.len_range is not None and not splits
+    P = splits or binding.mla_recommended_splits(d, x0.max_seq_len, props.multi_processor_count)
+    plan = binding.mla_plan_decode_splits(d, lens_host, x0.max_seq_len, props.multi_processor_count,
+                                          device=dev) if planned else None
+    steps_objs = []
+    for x in reps:
+        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
+                                   block_size=x.block_size, token_scale=x.token_scale)
+        if planned:
+            st = binding.PlannedDecodeStep(d, cache, x.seq_lens, x.max_seq_len, plan, dev, keep_latent=False)
+        else:
+            st = binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev, keep_latent=False)
+        steps_objs.append((x, st))
+
+    def run(i, ev=None):
+        x, st = steps_objs[i % R]
+        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
+        if ev is not None:
+            ev[0].record()
+        st.decode(x.q_pe)
+        if ev is not None:
+            ev[1].record()
+        st.finish(x.w_uv)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # eager step: every call launched from Python
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / steps
+
+    # headline: the K steps as one graph replay between two synchronisations
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            run(i)
+    graph.replay()  # untimed: the first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    # repeated replays: per-step time from HIP events at each replay's ends
+    per_step = []
+    n_rep = 7
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+    for e0, e1 in evs:
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = [e0.elapsed_time(e1) * 1e-3 / steps for e0, e1 in evs]
+    sclk = None
+    if sample_sclk:
+        sampler = SclkSampler()
+        with sampler:
+            t_end = time.perf_counter() + 0.4
+            while time.perf_counter() < t_end:
+                graph.replay()
+                torch.cuda.synchronize()
+        sclk = sampler.summary()
+    del graph
+
+    # kernel launches: events around each launch, host queued ahead
+    n_k = max(steps, 20)
+    kev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_k)]
+    _queue_ahead(min(200000.0, 80.0 * n_k))
+    for i in range(n_k):
+        run(i, kev[i])
+    torch.cuda.synchronize()
+    dec = [a.elapsed_time(b) * 1e-3 for a, b, _ in kev]
+    tail = [b.elapsed_time(c) * 1e-3 for _, b, c in kev]
+
+    lens_sum = sum(int(v) for v in lens_host)
+    flops = core_flops(x0.batch, x0.heads, lens_sum)
+    fp8 = wl.dtype == "fp8_e4m3"
+    t_med = float(sorted(per_step)[len(per_step) // 2])
+    t_dec = sum(dec) / len(dec)
+    t_roof = max(cache_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+    bound = "hbm" if cache_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) else "mfma"
+
+    def rates(t):
+        return {"gbs": round(cache_bytes / t / 1e9, 2), "hbm_frac": round(cache_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(flops / t / 1e12, 2), "mfma_frac": round(flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                "tokens_per_s": round(x0.batch / t, 1), "tokens_frac": round(t_roof / t, 4)}
+
+    obj = {
+        "workload": name, "description": wl.description, "batch": x0.batch, "heads": x0.heads,
+        "seq_len": x0.max_seq_len, "cache_dtype": wl.dtype, "layout": wl.layout,
+        "split": ({"kind": "plan", "items": plan.num_items,
+                   "longest_item_tiles": int(plan.items_host[:, 2].max()),
+                   "uniform_rule_splits": P} if planned else {"kind": "uniform", "splits": P}),
+        "input_replicas": R, "cache_bytes": cache_bytes, "core_flops": flops,
+        "roof": {"bound": bound, "time_us": round(t_roof * 1e6, 3),
+                 "note": "max(cache bytes / 8 TB/s, core FLOPs / 2.5 PFLOP/s bf16 MFMA)" +
+                         ("; E4M3 codes enter bf16 MFMAs exactly" if fp8 else "")},
+        "headline_step_us": round(t_step * 1e6, 3),
+        "step_us": _stats(per_step),
+        "step_eager_us": round(t_eager * 1e6, 3),
+        "decode_us": _stats(dec),
+        "merge_expand_us": _stats(tail),
+        "step": rates(t_med),
+        "decode": rates(t_dec),
+    }
+    if sclk is not None:
+        obj["sclk"] = sclk
+    if x0.max_seq_len <= FUSED_MAX_CONTEXT:
+        obj["fused_step"] = bench_fused_step(x0, d, dev, steps)
+    out = dict(obj=obj, t_step=t_step, t_dec=t_dec, x0=x0, d=d, P=P, R=R, cache_bytes=cache_bytes, flops=flops,
+               t_eager=t_eager, steps=steps_objs)
+    return out
+
+
+def cpu_baselines(x):
+    """The oracle on all host cores, then on one core (BLAS threads limited)."""
+    res = {"all": cpu_baseline(x)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = cpu_baseline(x, target_s=10.0)
+        one["cores"] = 1
+        res["one"] = one
+    except Exception as e:  # pragma: no cover - informational only
+        res["one"] = {"error": str(e)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3_b32_s4096")
-    ap.add_argument("--splits", type=int, default=0, help="0 = library recommendation")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library recommendation (plan for variable lengths)")
     ap.add_argument("--replicas", type=int, default=0, help="input replicas (0 = enough for > 512 MB)")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only (no other configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-append measurement")
     ap.add_argument("--no-naive", action="store_true", help="skip the naive-decode baseline and context sweep")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3 long-context decode measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3 long-context workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB elementwise copy (y = -x) 5 times: the reference kernel "
                          "for the HBM byte counters")
@@ -530,7 +748,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from mla_absorbed_latent_absorb_amd import binding, datagen
+    from mla_absorbed_latent_absorb_amd import binding
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -545,73 +763,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    wl = datagen.WORKLOADS[args.workload]
-    x0 = datagen.make_inputs(wl, device=dev)
-    cache_bytes = x0.cache_bytes()
-    # enough replicas that the rotated inputs exceed the 256 MB Infinity Cache
-    # (tiny launch-bound workloads are capped: they are not bandwidth-bound)
-    R = args.replicas or min(64, max(2, math.ceil(512e6 / cache_bytes) + 1))
-    reps = [x0] + [datagen.make_inputs(wl, device=dev) for _ in range(R - 1)]
-    d = binding.dims(x0.batch, x0.heads, x0.scale)
-    P = args.splits or binding.mla_recommended_splits(d, x0.max_seq_len, props.multi_processor_count)
-    steps = []
-    for x in reps:
-        cache = binding.make_cache(x.kv_rows, x.pe_rows, seq_stride=x.seq_stride, block_table=x.block_table,
-                                   block_size=x.block_size, token_scale=x.token_scale)
-        steps.append((x, binding.DecodeStep(d, cache, x.seq_lens, x.max_seq_len, P, dev, keep_latent=False)))
-
-    def run(i, ev=None):
-        x, st = steps[i % R]
-        binding.mla_absorb_q(d, x.q_nope, x.w_uk, q_lat=st.q_lat)
-        if ev is not None:
-            ev[0].record()
-        st.decode(x.q_pe)
-        if ev is not None:
-            ev[1].record()
-        st.finish(x.w_uv)
-        if ev is not None:
-            ev[2].record()
-
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
-
-    # eager step: every call launched from Python
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
-    torch.cuda.synchronize()
-    t_step_eager = (time.perf_counter() - t0) / args.steps
-
-    # whole-step timing: K steps between two synchronisations, issued as one
-    # replay of a HIP graph that holds the K steps' launches (step i on input
-    # replica i mod R): no per-call host overhead between steps
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            run(i)
-    graph.replay()  # untimed: the first replay uploads the graph
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / args.steps
-    del graph
-
-    # dominant kernel: HIP events around each decode launch, and around the
-    # merge + W_UV launch after it (all on the stream the calls launch on)
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        run(i, evs[i])
-    torch.cuda.synchronize()
-    t_dec = sum(a.elapsed_time(b) for a, b, _ in evs) / len(evs) * 1e-3
-    t_tail = sum(b.elapsed_time(c) for _, b, c in evs) / len(evs) * 1e-3
-
-    lens_sum = int(x0.seq_lens.to(torch.int64).sum().item())
-    flops_core = core_flops(x0.batch, x0.heads, lens_sum)
+    head = measure_config(args.workload, dev, args.steps, args.warmup, splits=args.splits, replicas=args.replicas,
+                          sample_sclk=True)
+    ho, x0, d = head["obj"], head["x0"], head["d"]
+    t_step, t_dec = head["t_step"], head["t_dec"]
+    cache_bytes = head["cache_bytes"]
+    flops_core = head["flops"]
     flops_step = flops_core + proj_flops(x0.batch, x0.heads)
     gbs_step = cache_bytes / t_step / 1e9
     gbs_dec = cache_bytes / t_dec / 1e9
+    wl = x0.workload
     traffic = traffic_from_counters(wl.name)
 
     result = {
@@ -622,9 +783,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
-        "ms_per_step_eager": round(t_step_eager * 1e3, 5),
-        "step_timing": "one HIP graph replay holding the K steps (three launches each: absorb_q, decode_latent, "
-                       "combine_expand_v or expand_v)",
+        "ms_per_step_eager": round(head["t_eager"] * 1e3, 5),
+        "step_timing": "the K steps as one HIP graph replay between two synchronisations (three launches per "
+                       "step: absorb_q, decode_latent, combine_expand_v or expand_v); step_us: 7 more replays "
+                       "timed with HIP events",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -632,23 +794,35 @@ def main():
         "data": "synthetic (seeded N(0,1) cache and queries, N(0,1/512) weights; no checkpoint)",
         "config": {"workload": wl.name, "batch": x0.batch, "heads": x0.heads, "seq_len": x0.max_seq_len,
                    "kv_lora_rank": 512, "qk_rope_head_dim": 64, "layout": wl.layout, "cache_dtype": wl.dtype,
-                   "num_splits": P, "input_replicas": R, "cache_bytes_per_step": cache_bytes},
+                   "split": ho["split"], "input_replicas": head["R"], "cache_bytes_per_step": cache_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs_dec, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_dec / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernel": "mla_decode_latent",
-        "decode_us": round(t_dec * 1e6, 3),
-        "merge_expand_us": round(t_tail * 1e6, 3),
+        "decode_us": ho["decode_us"]["mean"],
+        "decode_us_stats": ho["decode_us"],
+        "merge_expand_us": ho["merge_expand_us"]["mean"],
+        "step_us_stats": ho["step_us"],
         "tflops_step": round(flops_step / t_step / 1e12, 3),
         "tflops_decode": round(flops_core / t_dec / 1e12, 3),
         "decode_mfma_frac": round(flops_core / t_dec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         "tokens_per_s": round(x0.batch / t_step, 1),
+        "sclk": ho.get("sclk"),
         "device": props.name,
         "cus": props.multi_processor_count,
     }
-    if x0.max_seq_len <= FUSED_MAX_CONTEXT:
-        result["fused_step"] = bench_fused_step(x0, d, dev, args.steps)
-    if not args.no_fp8 and wl.name != "v3_b64_s32768_fp8":
-        result["fp8_long_context"] = bench_fp8(dev)
+    if "fused_step" in ho:
+        result["fused_step"] = ho["fused_step"]
+    configs = {wl.name: ho}
+    if not args.only:
+        for name in CONFIGS:
+            if name == wl.name or (args.no_fp8 and name == "v3_b64_s32768_fp8"):
+                continue
+            steps_c = max(4, min(args.steps, 40)) if name in ("v3_b128_paged", "v3_b64_s32768_fp8") else args.steps
+            c = measure_config(name, dev, steps_c, max(2, min(args.warmup, 5)))
+            configs[name] = c["obj"]
+            del c
+            torch.cuda.empty_cache()
+    result["configs"] = configs
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev)
     if not args.no_naive:
@@ -657,7 +831,9 @@ def main():
     if not args.no_append:
         result["append"] = bench_append(x0, d, dev, args.steps)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x0)
+        cb = cpu_baselines(x0)
+        result["cpu_baseline"] = cb["all"]
+        result["cpu_baseline_1core"] = cb["one"]
     print(json.dumps(result), flush=True)
 
 

@@ -591,3 +591,39 @@ class DecodeStep:
         self.decode(q_pe, stream=stream)
         self.finish(w_uv, stream=stream)
         return self.out
+
+
+class PlannedDecodeStep:
+    """One absorbed decode step over a length-aware split plan, with
+    preallocated buffers: mla_absorb_q, mla_decode_latent_planned, then
+    mla_combine_expand_v_planned.  Same interface as DecodeStep."""
+
+    def __init__(self, d, cache, seq_lens, max_seq_len, plan, device, keep_latent=True):
+        B, H = d.batch, d.num_heads
+        self.keep_latent = bool(keep_latent)
+        self.d, self.cache, self.seq_lens, self.plan = d, cache, seq_lens, plan
+        self.max_seq_len = int(max_seq_len)
+        self.num_splits = plan.num_items
+        bf, f32 = torch.bfloat16, torch.float32
+        self.q_lat = torch.empty((B, H, d.kv_lora_rank), dtype=bf, device=device)
+        self.o_lat = torch.empty((B, H, d.kv_lora_rank), dtype=bf, device=device)
+        self.lse = torch.empty((B, H), dtype=f32, device=device)
+        self.out = torch.empty((B, H, d.v_head_dim), dtype=bf, device=device)
+        self.o_part = torch.empty((plan.num_items, H, d.kv_lora_rank), dtype=bf, device=device)
+        self.lse_part = torch.empty((plan.num_items, H), dtype=f32, device=device)
+
+    def decode(self, q_pe, stream=None):
+        mla_decode_latent_planned(self.d, self.cache, self.q_lat, q_pe, self.seq_lens, self.max_seq_len, self.plan,
+                                  o_part=self.o_part, lse_part=self.lse_part, stream=stream)
+
+    def finish(self, w_uv, stream=None):
+        keep = self.keep_latent
+        mla_combine_expand_v_planned(self.d, self.o_part, self.lse_part, self.plan, w_uv, out=self.out,
+                                     o_lat=self.o_lat if keep else None, lse=self.lse if keep else None,
+                                     stream=stream)
+
+    def __call__(self, q_nope, q_pe, w_uk, w_uv, stream=None):
+        mla_absorb_q(self.d, q_nope, w_uk, q_lat=self.q_lat, stream=stream)
+        self.decode(q_pe, stream=stream)
+        self.finish(w_uv, stream=stream)
+        return self.out
