@@ -16,10 +16,10 @@ Prints one JSON line:
   step_us_stats   per-step time over 7 more replays, each timed with HIP
                   events at its ends: median / p10 / p90
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
-                  bytes per launch / its mean launch duration from HIP events
-                  around each launch (queued behind a GPU-side spin so no host
-                  gap falls inside), against 8 TB/s; traffic from the
-                  committed rocprofv3 byte counters
+                  bytes per launch / its mean launch duration (HIP events at the
+                  ends of graph replays of 16 back-to-back launches on the
+                  launch stream), against 8 TB/s; traffic from the committed
+                  rocprofv3 byte counters
   sclk            the shader clock sampled while the step runs
   configs         every workload (the 26-token V2-Lite step, V2-Lite B=64,
                   V3 B=32, paged V3 B=128 with varied lengths, E4M3 V3 B=64
@@ -522,25 +522,6 @@ class SclkSampler:
                                                   "replays of the step"}
 
 
-def _queue_ahead(us):
-    """Hold the stream in a GPU-side spin for about `us` microseconds so the
-    launches queued behind it run back to back (events then time GPU work,
-    not host launch gaps)."""
-    import torch
-    global _SLEEP_CYCLES_PER_US
-    if _SLEEP_CYCLES_PER_US is None:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(1000)
-        e0.record()
-        torch.cuda._sleep(1000000)
-        e1.record()
-        torch.cuda.synchronize()
-        _SLEEP_CYCLES_PER_US = 1000000 / max(e0.elapsed_time(e1) * 1e3, 1.0)
-    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US))
-
-
-_SLEEP_CYCLES_PER_US = None
-
 # the five workloads of the decode benchmark (headline: v3_b32_s4096)
 CONFIGS = ["v2lite_b1_s26", "v2lite_b64_s4096", "v3_b32_s4096", "v3_b128_paged", "v3_b64_s32768_fp8"]
 
@@ -559,9 +540,10 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
                     synchronisations (host clock)
       step_us       per-step time of >= 5 more replays (HIP events at the
                     start and end of each replay): median / p10 / p90
-      decode_us     mla_decode_latent[_planned] launches, HIP events around each
-                    launch on its stream, launches queued behind a GPU-side
-                    spin so no host gap falls between the events
+      decode_us     mla_decode_latent[_planned] alone: 16 launches (inputs
+                    rotating over the replicas) captured in a HIP graph, 9
+                    replays each timed with HIP events at its ends on the
+                    launch stream -> mean launch duration per replay
       merge_expand_us  the launch after it, timed the same way
     """
     import torch
@@ -644,15 +626,36 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
         sclk = sampler.summary()
     del graph
 
-    # kernel launches: events around each launch, host queued ahead
-    n_k = max(steps, 20)
-    kev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(n_k)]
-    _queue_ahead(min(200000.0, 80.0 * n_k))
-    for i in range(n_k):
-        run(i, kev[i])
-    torch.cuda.synchronize()
-    dec = [a.elapsed_time(b) * 1e-3 for a, b, _ in kev]
-    tail = [b.elapsed_time(c) * 1e-3 for _, b, c in kev]
+    # kernel launches: n_k launches of one kernel alone (inputs rotating over
+    # the replicas) captured in a graph; each replay timed with HIP events at
+    # its ends gives that replay's mean launch duration
+    def kernel_replays(fn):
+        n_k = 16
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_k):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(9)]
+        for e0, e1 in ev:
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        del g
+        return [e0.elapsed_time(e1) * 1e-3 / n_k for e0, e1 in ev]
+
+    def dec_only(i):
+        x, st = steps_objs[i % R]
+        st.decode(x.q_pe)
+
+    def tail_only(i):
+        x, st = steps_objs[i % R]
+        st.finish(x.w_uv)
+
+    dec = kernel_replays(dec_only)
+    tail = kernel_replays(tail_only)
 
     lens_sum = sum(int(v) for v in lens_host)
     flops = core_flops(x0.batch, x0.heads, lens_sum)
