@@ -178,13 +178,23 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  * fp8 query): the partials are bf16, since each split's o_i is a normalised
  * average with the relative rounding error of the bf16 o_lat, and there is
  * no query scale argument, since the queries stay bf16 for every cache dtype.
- * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): the codes enter the bf16
- * matrix products exactly (every E4M3 value is a bf16 value) and the token
- * scale in fp32: s_t = softmax_scale * token_scale[slot] * (q . code_t), and
- * the probability multiplying code_t in P.V is p_t * token_scale[slot],
- * rounded to bf16 as p_t alone is for a bf16 cache.  The queries stay bf16.
- * token_scale must then be non-NULL (4-byte aligned), else MLA_ERR_NULL; a
- * bf16 cache must pass token_scale = NULL (MLA_ERR_BUFFER).
+ * E4M3 cache (mla_cache.dtype = MLA_DTYPE_FP8_E4M3): the stored codes enter
+ * the products exactly and the token scale in fp32:
+ * s_t = softmax_scale * token_scale[slot] * (q . code_t).
+ *   16, 32 or 64 heads: bf16 products (every E4M3 value is a bf16 value); the
+ *   probability multiplying code_t in P.V is p_t * token_scale[slot], rounded
+ *   to bf16 as p_t alone is for a bf16 cache.
+ *   128 heads: fp8 matrix products on the codes.  q . code_t is computed with
+ *   the bf16 query split into two E4M3 parts (hi + lo / 16, scaled per head),
+ *   which carries the query's bf16 precision.  The P.V weights
+ *   p_t * token_scale[slot] are E4M3 with a power-of-two scale per (head, 32
+ *   tokens); o is normalised by the sum of the weights as stored (each over
+ *   its token scale; weights that round to zero count at their exact value),
+ *   so o_lat is a convex combination of the cached rows, within the fp8
+ *   tolerance of the exact result; lse keeps the exact sum of p_t.
+ * The queries stay bf16.  token_scale must then be non-NULL (4-byte aligned),
+ * else MLA_ERR_NULL; a bf16 cache must pass token_scale = NULL
+ * (MLA_ERR_BUFFER).
  */
 mla_status mla_decode_latent(const mla_dims *dims, const mla_cache *cache, const void *q_lat,
                              const void *q_pe, const int32_t *seq_lens, int32_t max_seq_len,

@@ -18,7 +18,7 @@ REPO = os.path.dirname(PKG_DIR)
 LIB_NAME = "libmla_absorb.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["decode_latent.hip", "decode_latent_wide.hip", "proj_combine.hip", "cache_append.hip", "decode_step_fused.hip",
+SOURCES = ["decode_latent.hip", "decode_latent_wide.hip", "decode_latent_fp8.hip", "proj_combine.hip", "cache_append.hip", "decode_step_fused.hip",
            "naive_decode.hip", "noalloc_scratch.hip", "mla_absorb.cpp"]
 
 # -packed-fp32-ops: plain fp32 code is compiled without v_pk_{add,mul,fma}_f32.

@@ -567,7 +567,7 @@ hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
       case 16: return launch_nw<1, 4, true>(a, grid, stream);
       case 32: return launch_nw<2, 4, true>(a, grid, stream);
       case 64: return launch_nw<4, 4, true>(a, grid, stream);
-      case 128: return launch_decode_latent_wide(a, stream);
+      case 128: return launch_decode_latent_fp8(a, stream);
       default: return hipErrorInvalidValue;
     }
   }

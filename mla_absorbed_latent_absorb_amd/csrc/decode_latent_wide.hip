@@ -33,15 +33,7 @@
 //     barrier per tile.
 //   - The running max of a head moves only when it grows by more than
 //     2^kRescaleLog2 in the exp2 domain, so O is rarely rescaled.
-//   - E4M3 cache (FP8): each wave copies the raw codes, RoPE codes and
-//     per-token scales of its own 8 rows of a tile into a ring of 2 raw
-//     tiles, and widens the codes to bf16 (exact: every E4M3 value is a bf16
-//     value) into a ring of 3 bf16 tiles and 2 RoPE buffers, in chunks spread
-//     over the P.V MFMAs of the iteration two tiles earlier, with the rows'
-//     scales into a ring of 2 scale rows.  The token scale s_t then enters
-//     in fp32: score = s_t (q . code_t), and the probability that multiplies
-//     code_t in P.V is p_t s_t, rounded to bf16 as p_t alone would be.  So
-//     the E4M3 path rounds exactly where the bf16 path does.
+// (A bf16 cache; an E4M3 cache with 128 heads runs decode_latent_fp8.hip.)
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -117,7 +109,7 @@ __device__ __forceinline__ uint32_t lat_swz(uint32_t r) {
 
 }  // namespace
 
-template <int NBUF, bool PAGED, bool FP8>
+template <int NBUF, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_latent_wide_kernel(DecodeArgs a) {
   static_assert(NBUF >= 3, "a tile's latent rows stay live for two iterations");
@@ -129,40 +121,24 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   constexpr int KV_PW = kTile / NW;       // latent rows copied per wave and tile
   constexpr int PE_PW = 4 / NW;           // RoPE copies (8 rows each) per wave
   constexpr int kCopies = KV_PW + PE_PW;  // copies per wave and tile
-  // E4M3 cache (FP8): raw codes stream into a ring of 2 raw tiles and each
-  // wave decodes the 8 rows it copied into a ring of 3 bf16 tiles and 2 RoPE
-  // buffers (the LDS holds no fourth bf16 tile beside the raw ring).
-  constexpr int NLAT = FP8 ? 3 : NBUF;    // bf16 latent ring length
-  constexpr int NPE = FP8 ? 2 : NBUF - 1; // RoPE ring length
-  constexpr int NRAW = FP8 ? 2 : 0;       // raw E4M3 ring length
-  // raw tile, per wave: latent codes of rows 8w .. 8w+7 (8 x 512 B) as four
-  // 1 KiB column blocks (16-byte chunk j of row r at (j / 8) KiB + 128 r +
-  // 16 (j % 8)), their RoPE codes (8 x 64 B) as two 256 B halves (byte b of
-  // row r at 4 KiB + 256 (b / 32) + 32 r + b % 32), and scales (8 x 4 B,
-  // then copies)
-  constexpr int kRawWave = 8 * kDc + 8 * kDr + 256;
-  constexpr int kCopies8 = 4 + 2 + 1;     // E4M3 copies per wave and tile
+  constexpr int NLAT = NBUF;              // latent ring length
+  constexpr int NPE = NBUF - 1;           // RoPE ring length
   constexpr int kLatBytes = kTile * kKvRow;
   constexpr int kPeBytes = kTile * kPeRow;
   constexpr int kPeRing = 0;                    // RoPE ring, then the latent ring
   constexpr int kLatRing = kPeRing + NPE * kPeBytes;
   constexpr int kPBuf = NW * 2048;              // one tile's probabilities, [head tile][k-step] 1 KiB
-  constexpr int kRawRing = kLatRing + NLAT * kLatBytes;
-  constexpr int kPOff = kRawRing + NRAW * NW * kRawWave;
+  constexpr int kPOff = kLatRing + NLAT * kLatBytes;
   constexpr int kAlphaOff = kPOff + 2 * kPBuf;  // [2][H] rescale factors, then 1/l
   constexpr int kFlagOff = kAlphaOff + 2 * H * 4;  // [2][8] byte per wave: its softmax rescaled
-  constexpr int kScaleOff = kFlagOff + 64;         // E4M3: [2][32] fp32 token scales, ring by tile parity
-  constexpr int kSmem = kScaleOff + (FP8 ? 2 * kTile * 4 : 0);
+  constexpr int kSmem = kFlagOff + 64;
   static_assert(kSmem <= 160 * 1024, "LDS budget");
   // query staging (prologue only): per wave 16 latent rows (16 KiB) + 16
-  // RoPE rows (2 KiB).  bf16: from latent buffer 2 on (latent buffers 2 .. 3
-  // and the probability slots, all unused until tile 2 is issued); E4M3:
-  // from latent buffer 0 on (the bf16 ring is written only after every
-  // wave has read its query block; the raw ring lies past it)
-  constexpr int kQStage = FP8 ? kLatRing : kLatRing + 2 * kLatBytes;
+  // RoPE rows (2 KiB), from latent buffer 2 on (latent buffers 2 .. 3 and the
+  // probability slots, all unused until tile 2 is issued)
+  constexpr int kQStage = kLatRing + 2 * kLatBytes;
   constexpr int kQWave = 16 * 1024 + 2048;
-  static_assert(NBUF == 4 && kQStage + NW * kQWave <= (FP8 ? kRawRing : kAlphaOff),
-                "query staging must fit before the factors (E4M3: before the raw ring)");
+  static_assert(NBUF == 4 && kQStage + NW * kQWave <= kAlphaOff, "query staging must fit before the factors");
   static_assert(NW * 32 * C * 2 <= kPOff, "epilogue staging must fit in the rings");
   static_assert(kLatBytes % 1024 == 0 && kPeBytes % 1024 == 0 && kLatRing % 1024 == 0 && kPOff % 1024 == 0,
                 "buffers must stay 1 KiB aligned");
@@ -252,17 +228,8 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     uint32_t peoff;   // per-lane source offset of the wave's RoPE copy
     uint32_t lat;     // LDS latent buffer
     uint32_t pe;      // LDS RoPE buffer
-    const char* sc0;  // E4M3: token scale of the source tile's first token
-    uint32_t raw;     // E4M3: this wave's region of the raw tile
-    uint32_t roff8;   // E4M3: per-lane row part of the latent source offset (row 8w + l/8, clamped)
-    uint32_t poff8;   // E4M3: the same for the RoPE codes
-    uint32_t soff8;   // E4M3: per-lane scale offset (row 8w + l%8, clamped)
   };
   auto lat_buf = [&](int tile) -> uint32_t { return lds0 + kLatRing + (uint32_t)(tile % NLAT) * kLatBytes; };
-  // E4M3: this wave's region of the raw tile
-  auto raw_buf = [&](int tile) -> uint32_t {
-    return lds0 + kRawRing + (uint32_t)((tile & 1) * NW + w) * (uint32_t)kRawWave;
-  };
   auto pe_buf = [&](int tile) -> uint32_t { return lds0 + kPeRing + (uint32_t)(tile % NPE) * kPeBytes; };
   // Row offsets inside a tile fit 32 bits (token strides are below 2^24 bytes).
   const uint32_t kv_sb32 = (uint32_t)a.kv_sb, pe_sb32 = (uint32_t)a.pe_sb;
@@ -280,7 +247,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   const char* kv_next = kv_base + ((int64_t)cb * a.seq_stride + t_begin) * a.kv_sb;
   const char* pe_next = pe_base + ((int64_t)cb * a.seq_stride + t_begin) * a.pe_sb;
   const uint32_t kv_step = kTile * kv_sb32, pe_step = kTile * pe_sb32;
-  const char* sc_next = FP8 ? reinterpret_cast<const char*>(a.token_scale + (int64_t)cb * a.seq_stride + t_begin) : nullptr;
   auto tile_src = [&](int tile) -> TileSrc {
     const int src = min(tile, n_tiles - 1);
     const int t0 = t_begin + src * kTile;
@@ -295,25 +261,13 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       const int64_t slot0 = (int64_t)blk * a.block_size + (t0 % a.block_size);
       ts.kv0 = uniform_ptr(kv_base + slot0 * a.kv_sb);
       ts.pe0 = uniform_ptr(pe_base + slot0 * a.pe_sb);
-      if (FP8) ts.sc0 = uniform_ptr(reinterpret_cast<const char*>(a.token_scale + slot0));
     } else {
       ts.kv0 = uniform_ptr(kv_next);
       ts.pe0 = uniform_ptr(pe_next);
-      if (FP8) ts.sc0 = uniform_ptr(sc_next);
       if (tile < n_tiles - 1) {
         kv_next += kv_step;
         pe_next += pe_step;
-        if (FP8) sc_next += kTile * 4;
       }
-    }
-    if (FP8) {
-      // rows past the end re-read the last
-      const uint32_t ln = lane_id();
-      const uint32_t rc = (uint32_t)min(8 * w + (int)(ln >> 3), last);
-      const uint32_t rs = (uint32_t)min(8 * w + (int)(ln & 7u), last);
-      ts.roff8 = rc * kv_sb32 + ((ln & 7u) << 4);
-      ts.poff8 = rc * pe_sb32 + ((ln & 7u) << 2);
-      ts.soff8 = rs * 4u;
     }
     ts.kvoff = kvoff_full;
     ts.peoff = peoff_full;
@@ -326,7 +280,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     }
     ts.lat = lat_buf(tile);
     ts.pe = pe_buf(tile);
-    if (FP8) ts.raw = raw_buf(tile);
     return ts;
   };
   // Copy k < 8: latent block (w, k) (the immediate offset 128 k moves the
@@ -345,69 +298,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
       case 7: dma16_off<896, 6272>(ts.kv0, ts.kvoff, blk0); break;
       default: dma16(ts.pe0, ts.peoff, ts.pe + (uint32_t)w * 1024u); break;
     }
-  };
-  // E4M3 copy k of this wave (rows 8w .. 8w+7 of the tile): k < 4 latent
-  // column block k (16 B per lane: row l/8, chunk 8k + l%8); k = 4, 5 RoPE
-  // bytes 32(k-4) .. +31 (4 B per lane: row l/8); k = 6 the 8 scales.  The
-  // immediate offset moves the source and the destination by the same
-  // amount, so one per-lane offset serves every copy of a kind.
-  auto issue_copy8 = [&](const TileSrc& ts, int k) {
-    switch (k) {
-      case 0: dma16_off<0, 0>(ts.kv0, ts.roff8, ts.raw); break;
-      case 1: dma16_off<128, 896>(ts.kv0, ts.roff8, ts.raw); break;
-      case 2: dma16_off<256, 1792>(ts.kv0, ts.roff8, ts.raw); break;
-      case 3: dma16_off<384, 2688>(ts.kv0, ts.roff8, ts.raw); break;
-      case 4: dma4_off<0, 4096>(ts.pe0, ts.poff8, ts.raw); break;
-      case 5: dma4_off<32, 4096 + 224>(ts.pe0, ts.poff8, ts.raw); break;
-      default: dma4(ts.sc0, ts.soff8, ts.raw + (uint32_t)(8 * kDc + 8 * kDr)); break;
-    }
-  };
-  // E4M3: decode this wave's 8 rows of a raw tile (code times its token's
-  // scale in fp32, rounded to bf16) into the tile's bf16 latent and RoPE
-  // buffers.  Lane l: row 8w + l/8, 16-byte chunks (l % 8) + 8k.
-  // Per-lane parts of the decode addresses (lane l: row 8w + l/8, bf16
-  // chunks 8i + l%8 of the latent row for i < 8, RoPE chunk l%8 for i = 8),
-  // computed once where they are used; chunk i adds an immediate.
-  struct XAddr {
-    uint32_t src, src_pe, dst, dst_pe, sc;
-  };
-  auto x_addr = [&](int tile) -> XAddr {
-    const uint32_t ln = lane_id(), r8 = ln >> 3, c8 = ln & 7u, r = 8u * (uint32_t)w + r8;
-    const uint32_t rw = raw_buf(tile);
-    XAddr x;
-    x.src = rw + r8 * 128u + c8 * 8u;
-    x.src_pe = rw + (uint32_t)(8 * kDc) + (c8 >> 2) * 256u + r8 * 32u + (c8 & 3u) * 8u;
-    x.dst = lat_buf(tile) + 8u * (uint32_t)w * 1024u + r8 * 128u + ((c8 ^ lat_swz(r)) << 4);
-    x.dst_pe = pe_buf(tile) + r * (uint32_t)kPeRow + ((c8 ^ pe_swizzle(r)) << 4);
-    x.sc = rw + (uint32_t)(8 * kDc + 8 * kDr) + r8 * 4u;
-    return x;
-  };
-  auto x_src = [&](const XAddr& x, int i) -> uint32_t {
-    return i < 8 ? x.src + (uint32_t)(i >> 1) * 1024u + (uint32_t)(i & 1) * 64u : x.src_pe;
-  };
-  auto x_dst = [&](const XAddr& x, int i) -> uint32_t { return i < 8 ? x.dst + (uint32_t)i * 1024u : x.dst_pe; };
-  // eight codes -> eight bf16 values (exact)
-  auto x_dec = [&](u32x2 v) -> u32x4 {
-    u32x4 out;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x2 f = (e & 1) ? e4m3x2_to_f32<true>(v[e >> 1]) : e4m3x2_to_f32<false>(v[e >> 1]);
-      out[e] = pack_bf16x2(f[0], f[1]);
-    }
-    return out;
-  };
-  // scale row of a tile: the 32 token scales by tile parity (written by the
-  // wave that widens each row, read by every wave's softmax of that tile)
-  auto scale_row = [&](int tile) -> uint32_t { return lds0 + kScaleOff + (uint32_t)(tile & 1) * (kTile * 4); };
-  auto x_scale = [&](int tile, float sc) {
-    const uint32_t ln = lane_id();
-    if ((ln & 7u) == 0) lds_write_f32(scale_row(tile) + (8u * (uint32_t)w + (ln >> 3)) * 4u, sc);
-  };
-  auto expand = [&](int tile) {
-    const XAddr x = x_addr(tile);
-    x_scale(tile, lds_read_f32(x.sc));
-#pragma unroll
-    for (int i = 0; i < 9; ++i) lds_write_u32x4(x_dst(x, i), x_dec(lds_read_u32x2(x_src(x, i))));
   };
   auto issue_tile = [&](int tile) {
     const TileSrc ts = tile_src(tile);
@@ -459,45 +349,18 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // the reads are complete before the staging area is overwritten
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  if constexpr (FP8) {
-    // E4M3: raw tiles 0 and 1 travel with the query halves (the raw ring is
-    // apart from the staging area); once every wave has read its query block,
-    // each wave decodes its rows of tiles 0 and 1 and requests raw tile 2
-    // into the raw buffer of tile 0, which its own decode has just read.
-    stage_q(0);
-    const TileSrc ts0 = tile_src(0);
-    const TileSrc ts1 = tile_src(1);
-#pragma unroll
-    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts0, k);
-#pragma unroll
-    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts1, k);
-    wait_vmcnt<2 * kCopies8>();
-    read_q(0);
-    stage_q(1);
-    wait_vmcnt<0>();
-    read_q(1);
-    barrier();
-    expand(0);
-    expand(1);
-    const TileSrc ts2 = tile_src(2);
-#pragma unroll
-    for (int k = 0; k < kCopies8; ++k) issue_copy8(ts2, k);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier();  // the bf16 tiles 0 and 1 are complete
-  } else {
-    stage_q(0);
-    issue_tile(0);
-    wait_vmcnt<kCopies>();
-    read_q(0);
-    stage_q(1);
-    issue_tile(1);
-    wait_vmcnt<kCopies>();
-    read_q(1);
-    // every wave has read its query block (the staging area is free) and its
-    // copies of tile 0 have landed; tile 1 may still be in flight
-    barrier();
-    issue_tile(2);
-  }
+  stage_q(0);
+  issue_tile(0);
+  wait_vmcnt<kCopies>();
+  read_q(0);
+  stage_q(1);
+  issue_tile(1);
+  wait_vmcnt<kCopies>();
+  read_q(1);
+  // every wave has read its query block (the staging area is free) and its
+  // copies of tile 0 have landed; tile 1 may still be in flight
+  barrier();
+  issue_tile(2);
 
   // ---- per-lane LDS addresses inside a tile ----
   //   K fragment of score step s < 16, token half th: row 16 th + l%16, latent
@@ -590,19 +453,10 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   //   O *= alpha of slot pb if any wave's softmax of tile tv moved its
   //   reference max.
   auto iteration = [&](auto pv_tag, int tq, Scores& sc, int tv, int pb, int ps, bool rescale_check,
-                       bool commit, const TileSrc& nts, int tx) {
+                       bool commit, const TileSrc& nts) {
     constexpr bool DO_PV = decltype(pv_tag)::value;
     // one byte per wave; read now, tested after the deferred MFMAs
     const uint32_t flags = DO_PV ? lds_read_u32(lds0 + kFlagOff + pb * 8) : 0u;
-    // E4M3: scales of this lane's tokens 16 th + 4 q4 + j of tile tq, read
-    // from LDS where they are used (kept in registers they would spill)
-    auto tok_scale = [&](int th) -> f32x4 {
-      return lds_read_f32x4(scale_row(tq) + (uint32_t)(lane_id() >> 4) * 16u + (uint32_t)th * 64u);
-    };
-    // The E4M3 variant holds more state across the softmax (decode addresses
-    // and codes), so it recomputes the lane's indices where they are used.
-    auto lane_h16 = [&]() -> int { return FP8 ? (int)(lane_id() & 15u) : h16; };
-    auto lane_q4 = [&]() -> int { return FP8 ? (int)(lane_id() >> 4) : q4; };
     const uint32_t kbe = lat_buf(tq) + kb_lane;
     const uint32_t kbo = kbe ^ 64u;
     const uint32_t pb0 = pe_buf(tq) + pb_lane;
@@ -656,13 +510,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
     // slot work of step st (two slots per step): this wave's copy i in the
     // first slot of step 2i + 1, P.V operand preloads in steps 0 .. 3
     auto slot = [&](int st, int k) {
-      if (DO_PV && (st & 1) == 1 && k == 0) {
-        if constexpr (FP8) {
-          if ((st >> 1) < kCopies8) issue_copy8(nts, st >> 1);
-        } else if ((st >> 1) < kCopies) {
-          issue_copy(nts, st >> 1);
-        }
-      }
+      if (DO_PV && (st & 1) == 1 && k == 0 && (st >> 1) < kCopies) issue_copy(nts, st >> 1);
       if (DO_PV) {
         if (k == 0 && st < 2) pf[2 * st] = pf_load(2 * st, 0);
         else if (k == 1 && st < 2) pf[2 * st + 1] = pf_load(2 * st + 1, 0);
@@ -700,17 +548,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         drain_v(sp[0][1], false);
         drain_v(sp[1][0], false);
         drain_v(sp[1][1], false);
-        if constexpr (FP8) {
-          // q . code_t -> q . k_t (token scale in fp32)
-#pragma unroll
-          for (int th = 0; th < 2; ++th) {
-            const f32x4 ts = tok_scale(th);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) sp[th][hh][j] *= ts[j];
-          }
-        }
         // ragged tail (and, in a query group, tokens past each half's own
         // query): tokens 16 th + 4 q4 + j at or past the half's count
         if (min(nvalid_h[0], nvalid_h[1]) < kTile) {
@@ -720,7 +557,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (16 * th + 4 * lane_q4() + j >= nvalid_h[hh]) sp[th][hh][j] = -INFINITY;
+                if (16 * th + 4 * q4 + j >= nvalid_h[hh]) sp[th][hh][j] = -INFINITY;
         }
       } else if (c == 1 || c == 2) {
         const int hh = c - 1;
@@ -758,18 +595,12 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         // tokens 16 th + 8 g' + i; this lane's 4 tokens 16 th + 4 q4 + j are
         // elements 4 (q4 % 2) + j of lane (16 hh + h16) + 32 (q4 / 2)
         const int th = c - 22;
-        f32x4 ts = {};
-        if constexpr (FP8) ts = tok_scale(th);
         const uint32_t pw = lds0 + kPOff + (uint32_t)ps * kPBuf + (uint32_t)w * 2048u + (uint32_t)th * 1024u;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          // E4M3: P.V multiplies the codes, so the probability carries the token scale
-          f32x4 pv = {sp[th][hh][0], sp[th][hh][1], sp[th][hh][2], sp[th][hh][3]};
-          if constexpr (FP8) pv *= ts;
-          const u32x2 pk = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-          const int lq4 = lane_q4();
-          const uint32_t dl = (uint32_t)(16 * hh + lane_h16() + 32 * (lq4 >> 1));
-          lds_write_b64(pw + dl * 16u + (uint32_t)(lq4 & 1) * 8u, pk);
+          const u32x2 pk = {pack_bf16x2(sp[th][hh][0], sp[th][hh][1]), pack_bf16x2(sp[th][hh][2], sp[th][hh][3])};
+          const uint32_t dl = (uint32_t)(16 * hh + h16 + 32 * (q4 >> 1));
+          lds_write_b64(pw + dl * 16u + (uint32_t)(q4 & 1) * 8u, pk);
         }
       } else if (c == 24 || c == 25) {
         const int hh = c - 24;
@@ -778,20 +609,14 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         const float nl = fmaf(l_sum[hh], alpha[hh], psum);
         if (commit) l_sum[hh] = nl;
       } else if (c == 26) {
-        if (lane_q4() == 0) {
+        if (q4 == 0) {
           const uint32_t ab = lds0 + kAlphaOff + (uint32_t)ps * (H * 4);
-          const int lh = lane_h16();
-          lds_write_f32(ab + (32 * w + lh) * 4, alpha[0]);
-          lds_write_f32(ab + (32 * w + 16 + lh) * 4, alpha[1]);
+          lds_write_f32(ab + (32 * w + h16) * 4, alpha[0]);
+          lds_write_f32(ab + (32 * w + 16 + h16) * 4, alpha[1]);
         }
         if (lane == 0) lds_write_u8(lds0 + kFlagOff + ps * 8 + w, any_grow ? 1u : 0u);
       }
     };
-    // E4M3: this wave's rows of tile tx are decoded in 9 chunks, one after
-    // every third P.V MFMA, each chunk's LDS read issued a chunk ahead.
-    u32x2 xr[2];
-    float xsc = 0.f;
-    XAddr xa{};
 #pragma unroll
     for (int m = 0; m < 28; ++m) {
       if (DO_PV) {
@@ -802,25 +627,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
         if (m >= 12 && m < 16) pf[n] = pf_load(n, 1);
       }
       softmax_chunk(m);
-      if constexpr (FP8) {
-        if (DO_PV) {
-          if (m == 0) {
-            // raw tile tx was requested an iteration ago; only tile tx + 1's
-            // copies (issued in the score phase) may still be in flight
-            wait_vmcnt<kCopies8>();
-            xa = x_addr(tx);
-            xsc = lds_read_f32(xa.sc);
-            xr[0] = lds_read_u32x2(x_src(xa, 0));
-            x_scale(tx, xsc);
-          }
-          if (m % 3 == 1 && m / 3 < 9) {
-            const int i = m / 3;
-            const u32x2 cur = xr[i & 1];
-            if (i + 1 < 9) xr[(i + 1) & 1] = lds_read_u32x2(x_src(xa, i + 1));
-            lds_write_u32x4(x_dst(xa, i), x_dec(cur));
-          }
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -838,25 +644,14 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   static_assert(NBUF == 4, "the waits count one tile of copies in flight");
   Scores sc;
   __builtin_amdgcn_sched_barrier(0);
-  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{}, 0);
+  iteration(std::false_type(), 0, sc, 0, 0, 0, false, true, TileSrc{});
   for (int it = 0; it < n_tiles; ++it) {
     const bool has_next = it + 1 < n_tiles;
-    if constexpr (FP8) {
-      // E4M3: tile it + 1 was decoded (by every wave) in iteration it - 1
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    } else {
-      wait_vmcnt<kCopies>();
-    }
+    wait_vmcnt<kCopies>();
     barrier();  // barrier A
     __builtin_amdgcn_sched_barrier(0);
     const TileSrc nts = tile_src(it + 3);
-    // E4M3: the P.V phase also decodes this wave's rows of tile it + 2 (its
-    // raw copies, requested in iteration it - 1, have landed; those of tile
-    // it + 3 may be in flight) into the bf16 buffers of tiles it - 1 (free
-    // since barrier A) and it (RoPE rows, read by the scores of iteration
-    // it - 1).  Past the last tile the source is the last tile, so the bytes
-    // written equal the ones already there.
-    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts, it + 2);
+    iteration(std::true_type(), has_next ? it + 1 : it, sc, it, it & 1, (it + 1) & 1, it > 0, has_next, nts);
   }
 #pragma unroll
   for (int m = 28; m < 32; ++m) pv_mfma(m);  // deferred from the last tile
@@ -868,7 +663,6 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // every wave is done with the tiles and the rescale factors, and its last
   // copies (past the last tile) have landed before the rings are reused
   wait_vmcnt<0>();
-  if constexpr (FP8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
   if (q4 == 0) {
 #pragma unroll
@@ -930,21 +724,15 @@ void decode_latent_wide_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1 || a.fp8)))
+  if (a.fp8 || a.num_heads * a.q_group != 128 || (a.q_group > 1 && (a.q_start == nullptr || a.num_splits != 1)))
     return hipErrorInvalidValue;
   const int groups = (a.q_per_seq + a.q_group - 1) / a.q_group;
   const int grid = a.items != nullptr ? a.num_items
                                       : (a.q_group > 1 ? (a.batch / a.q_per_seq) * groups : a.batch) * a.num_splits;
-  if (a.fp8) {
-    if (a.block_table != nullptr) {
-      hipLaunchKernelGGL((decode_latent_wide_kernel<4, true, true>), dim3(grid), dim3(256), 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((decode_latent_wide_kernel<4, false, true>), dim3(grid), dim3(256), 0, stream, a);
-    }
-  } else if (a.block_table != nullptr) {
-    hipLaunchKernelGGL((decode_latent_wide_kernel<4, true, false>), dim3(grid), dim3(256), 0, stream, a);
+  if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, true>), dim3(grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((decode_latent_wide_kernel<4, false, false>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_latent_wide_kernel<4, false>), dim3(grid), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }

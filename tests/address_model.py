@@ -1,9 +1,9 @@
-"""Host-side model of every memory access the two decode kernels make.
+"""Host-side model of every memory access the three decode kernels make.
 
 For a launch description (the kernel arguments) this module enumerates, per
 workgroup, wave and lane, the address arithmetic of the kernels as written in
-csrc/decode_latent_wide.hip (128 heads) and csrc/decode_latent.hip (16, 32 and
-64 heads):
+csrc/decode_latent_wide.hip (128 heads, bf16 cache), csrc/decode_latent_fp8.hip
+(128 heads, E4M3 cache) and csrc/decode_latent.hip (16, 32 and 64 heads):
 
   * every direct-to-LDS copy (global_load_lds_dword[x4]): its global source
     bytes and its LDS destination bytes, including the copies issued past the
@@ -99,24 +99,20 @@ def _need(cond, msg):
 # 128-head kernel (decode_latent_wide_kernel<4, PAGED, FP8>)
 # ---------------------------------------------------------------------------
 
-def wide_lds_layout(fp8):
+def wide_lds_layout():
     NW, H = 4, 128
-    NLAT, NPE, NRAW = (3, 2, 2) if fp8 else (4, 3, 0)
+    NLAT, NPE = 4, 3
     kLatBytes, kPeBytes = TILE * 1024, TILE * 128
-    kRawWave = 8 * 512 + 8 * 64 + 256
     kPeRing = 0
     kLatRing = kPeRing + NPE * kPeBytes
-    kRawRing = kLatRing + NLAT * kLatBytes
-    kPOff = kRawRing + NRAW * NW * kRawWave
+    kPOff = kLatRing + NLAT * kLatBytes
     kPBuf = NW * 2048
     kAlphaOff = kPOff + 2 * kPBuf
     kFlagOff = kAlphaOff + 2 * H * 4
-    kScaleOff = kFlagOff + 64
-    kSmem = kScaleOff + (2 * TILE * 4 if fp8 else 0)
-    kQStage = kLatRing if fp8 else kLatRing + 2 * kLatBytes
-    return dict(NLAT=NLAT, NPE=NPE, kLatBytes=kLatBytes, kPeBytes=kPeBytes, kRawWave=kRawWave, kLatRing=kLatRing,
-                kPeRing=kPeRing, kRawRing=kRawRing, kSmem=kSmem, kQStage=kQStage, kQWave=16 * 1024 + 2048,
-                kScaleOff=kScaleOff)
+    kSmem = kFlagOff + 64
+    kQStage = kLatRing + 2 * kLatBytes
+    return dict(NLAT=NLAT, NPE=NPE, kLatBytes=kLatBytes, kPeBytes=kPeBytes, kLatRing=kLatRing,
+                kPeRing=kPeRing, kSmem=kSmem, kQStage=kQStage, kQWave=16 * 1024 + 2048)
 
 
 def wide_items(L):
@@ -166,7 +162,8 @@ def check_wide(L, max_items=None):
     """Enumerate and check every access of the 128-row kernel; returns counts.
     L.H is the number of heads per query (Hq); with fewer than 128 (grouped
     prefill) a workgroup's 128 rows are q_group queries of Hq heads."""
-    lay = wide_lds_layout(L.fp8)
+    _need(not L.fp8, "the 128-row kernel takes a bf16 cache")
+    lay = wide_lds_layout()
     Hq = L.H
     counts = dict(copies=0, stores=0, workgroups=0)
     lanes = np.arange(64)
@@ -225,44 +222,21 @@ def check_wide(L, max_items=None):
             rc = np.minimum(r[None, :], last[:, None]) if CLAMP_RAGGED_ROWS else np.broadcast_to(r, last.shape + r.shape)
             tok = t0[:, None] + rc
             _need((tok >= tb) & (tok < te), "cache row outside the workgroup's token range")
-            if not L.fp8:
-                for k in range(9):
-                    if k < 8:
-                        byte = (((lanes & 7) ^ lat_swz(r)) << 4) + 128 * k
-                        _need((byte >= 0) & (byte + 16 <= 1024), "latent copy outside the row")
-                        lat_buf = lay["kLatRing"] + (tiles % lay["NLAT"]) * lay["kLatBytes"]
-                        dst = lat_buf[:, None] + w * 8192 + 1024 * k + 16 * lanes[None, :]
-                        _need((dst >= lat_buf[:, None]) & (dst + 16 <= lat_buf[:, None] + lay["kLatBytes"]),
-                              "latent copy outside its ring buffer")
-                    else:
-                        byte = ((lanes & 7) ^ pe_swizzle(r)) << 4
-                        _need(byte + 16 <= 128, "RoPE copy outside the row")
-                        pe_buf = lay["kPeRing"] + (tiles % lay["NPE"]) * lay["kPeBytes"]
-                        dst = pe_buf[:, None] + w * 1024 + 16 * lanes[None, :]
-                        _need(dst + 16 <= pe_buf[:, None] + lay["kPeBytes"], "RoPE copy outside its buffer")
-                    counts["copies"] += tok.size
-            else:
-                rs = np.minimum((8 * w + (lanes & 7))[None, :], last[:, None])
-                raw = lay["kRawRing"] + ((tiles & 1) * 4 + w) * lay["kRawWave"]
-                for k in range(7):
-                    if k < 4:
-                        byte = ((lanes & 7) << 4) + 128 * k
-                        _need(byte + 16 <= 512, "E4M3 latent copy outside the row")
-                        dst = raw[:, None] + 1024 * k + 16 * lanes[None, :]
-                        hi = raw[:, None] + 4096
-                    elif k < 6:
-                        byte = 4 * (lanes & 7) + 32 * (k - 4)
-                        _need(byte + 4 <= 64, "E4M3 RoPE copy outside the row")
-                        dst = raw[:, None] + 4096 + 256 * (k - 4) + 4 * lanes[None, :]
-                        hi = raw[:, None] + 4096 + 512
-                    else:
-                        stok = t0[:, None] + rs
-                        _need((stok >= tb) & (stok < te), "token scale outside the range")
-                        dst = raw[:, None] + 4608 + 4 * lanes[None, :]
-                        hi = raw[:, None] + lay["kRawWave"]
-                    _need((dst >= raw[:, None]) & (dst + (16 if k < 4 else 4) <= hi), "E4M3 copy outside its region")
-                    _need(hi <= lay["kSmem"], "raw ring outside LDS")
-                    counts["copies"] += tok.size
+            for k in range(9):
+                if k < 8:
+                    byte = (((lanes & 7) ^ lat_swz(r)) << 4) + 128 * k
+                    _need((byte >= 0) & (byte + 16 <= 1024), "latent copy outside the row")
+                    lat_buf = lay["kLatRing"] + (tiles % lay["NLAT"]) * lay["kLatBytes"]
+                    dst = lat_buf[:, None] + w * 8192 + 1024 * k + 16 * lanes[None, :]
+                    _need((dst >= lat_buf[:, None]) & (dst + 16 <= lat_buf[:, None] + lay["kLatBytes"]),
+                          "latent copy outside its ring buffer")
+                else:
+                    byte = ((lanes & 7) ^ pe_swizzle(r)) << 4
+                    _need(byte + 16 <= 128, "RoPE copy outside the row")
+                    pe_buf = lay["kPeRing"] + (tiles % lay["NPE"]) * lay["kPeBytes"]
+                    dst = pe_buf[:, None] + w * 1024 + 16 * lanes[None, :]
+                    _need(dst + 16 <= pe_buf[:, None] + lay["kPeBytes"], "RoPE copy outside its buffer")
+                counts["copies"] += tok.size
             slots = L.slot(cb, tok)
             if L.num_slots is not None:
                 _need((slots >= 0) & (slots < L.num_slots), "cache slot outside the allocation")
@@ -280,6 +254,162 @@ def check_wide(L, max_items=None):
                     counts["stores"] += int(keep.sum())
             hd = 32 * w + np.arange(32)
             _need(row_lo + hd[hd < n_rows] < row_hi, "lse store outside the rows")
+    return counts
+
+
+# ---------------------------------------------------------------------------
+# 128-head E4M3 kernel (decode_latent_fp8_kernel<PAGED>)
+# ---------------------------------------------------------------------------
+
+T8 = 64   # rows per tile
+
+
+def fp8_lds_layout():
+    NW = 4
+    kLat8, kPe8, kSc8 = T8 * 512, T8 * 64, 512
+    kLatRing = 0
+    kPeRing = kLatRing + 4 * kLat8
+    kScRing = kPeRing + 3 * kPe8
+    kRtsOff = kScRing + 4 * kSc8
+    kSmem = kRtsOff + NW * 2 * 256
+    return dict(kLat8=kLat8, kPe8=kPe8, kSc8=kSc8, kLatRing=kLatRing, kPeRing=kPeRing, kScRing=kScRing,
+                kRtsOff=kRtsOff, kSmem=kSmem)
+
+
+def fp8_lds_reads():
+    """Every LDS byte range the E4M3 kernel reads inside one tile buffer, per
+    lane: (name, offsets [n, 64], width, buffer size).  These do not depend on
+    the launch."""
+    ln = np.arange(64)
+    ki, kg = ln & 31, ln >> 5
+    out = []
+    # K fragments: latent chunks of slices s < 8, token half tb
+    kbl = [ki * 512 + (((2 * kg + q) ^ (ki & 15)) << 4) for q in range(2)]
+    offs = []
+    for tb in range(2):
+        for sl in range(8):
+            x, m = (sl & 3) << 6, 256 * (sl >> 2) + 16384 * tb
+            for q in range(2):
+                offs.append((kbl[q] ^ x) + m)
+    out.append(("K latent fragment", np.array(offs), 16, T8 * 512))
+    pbl = ki * 64 + (((2 * kg) ^ ((ki >> 2) & 3)) << 4)
+    out.append(("K RoPE fragment", np.array([pbl + 2048 * tb for tb in range(2)] +
+                                            [(pbl ^ 16) + 2048 * tb for tb in range(2)]), 16, T8 * 64))
+    # V^T fragments (transposing 8-byte reads)
+    vG, vi = ln >> 4, ln & 15
+    vr0 = 8 * (vi >> 3) + 4 * (vG >> 1) + ((vi >> 1) & 3)
+    vbl = vr0 * 512 + (((vG & 1) ^ vr0) << 4) + 8 * (vi & 1)
+    out.append(("V^T fragment", np.array([((vbl ^ ((ct & 7) << 5)) + 256 * (ct >> 3)) + 8192 * q
+                                          for ct in range(16) for q in range(4)]), 8, T8 * 512))
+    # token scales (first copy of each half) and their reciprocals
+    lgo = 16 * kg
+    out.append(("token scales", np.array([256 * h + 32 * a4 + lgo for h in range(2) for a4 in range(4)]), 16, 512))
+    out.append(("token scale for its reciprocal", np.array([256 * kg + 4 * ki]), 4, 512))
+    out.append(("reciprocal scales", np.array([128 * h + 32 * a4 + lgo for h in range(2) for a4 in range(4)]),
+                16, 256))
+    return out
+
+
+def check_fp8(L, max_items=None):
+    """Enumerate and check every access of the 128-head E4M3 kernel."""
+    _need(L.fp8 and L.H == 128 and L.q_group == 1, "the E4M3 128-head kernel")
+    lay = fp8_lds_layout()
+    _need(lay["kSmem"] <= 160 * 1024, "LDS budget")
+    for name, offs, width, size in fp8_lds_reads():
+        _need((offs >= 0) & (offs % width == 0) & (offs + width <= size), name + " outside its buffer")
+    counts = dict(copies=0, stores=0, workgroups=0)
+    lanes = np.arange(64)
+    wgs = wide_items(L)
+    if max_items is not None:
+        wgs = wgs[:max_items]
+    q_rows_total = (len(L.lens) if L.q_start is None else len(L.q_start) * L.q_per_seq) * 128
+    for wg in wgs:
+        counts["workgroups"] += 1
+        row_lo = (wg["row0"] if wg["final"] else wg["part"]) * 128
+        row_hi = row_lo + 128
+        tb, te = wg["t_begin"], wg["t_end"]
+        for w in range(4):
+            # epilogue (also the empty range): rows 32w + r, 16 bytes per lane; lse of 32w + li
+            rows = row_lo + 32 * w + np.arange(32)
+            _need((rows >= row_lo) & (rows < row_hi) & (8 * lanes.max() + 8 <= 512), "o store outside the rows")
+            counts["stores"] += 32 * 64
+        if tb >= te:
+            continue
+        # query: head 32w + li, 16-byte reads 8s + 4lg + k (latent) and 4lg + k (RoPE)
+        for w in range(4):
+            head = wg["row0"] * 128 + 32 * w + (lanes & 31)
+            _need(head < q_rows_total, "q row outside the queries")
+            lat_chunks = np.array([8 * s_ + 4 * (lanes >> 5) + k for s_ in range(8) for k in range(4)])
+            _need((lat_chunks >= 0) & (16 * lat_chunks + 16 <= 1024), "q_lat read outside its row")
+            pe_chunks = np.array([4 * (lanes >> 5) + k for k in range(4)])
+            _need(16 * pe_chunks + 16 <= 128, "q_pe read outside its row")
+        n_tiles = -(-(te - tb) // T8)
+        cb = wg["cb"]
+        tiles = np.arange(n_tiles)[:, None]                  # [n, 1]
+        t0 = tb + tiles * T8
+        last = np.minimum(T8, te - t0) - 1
+        _need(last >= 0, "tile past the range")
+        lat = lay["kLatRing"] + (tiles % 4) * lay["kLat8"]
+        pe = lay["kPeRing"] + (tiles % 3) * lay["kPe8"]
+        sc = lay["kScRing"] + (tiles % 4) * lay["kSc8"]
+        if L.block_table is not None:
+            for hf in range(2):
+                h0 = t0 + 32 * hf
+                has = (hf == 0) | (last >= 32)
+                rows_h = np.minimum(32, te - h0)
+                _need(~has | ((h0 % 32 == 0) & ((h0 % L.block_size) + rows_h <= L.block_size)),
+                      "half tile crosses a block")
+
+        def src_row(hf, rc):
+            # a copy reads row rc of half hf from that half's first slot
+            base_tok = t0 + 32 * hf
+            tok = base_tok + rc
+            _need((tok >= tb) & (tok < te), "cache row outside the workgroup's token range")
+            slot = L.slot(cb, base_tok) + rc
+            _need(slot == L.slot(cb, tok), "a half tile's rows are not contiguous slots")
+            if L.num_slots is not None:
+                _need((slot >= 0) & (slot < L.num_slots), "cache slot outside the allocation")
+        for w in range(4):
+            for c in range(10):
+                if c < 8:
+                    r0 = 16 * w + 2 * c
+                    hf = np.minimum(r0, last) >> 5
+                    r = r0 + (lanes >> 5)
+                    rc = np.minimum(r, last) - 32 * hf
+                    _need((rc >= 0) & (rc < 32), "latent row outside its half")
+                    byte = ((lanes & 31) ^ (r & 15)) << 4
+                    _need(byte + 16 <= 512, "latent copy outside the row")
+                    dst = lat + r0 * 512 + 16 * lanes
+                    _need((dst >= lat) & (dst + 16 <= lat + lay["kLat8"]), "latent copy outside its buffer")
+                elif c == 8:
+                    r0 = 16 * w
+                    hf = np.minimum(r0, last) >> 5
+                    r = r0 + (lanes >> 2)
+                    rc = np.minimum(r, last) - 32 * hf
+                    _need((rc >= 0) & (rc < 32), "RoPE row outside its half")
+                    byte = ((lanes & 3) ^ ((r >> 2) & 3)) << 4
+                    _need(byte + 16 <= 64, "RoPE copy outside the row")
+                    dst = pe + r0 * 64 + 16 * lanes
+                    _need((dst >= pe) & (dst + 16 <= pe + lay["kPe8"]), "RoPE copy outside its buffer")
+                elif w < 2:
+                    hf = np.minimum(32 * w, last) >> 5
+                    r = 32 * w + (lanes & 31)
+                    rc = np.minimum(r, last) - 32 * hf
+                    _need((rc >= 0) & (rc < 32), "scale row outside its half")
+                    dst = sc + 256 * w + 4 * lanes
+                    _need((dst >= sc) & (dst + 4 <= sc + lay["kSc8"]), "scale copy outside its buffer")
+                else:
+                    continue
+                src_row(hf, rc)
+                counts["copies"] += int(rc.size)
+        _need((lat + lay["kLat8"] <= lay["kPeRing"]) & (sc + lay["kSc8"] <= lay["kRtsOff"]), "ring overlap")
+        # epilogue staging: wave w's 32 rows of 1 KiB in the latent ring
+        for w in range(4):
+            stage = w * 32768
+            ch = np.arange(64)
+            for r in range(32):
+                off = stage + r * 1024 + ((ch ^ (r & 15)) << 4)
+                _need(off + 16 <= lay["kPeRing"], "output staging outside the latent ring")
     return counts
 
 

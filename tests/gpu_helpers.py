@@ -5,9 +5,15 @@ import torch
 
 import oracle
 
-# Tolerances of the parity bar: max |gpu - ref| / max |ref| per tensor.
+# Tolerances of the parity bar: max |gpu - ref| / max |ref| per tensor, for a
+# bf16 cache and for an E4M3 cache.
 TOL_BF16 = 2e-2
 TOL_FP8 = 6e-2
+
+
+def tol_for(x):
+    """The parity bar of DecodeInputs x's cache format."""
+    return TOL_FP8 if x.workload.dtype == "fp8_e4m3" else TOL_BF16
 
 
 def bits16(t):

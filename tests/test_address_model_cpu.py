@@ -1,15 +1,15 @@
-"""Every cache read, LDS write and output store of the two decode kernels
+"""Every cache read, LDS access and output store of the three decode kernels
 stays in bounds (tests/address_model.py: the kernels' address arithmetic on
 the host), for the shapes the GPU tests use and the five benchmark
 workloads at full size -- including the copies issued past the last tile,
 the clamped rows of ragged tiles, split boundaries, planned items, paged
-caches with 32-, 64- and 256-token blocks, E4M3 raw tiles and prefill query
-groups.  No GPU is used."""
+caches with 32-, 64- and 256-token blocks, E4M3 tiles (64-row tiles in two
+32-row halves for 128 heads) and prefill query groups.  No GPU is used."""
 import numpy as np
 import pytest
 
 from mla_absorbed_latent_absorb_amd import binding
-from tests.address_model import Launch, Violation, check_narrow, check_wide
+from tests.address_model import Launch, Violation, check_fp8, check_narrow, check_wide
 
 
 def _paged(lens, bs, seed):
@@ -25,7 +25,9 @@ def _paged(lens, bs, seed):
 
 
 def _check(L, max_items=None):
-    return (check_wide if L.H == 128 else check_narrow)(L, max_items)
+    if L.H == 128:
+        return (check_fp8 if L.fp8 else check_wide)(L, max_items)
+    return check_narrow(L, max_items)
 
 
 def _recommended(B, H, S, cus=256):
@@ -46,7 +48,8 @@ def test_benchmark_workloads_contiguous(name, H, B, S, fp8, P):
 
 
 @pytest.mark.parametrize("planned", [False, True])
-def test_paged_v3_workload(planned):
+@pytest.mark.parametrize("fp8", [False, True])
+def test_paged_v3_workload(planned, fp8):
     rng = np.random.default_rng(20264)
     lens = rng.integers(1024, 16385, 128)
     S = int(lens.max())
@@ -55,9 +58,9 @@ def test_paged_v3_workload(planned):
     if planned:
         it, _ = binding.mla_plan_decode_splits(binding.dims(128, 128, 0.07), lens, S, 256)
         items = it.numpy()
-    L = Launch(128, lens, S, num_splits=_recommended(128, 128, S), block_table=table, block_size=64,
+    L = Launch(128, lens, S, num_splits=_recommended(128, 128, S), fp8=fp8, block_table=table, block_size=64,
                num_slots=slots, items=items)
-    c = check_wide(L, max_items=64)
+    c = _check(L, max_items=64)
     assert c["workgroups"] == 64
 
 
@@ -106,6 +109,19 @@ def test_checker_catches_a_cache_too_small_for_the_lengths():
     L = Launch(16, [100, 100], 100, seq_stride=100, num_slots=150)
     with pytest.raises(Violation):
         check_narrow(L)
+    L = Launch(128, [100, 100], 100, fp8=True, seq_stride=100, num_slots=150)
+    with pytest.raises(Violation):
+        check_fp8(L)
+
+
+def test_fp8_checker_catches_a_half_tile_across_blocks():
+    """A 64-row tile is copied as two 32-row halves, each from its own block:
+    with 16-token blocks a half would span two blocks, which the model reports
+    (the host accepts block sizes that are multiples of 32 only)."""
+    lens = [100]
+    table, slots = _paged(lens, 16, 3)
+    with pytest.raises(Violation):
+        check_fp8(Launch(128, lens, 100, fp8=True, block_table=table, block_size=16, num_slots=slots))
 
 
 def test_checker_catches_unclamped_ragged_rows(monkeypatch):

@@ -1,18 +1,31 @@
-"""The E4M3 decode paths through the C ABI: the codes are widened to bf16
-exactly, the per-token scale multiplies the fp32 score, and the probability
-that multiplies the codes in P.V carries the scale.  With power-of-two token
-scales every one of these products is exact, so an E4M3 cache must give
-bit-identical o_lat / lse (or partials) to a bf16 cache holding code * scale
-(exact in bf16) -- for the 128-head kernel and the 16/32/64-head kernel, with
-and without splits, contiguous and paged, and in prefill.  Parity of the E4M3
-path with the float64 oracle at general scales is covered by the E4M3 cases
-of test_parity_gpu.py, test_rescale_gpu.py and test_prefill_gpu.py."""
+"""The E4M3 decode paths through the C ABI against a bf16 cache holding the
+same values (code * scale, exact in bf16 when the token scales are powers of
+two).
+
+16, 32 and 64 heads: the codes are widened to bf16 exactly, the token scale
+multiplies the fp32 score, and the probability that multiplies the codes in
+P.V carries the scale; with power-of-two scales every one of these products
+is exact, so the E4M3 cache gives bit-identical o_lat / lse (or partials) to
+the bf16 cache, with and without splits, contiguous and paged, and in
+prefill.
+
+128 heads: the stored codes go to fp8 MFMAs and the P.V weights are E4M3
+with a power-of-two scale per (head, 32 tokens), so o differs from the bf16
+cache's by that rounding: checked against the oracle and against the bf16
+cache's result at the E4M3 bar (6e-2); lse keeps the exact sum (within 1e-3
+of the bf16 cache's).
+Parity of every E4M3 path with the float64 oracle at general scales is
+covered by the E4M3 cases of test_parity_gpu.py, test_rescale_gpu.py and
+test_prefill_gpu.py."""
 import dataclasses
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
+from tests.gpu_helpers import TOL_FP8, cache_args, f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +86,29 @@ def test_fp8_pow2_scales_equal_bf16_cache(workload, H, B, T, P):
     r8 = binding.mla_decode_latent(d, c8, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, P)
     r16 = binding.mla_decode_latent(d, c16, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, P)
     torch.cuda.synchronize()
-    assert torch.equal(r8[0], r16[0]) and torch.equal(r8[1], r16[1])
     assert torch.isfinite(r8[0].float()).all()
+    if H < 128:
+        assert torch.equal(r8[0], r16[0]) and torch.equal(r8[1], r16[1])
+        return
+    _check_fp8_mfma(x, d, q_lat, r8, r16, P)
+
+
+def _check_fp8_mfma(x, d, q_lat, r8, r16, P):
+    """128 heads: oracle parity at the E4M3 bar, and close to the bf16 cache."""
+    if P > 1:
+        o8, l8 = binding.mla_combine_splits(d, *r8)
+        o16, l16 = binding.mla_combine_splits(d, *r16)
+    else:
+        (o8, l8), (o16, l16) = r8, r16
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=x.seq_lens.cpu().numpy(), scale=x.scale,
+                                        **cache_args(x))
+    e_o, e_l = rel_err(f64(o8), ref_o), float(np.max(np.abs(l8.cpu().numpy() - ref_l)))
+    e_b = rel_err(f64(o8), f64(o16))
+    e_bl = float(torch.max(torch.abs(l8 - l16)))
+    print(f"  vs oracle: o_lat {e_o:.2e} lse {e_l:.2e}; vs bf16 cache: o_lat {e_b:.2e} lse {e_bl:.2e}")
+    assert e_o <= TOL_FP8 and e_l <= TOL_FP8
+    assert e_b <= TOL_FP8 and e_bl <= 1e-3
 
 
 # (H, P): with fewer than 128 heads and one split, a bf16 prefill groups
@@ -96,4 +130,12 @@ def test_fp8_pow2_prefill_equals_bf16_cache(H, P):
     r8 = binding.mla_prefill_latent(d, c8, q_lat, q_pe, q_start, T, num_splits=P)
     r16 = binding.mla_prefill_latent(d, c16, q_lat, q_pe, q_start, T, num_splits=P)
     torch.cuda.synchronize()
-    assert torch.equal(r8[0], r16[0]) and torch.equal(r8[1], r16[1])
+    if H < 128:
+        assert torch.equal(r8[0], r16[0]) and torch.equal(r8[1], r16[1])
+    else:
+        # empty split ranges are o = 0, lse = -inf in both
+        l8, l16 = r8[1].cpu().numpy(), r16[1].cpu().numpy()
+        assert np.array_equal(np.isneginf(l8), np.isneginf(l16))
+        fin = np.isfinite(l16)
+        assert rel_err(f64(r8[0]), f64(r16[0])) <= TOL_FP8
+        assert float(np.max(np.abs(l8[fin] - l16[fin]))) <= 1e-3

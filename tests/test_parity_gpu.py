@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import (TOL_BF16, TOL_FP8, assert_guards, bits8, bits16, cache_args, f64, guarded, rel_err,
+from tests.gpu_helpers import (TOL_BF16, TOL_FP8, assert_guards, bits8, bits16, cache_args, f64, guarded, rel_err, tol_for,
                                split_bounds)
 
 pytestmark = pytest.mark.gpu
@@ -130,7 +130,7 @@ def test_decode_latent_single_split(workload, H, B, T):
                                         scale=x.scale, **cache_args(x))
     err = rel_err(f64(o_lat), ref_o)
     lerr = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
-    assert err <= TOL_BF16 and lerr <= TOL_BF16, (err, lerr)
+    assert err <= tol_for(x) and lerr <= tol_for(x), (err, lerr)
 
 
 # ---------------------------------------------------------------------------
@@ -174,8 +174,8 @@ def test_decode_latent_splits_and_combine(workload, H, B, T, P):
             if np.isneginf(rl[i]).all():
                 assert np.isneginf(lse_part_h[b, i]).all() and np.all(o_part_h[b, i] == 0), (b, i)
             else:
-                assert rel_err(o_part_h[b, i], ro[i]) <= TOL_BF16, (b, i)
-                assert np.max(np.abs(lse_part_h[b, i] - rl[i])) <= TOL_BF16, (b, i)
+                assert rel_err(o_part_h[b, i], ro[i]) <= tol_for(x), (b, i)
+                assert np.max(np.abs(lse_part_h[b, i] - rl[i])) <= tol_for(x), (b, i)
     ref_o, ref_l = oracle.latent_decode(q64, qpe64, seq_lens=lens, scale=x.scale, **args)
     assert rel_err(f64(o_lat), ref_o) <= TOL_BF16
     assert np.max(np.abs(lse.cpu().numpy() - ref_l)) <= TOL_BF16
@@ -355,9 +355,10 @@ def test_v2lite_s26_against_naive_oracle():
 
 def test_fp8_decode_matches_bf16_decode_of_the_decoded_cache():
     """An E4M3 cache and the bf16 cache holding the same decoded values
-    (e4m3 * scale, rounded to bf16, which is what the kernel multiplies)
-    give the same result up to the bf16 rounding of P: a property check that
-    needs no oracle."""
+    (e4m3 * scale, rounded to bf16) give the same result up to the rounding
+    of the P.V weights (E4M3 with a block scale per 32 tokens for 128 heads)
+    and of the bf16 copy: a property check that needs no oracle; lse, which
+    keeps the exact sum, agrees closely."""
     announce("fp8 vs bf16 of the decoded values, H=128 B=2 T=700")
     x = _inputs("v3_b64_s32768_fp8", batch=2, seq_len=700, heads=128)
     d = binding.dims(2, 128, x.scale)
@@ -372,7 +373,7 @@ def test_fp8_decode_matches_bf16_decode_of_the_decoded_cache():
     c16 = binding.make_cache(kv16, pe16, seq_stride=x.seq_stride)
     o16, l16 = binding.mla_decode_latent(d, c16, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, 1)
     torch.cuda.synchronize()
-    assert rel_err(f64(o8), f64(o16)) <= 1e-2
+    assert rel_err(f64(o8), f64(o16)) <= TOL_FP8
     assert float(torch.max(torch.abs(l8 - l16))) <= 1e-2
 
 
@@ -402,5 +403,5 @@ def test_decode_lengths_zero_one_ragged_and_clamped(workload, H, P):
     got, gl = f64(o_lat), lse.cpu().numpy()
     assert np.all(got[0] == 0) and np.isneginf(gl[0]).all()
     for b in (1, 2, 3):
-        assert rel_err(got[b], ref_o[b]) <= TOL_BF16, b
-        assert np.max(np.abs(gl[b] - ref_l[b])) <= TOL_BF16, b
+        assert rel_err(got[b], ref_o[b]) <= tol_for(x), b
+        assert np.max(np.abs(gl[b] - ref_l[b])) <= tol_for(x), b
