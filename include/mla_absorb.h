@@ -188,10 +188,13 @@ mla_status mla_absorb_q(const mla_dims *dims, const void *q_nope, const void *w_
  *   the bf16 query split into two E4M3 parts (hi + lo / 16, scaled per head),
  *   which carries the query's bf16 precision.  The P.V weights
  *   p_t * token_scale[slot] are E4M3 with a power-of-two scale per (head, 32
- *   tokens); o is normalised by the sum of the weights as stored (each over
- *   its token scale; weights that round to zero count at their exact value),
- *   so o_lat is a convex combination of the cached rows, within the fp8
- *   tolerance of the exact result; lse keeps the exact sum of p_t.
+ *   tokens), set from a bound (the largest p_t times the largest token scale
+ *   of the 32) so that the largest weight is below 256; o is normalised by
+ *   the sum of the weights as stored, each over its token scale, except that
+ *   a token whose scale is 0 or below 2^-6 of the largest of its 32 counts
+ *   at its exact p_t; so o_lat is a convex combination of the cached rows,
+ *   within the fp8 tolerance of the exact result; lse keeps the exact sum
+ *   of p_t.
  * The queries stay bf16.  token_scale must then be non-NULL (4-byte aligned),
  * else MLA_ERR_NULL; a bf16 cache must pass token_scale = NULL
  * (MLA_ERR_BUFFER).

@@ -14,13 +14,17 @@
 //     scales carry 2^k and 2^(k-4), so s = q . code is as close to the bf16
 //     query's as a bf16 product; the token scale then multiplies s in fp32;
 //   - P.V: the probability that multiplies code_t is p_t * token_scale_t,
-//     stored as E4M3 with a power-of-two scale per (head, 32 tokens) that puts
-//     the block's largest value in [128, 256).  The 3-bit mantissa of these
+//     stored as E4M3 with a power-of-two scale per (head, 32 tokens) taken
+//     from a bound (the block's largest p times its largest token scale) so
+//     that its largest value is below 256.  The 3-bit mantissa of these
 //     weights is the one rounding that bf16 products would not make; the
 //     normaliser is therefore the sum of the weights as stored (each divided
 //     by its token scale), so that o is a convex combination of the cached
-//     rows with the stored weights, while lse keeps the exact sum.  Weights
-//     that round to zero keep their exact value in the normaliser.
+//     rows with the stored weights, while lse keeps the exact sum.  A token
+//     whose scale is 0 or below 2^-6 of the block's largest counts at its
+//     exact p in the normaliser (its row is (nearly) zero but its p is not);
+//     any other weight that rounds to zero has p below 2^-11 of the block's
+//     largest and leaves both sums alike.
 // No code is widened to bf16: tiles stay in LDS as the stored bytes.
 //
 // One workgroup per (sequence, split) or planned item, 4 waves, one per SIMD;
@@ -45,12 +49,12 @@
 //     scale block), so they never leave registers, and a later max of the
 //     same tile corrects the first half's block scale.
 //   - Per tile k, three stages: the score MFMAs of half 0 of tile k with the
-//     softmax of half 1 of tile k-1 and the copies of tile k+2 between them;
-//     the P.V MFMAs of tile k-1 with the first part of the softmax of half 0
-//     of tile k; the score MFMAs of half 1 of tile k with the rest of that
-//     softmax.  A wave's vector work does not run under its own MFMAs, so
-//     this order is about latency (every LDS read and MFMA result has time
-//     to arrive), not overlap.
+//     softmax of half 1 of tile k-1 between them; the P.V MFMAs of tile k-1
+//     with the first part of the softmax of half 0 of tile k; the score MFMAs
+//     of half 1 of tile k with the rest of that softmax and the copies of
+//     tile k+2.  A wave's vector work issues while its own MFMA runs, so the
+//     softmax is cut into steps of about one MFMA's time, one after each
+//     MFMA: the matrix core then waits on neither.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "tile_layout.hpp"
@@ -69,6 +73,9 @@ constexpr int kLat8 = kT8 * kDc;        // 32768: latent codes of a tile
 constexpr int kPe8 = kT8 * kDr;         // 4096: RoPE codes of a tile
 constexpr int kSc8 = 2 * 256;           // token scales of a tile: two halves of 32 (plus copies)
 constexpr uint32_t kE8m0One = 0x7F7F7F7Fu;  // block scale 1.0 in every byte
+// Smallest exponent of a weight bound: the scaled p (at most 2^(142 - eb))
+// of 32 tokens then sum below 2^128.
+constexpr int kEbMin = 20;
 
 // v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 A and B.  Lanes l and l+32 hold
 // row (A) / column (B) l % 32; byte p of lane l + 32 g is contraction element
@@ -131,8 +138,37 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)v;
 }
 
+// Latent copy c (0..7) of a full tile: 1 KiB from sbase + voff to LDS
+// lds + 1024 c (the offset as an immediate of the M0 add).
+__device__ __forceinline__ void lat_copy_full(int c, const char* sbase, uint32_t voff, uint32_t lds) {
+  switch (c) {
+    case 0: dma16_off<0, 0>(sbase, voff, lds); break;
+    case 1: dma16_off<0, 1024>(sbase, voff, lds); break;
+    case 2: dma16_off<0, 2048>(sbase, voff, lds); break;
+    case 3: dma16_off<0, 3072>(sbase, voff, lds); break;
+    case 4: dma16_off<0, 4096>(sbase, voff, lds); break;
+    case 5: dma16_off<0, 5120>(sbase, voff, lds); break;
+    case 6: dma16_off<0, 6144>(sbase, voff, lds); break;
+    default: dma16_off<0, 7168>(sbase, voff, lds); break;
+  }
+}
+
 // Biased fp32 exponent of x (0 for zero).
 __device__ __forceinline__ int f32_exp(float x) { return (int)((__float_as_uint(x) >> 23) & 0xFFu); }
+
+// Maximum over the 32 lanes of each wave half (DPP within rows of 16, then
+// the row swap): lanes 0..31 get the max of lanes 0..31, lanes 32..63 of 32..63.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return vmax(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float max_lanes32(float x) {
+  x = dpp_max<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  return vmax_xor16(x);
+}
 
 }  // namespace
 
@@ -238,7 +274,30 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
     t.sc = sc_buf(tile);
     return t;
   };
+  // A full tile (64 valid rows) needs no clamping: copy c's rows lie in half
+  // w / 2, and its latent offsets follow from two lane constants: the chunk
+  // part XOR 2c (the lane chunk XOR (2c + lg) is (lane chunk ^ lg) ^ 2c) plus
+  // the row part plus 2c rows.  copy_refresh() hides their values from the
+  // compiler once per tile, so that it does not hoist the eight per-copy
+  // offsets out of the loop (they would not fit the registers).
+  uint32_t cp_lat_chunk = (((uint32_t)lane & 31u) ^ ((uint32_t)lane >> 5)) << 4;
+  uint32_t cp_lat_row = (16u * (uint32_t)(w & 1) + ((uint32_t)lane >> 5)) * kv_sb;
+  auto copy_refresh = [&]() { asm volatile("" : "+v"(cp_lat_chunk), "+v"(cp_lat_row)); };
   auto copy = [&](const TileSrc& t, int c) {
+    if (t.last == kT8 - 1) {
+      const Half& hs = w >= 2 ? t.h1 : t.h0;
+      if (c < 8) {
+        const uint32_t voff = (cp_lat_chunk ^ ((uint32_t)c << 5)) + (cp_lat_row + (uint32_t)(2 * c) * kv_sb);
+        lat_copy_full(c, hs.kv, voff, t.lat + (uint32_t)(16 * w) * kDc);
+      } else if (c == 8) {
+        const uint32_t ln = lane_id();
+        const uint32_t voff = (16u * (uint32_t)(w & 1) + (ln >> 2)) * pe_sb + (((ln & 3u) ^ ((ln >> 4) & 3u)) << 4);
+        dma16(hs.pe, voff, t.pe + (uint32_t)(16 * w) * kDr);
+      } else if (c == 9 && w < 2) {
+        dma4(w ? t.h1.sc : t.h0.sc, (lane_id() & 31u) * 4u, t.sc + 256u * (uint32_t)w);
+      }
+      return;
+    }
     const uint32_t ln = lane_id();
     if (c < 8) {
       // latent rows 16w + 2c + (ln / 32): slot ln % 32 holds chunk slot ^ (row % 16)
@@ -418,26 +477,37 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
   // inputs live across the MFMAs in between.
   auto pin = [](auto& x) { asm volatile("" : "+v"(x)); };
 
-  // ---- softmax of half h of a tile, in 18 steps of about one MFMA's time ----
-  // One step follows each MFMA, so the matrix core is never left waiting on a
-  // long stretch of vector work.  scb / rtsb: the tile's token scales and
-  // their reciprocals (16-byte reads of 4 tokens issued a step ahead); nvalid:
-  // the tile's rows.  Lane li + 32 lg holds tokens 32 h + 8 (j/4) + 4 lg + j%4
-  // of head li in sc[h][j].  fresh: the half's last score MFMA was just issued.
+  // ---- softmax of half h of a tile, in 18 steps ----
+  // A step follows an MFMA and runs while it does (a wave's vector work
+  // issues under its own MFMA), so each step holds at most ~12 vector
+  // instructions (about one MFMA's time) and short dependent chains.  Step 0
+  // only requests the token scales; the others:
+  //    1-2  q . code -> q . k (token scales in fp32), ragged tail at -inf
+  //    3    the half's max;  4  the reference max (and the rescale it implies)
+  //    5    the weight bound's exponent eb, exponentials 0-1
+  //    6-9  exponentials (p 2^(134 - eb)) and the first partial sum
+  //    10   the sums l (exact) and lh
+  //    11-12 weights p * token scale (scaled);  13  their E4M3 codes
+  //    14-17 the stored-weight normaliser lh, the block scale
+  // scb / rtsb: the tile's token scales and reciprocal scales (16-byte reads
+  // of 4 tokens, issued a step or two ahead); nvalid: the tile's rows.  Lane
+  // li + 32 lg holds tokens 32 h + 8 (j/4) + 4 lg + j%4 of head li in sc[h][j].
+  // fresh: the half's last score MFMA was just issued.
   f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-  float hm = 0.f, cs = 0.f;
-  int eb = 8;
+  float hm = 0.f, xmh = 0.f, bias = 0.f, psa = 0.f, cs0 = 0.f, cs1 = 0.f;
+  int eb = kEbMin;       // biased exponent of the half's weight bound
+  float tsm0 = 0.f, tsm1 = 0.f;  // largest token scale of each half of the newest tile
   auto step = [&](int h, int i, uint32_t scb, uint32_t rtsb, int nvalid, bool fresh) {
     f32x16& s = sc[h];
     const uint32_t sp = scb + 256u * (uint32_t)h + lgo;    // token scales, + 32 a4
     const uint32_t rp = rtsb + 128u * (uint32_t)h + lgo;   // their reciprocals
-    const float mult = __uint_as_float((uint32_t)(261 - eb) << 23);
+    // the inverse of the weights' scale 2^(134 - eb) (the E8M0 block scale)
+    auto inv_mult = [&]() { return __uint_as_float((uint32_t)(eb - 7) << 23); };
     if (i == 0) {
-      drain8_v(s, fresh);
       t0 = lds_read_f32x4(sp);
       t1 = lds_read_f32x4(sp + 32u);
     } else if (i == 1 || i == 2) {
-      // q . code -> q . k (token scales in fp32)
+      if (i == 1) drain8_v(s, fresh);
       const int j0 = 8 * (i - 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -447,22 +517,21 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
       if (i == 1) {
         t0 = lds_read_f32x4(sp + 64u);
         t1 = lds_read_f32x4(sp + 96u);
-      } else if (nvalid < 32 * (h + 1)) {  // ragged tail at -inf
+      } else if (nvalid < 32 * (h + 1)) {
         const int tl = 4 * (int)kg;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
           if (32 * h + 8 * (j >> 2) + tl + (j & 3) >= nvalid) s[j] = -INFINITY;
       }
     } else if (i == 3) {
-      hm = s[0];
-#pragma unroll
-      for (int j = 1; j < 15; j += 2) hm = vmax3(hm, s[j], s[j + 1]);
-      hm = vmax_xor32(vmax(hm, s[15]));
+      const float h0 = vmax3(vmax3(s[0], s[1], s[2]), vmax3(s[3], s[4], s[5]), vmax3(s[6], s[7], s[8]));
+      const float h1 = vmax3(vmax3(s[9], s[10], s[11]), vmax3(s[12], s[13], s[14]), s[15]);
+      hm = vmax_xor32(vmax(h0, h1));
     } else if (i == 4) {
       // a new reference max when the half's max grows past the threshold
-      const float xm = hm * c2;
-      const bool up = xm > m + kRescaleLog2;
-      const float mn = up ? ceilf(xm) : m;
+      xmh = hm * c2;
+      const bool up = xmh > m + kRescaleLog2;
+      const float mn = up ? ceilf(xmh) : m;
       const int d = (up && m != -INFINITY) ? (int)fminf(mn - m, 255.f) : 0;
       m = mn;
       const float f = d >= 127 ? 0.f : __uint_as_float((uint32_t)(127 - d) << 23);  // 2^-d
@@ -476,68 +545,66 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
       pin(lh);
       pin(dpend);
       pin(pscale);
-    } else if (i >= 5 && i <= 8) {
+    } else if (i >= 5 && i <= 9) {
+      if (i == 5) {
+        // the weights p * token scale are at most (largest p) x (largest
+        // token scale) of the half: they are scaled by 2^(134 - eb) with eb
+        // the bound's exponent, so that the largest is below 256 (E4M3 holds
+        // 448); p 2^(134 - eb) = exp2(x - m + 134 - eb)
+        eb = max(f32_exp(fast_exp2(xmh - m) * (h ? tsm1 : tsm0)), kEbMin);
+        bias = (float)(134 - eb) - m;
+        pin(eb);
+      }
+      const int j0 = i == 5 ? 0 : 4 * (i - 6) + 2;
+      const int j1 = i == 9 ? 16 : (i == 5 ? 2 : j0 + 4);
 #pragma unroll
-      for (int j = 4 * (i - 5); j < 4 * (i - 4); ++j) s[j] = fast_exp2(fmaf(s[j], c2, -m));
-    } else if (i == 9) {
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; j += 4) ps += (s[j] + s[j + 1]) + (s[j + 2] + s[j + 3]);
-      l += ps;
-      lh += ps;
+      for (int j = j0; j < j1; ++j) s[j] = fast_exp2(fmaf(s[j], c2, bias));
+      if (i == 9) psa = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    } else if (i == 10) {
+      const float ps = psa + (((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15])));
+      l = fmaf(ps, inv_mult(), l);
+      lh = fmaf(ps, inv_mult(), lh);
       pin(l);
       pin(lh);
       t0 = lds_read_f32x4(sp);
       t1 = lds_read_f32x4(sp + 32u);
-    } else if (i == 10 || i == 11) {
-      // weights p * token scale and their block max
-      const int j0 = 8 * (i - 10);
-      float bm = i == 10 ? 0.f : hm;
+    } else if (i == 11 || i == 12) {
+      const int j0 = 8 * (i - 11);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         s[j0 + k] *= t0[k];
         s[j0 + 4 + k] *= t1[k];
-        bm = vmax3(bm, s[j0 + k], s[j0 + 4 + k]);
       }
-      if (i == 10) {
-        hm = bm;
+      if (i == 11) {
         t0 = lds_read_f32x4(sp + 64u);
         t1 = lds_read_f32x4(sp + 96u);
       } else {
-        eb = max(f32_exp(vmax_xor32(bm)), 8);
-        pin(eb);
-      }
-    } else if (i == 12 || i == 13) {
-      // E4M3 codes of the weights with the block max in [128, 256) (this
-      // half's previous codes were last read by the P.V of the tile before)
-      const int a0 = 2 * (i - 12);
-#pragma unroll
-      for (int a4 = a0; a4 < a0 + 2; ++a4) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) s[4 * a4 + k] *= mult;
-        pcur[4 * h + a4] = (int)pack_e4m3x4(s[4 * a4], s[4 * a4 + 1], s[4 * a4 + 2], s[4 * a4 + 3]);
-      }
-      if (i == 12) {
         t0 = lds_read_f32x4(rp);
         t1 = lds_read_f32x4(rp + 32u);
-      } else {
-        pin(pcur);
+        pin(s);
       }
+    } else if (i == 13) {
+      // E4M3 codes (this half's previous codes were last read by the P.V of
+      // the tile before)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        pcur[4 * h + a4] = (int)pack_e4m3x4(s[4 * a4], s[4 * a4 + 1], s[4 * a4 + 2], s[4 * a4 + 3]);
+      pin(pcur);
     } else if (i >= 14 && i <= 17) {
-      // normaliser: replace each exact p by (stored weight) / (token scale),
-      // except where the stored weight is zero
+      // normaliser: each exact p replaced by (stored weight) / (token scale);
+      // a token whose reciprocal scale was set to 0 (a zero scale, or one far
+      // below the half's largest) keeps its exact p
       const int a4 = i - 14;
       const f32x4 rt = (a4 & 1) ? t1 : t0;
-      if (a4 == 0) cs = 0.f;
       const f32x2 d01 = e4m3x2_to_f32<false>((uint32_t)pcur[4 * h + a4]);
       const f32x2 d23 = e4m3x2_to_f32<true>((uint32_t)pcur[4 * h + a4]);
-      const float dv[4] = {d01[0], d01[1], d23[0], d23[1]};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) cs = fmaf(dv[k] != 0.f ? dv[k] - s[4 * a4 + k] : 0.f, rt[k], cs);
+      const float c0 = a4 == 0 ? 0.f : cs0, c1 = a4 == 0 ? 0.f : cs1;
+      cs0 = fmaf(d01[0] - s[4 * a4], rt[0], fmaf(d23[0] - s[4 * a4 + 2], rt[2], c0));
+      cs1 = fmaf(d01[1] - s[4 * a4 + 1], rt[1], fmaf(d23[1] - s[4 * a4 + 3], rt[3], c1));
       if (a4 == 0) t0 = lds_read_f32x4(rp + 64u);
       if (a4 == 1) t1 = lds_read_f32x4(rp + 96u);
       if (a4 == 3) {
-        lh = fmaf(cs, __uint_as_float((uint32_t)(eb - 7) << 23), lh);  // cs / mult
+        lh = fmaf(cs0 + cs1, inv_mult(), lh);
         if (lg == h) pscale = (uint32_t)(eb - 7);
         pin(lh);
         pin(pscale);
@@ -545,11 +612,21 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
     }
   };
 
-  // reciprocal token scales of a tile (0 for a zero scale), in a per-wave region
+  // Per tile, once its scales have landed: the largest token scale of each
+  // half (tsm0 / tsm1, for the weight bounds) and the reciprocal scales in a
+  // per-wave region, 0 where the scale is 0 or below 2^-6 of its half's
+  // largest (such a token's weight may round to zero while its p matters).
   float rts_v = 0.f;
-  auto rts_load = [&](int tile) { rts_v = lds_read_f32(sc_buf(tile) + 256u * kg + 4u * ki); };
+  auto rts_load = [&](int tile) {
+    const uint32_t ln = lane_id();  // (formed here: a lane constant held across the loop would spill)
+    rts_v = lds_read_f32(sc_buf(tile) + 256u * (ln >> 5) + 4u * (ln & 31u));
+  };
   auto rts_store = [&](int tile) {
-    lds_write_f32(rts_buf(tile) + 4u * ln0, rts_v != 0.f ? __builtin_amdgcn_rcpf(rts_v) : 0.f);
+    const float mx = max_lanes32(rts_v);
+    tsm0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
+    tsm1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 32));
+    const bool keep = rts_v > 0.f && rts_v * 64.f >= mx;
+    lds_write_f32(rts_buf(tile) + 4u * lane_id(), keep ? __builtin_amdgcn_rcpf(rts_v) : 0.f);
   };
 
   // score MFMAs of half h of a tile, chunk(j) after the j-th (j = 0..17); two
@@ -607,28 +684,29 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
 
   // ---- pipeline ----
   // Iteration k < n_tiles, after the barrier (tile k landed; tile k+1's copies
-  // may be in flight; every wave is done with iteration k-1): tile k+2's
-  // copies go to the buffers of tile k-2 (latent and scales: last read in
-  // iteration k-1) and k-1 (RoPE: scored in iteration k-1).  Then
-  //   1. scores of half 0 of tile k | softmax steps 0..17 of half 1 of tile
-  //      k-1, this wave's copies of tile k+2
-  //   2. O rescale; P.V of tile k-1 | softmax steps 0..11 of half 0 of tile k
-  //   3. scores of half 1 of tile k | softmax steps 12..17 of half 0 of tile k
-  // (steps 12.. rewrite half 0's probability registers, which the P.V of
-  // stage 2 has read by then).  A last part finishes tile n_tiles-1: the
-  // softmax of its half 1 and its P.V.
+  // may be in flight; every wave is done with iteration k-1):
+  //   A. scores of half 0 of tile k | softmax steps 1..17 of half 1 of tile
+  //      k-1; the scale maxima and reciprocal scales of tile k
+  //   B. O rescale; P.V of tile k-1 | softmax steps 0..12 of half 0 of tile k
+  //   C. scores of half 1 of tile k | softmax steps 13..17 of half 0 of tile
+  //      k, this wave's copies of tile k+2 (into the buffers of tile k-2 --
+  //      latent and scales, last read in iteration k-1 -- and of tile k-1 for
+  //      the RoPE rows, scored in iteration k-1), step 0 of half 1 of tile k
+  // (step 13 rewrites half 0's probability registers, which the P.V of stage
+  // B has read by then).  A last part finishes tile n_tiles-1: the softmax of
+  // its half 1 and its P.V.
   auto begin_tile = [&](int k) {
+    copy_refresh();
     wait_tile(k + 1 < n_tiles);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // stage-1 extras of iteration k: tile k+2's copies after MFMAs 0..9, the
-  // reciprocal scales of tile k after MFMAs 10 and 12
-  auto extras = [&](int k, const TileSrc& t2, int j) {
-    if (k + 2 < n_tiles && j < 10) copy(t2, j);
-    if (j == 10) rts_load(k);
-    if (j == 12) rts_store(k);
+  // stage C of iteration k (after score MFMA j of half 1)
+  auto stage_c = [&](int k, const TileSrc& t2, int j, uint32_t sc_k, uint32_t rts_k, int nv_k) {
+    if (j < 5) step(0, 13 + j, sc_k, rts_k, nv_k, false);
+    else if (j < 15 && k + 2 < n_tiles) copy(t2, j - 5);
+    else if (j == 17) step(1, 0, sc_k, rts_k, nv_k, false);
   };
   {
     begin_tile(0);
@@ -636,12 +714,13 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
     const KAddr ka = k_addr(lat_buf(0), pe_buf(0));
     const uint32_t sc_k = sc_buf(0), rts_k = rts_buf(0);
     const int nv_k = tile_rows(0);
-    scores(ka, 0, [&](int j) { extras(0, t2, j); });
-#pragma unroll
-    for (int i = 0; i < 12; ++i) step(0, i, sc_k, rts_k, nv_k, true);
-    scores(ka, 1, [&](int j) {
-      if (j % 3 == 0) step(0, 12 + j / 3, sc_k, rts_k, nv_k, false);
+    scores(ka, 0, [&](int j) {
+      if (j == 16) rts_load(0);
+      if (j == 17) rts_store(0);
     });
+#pragma unroll
+    for (int i = 0; i < 13; ++i) step(0, i, sc_k, rts_k, nv_k, i == 1);
+    scores(ka, 1, [&](int j) { stage_c(0, t2, j, sc_k, rts_k, nv_k); });
   }
   for (int k = 1; k < n_tiles; ++k) {
     begin_tile(k);
@@ -652,23 +731,22 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
     const uint32_t sc_p = sc_buf(k - 1), rts_p = rts_buf(k - 1);
     const int nv_p = tile_rows(k - 1);
     scores(ka, 0, [&](int j) {
-      step(1, j, sc_p, rts_p, nv_p, false);
-      extras(k, t2, j);
+      if (j < 17) step(1, j + 1, sc_p, rts_p, nv_p, false);
+      if (j == 16) rts_load(k);
+      if (j == 17) rts_store(k);
     });
     rescale_o();
     pv(lat_buf(k - 1), [&](int ct) {
-      if (ct < 12) step(0, ct, sc_k, rts_k, nv_k, true);
+      if (ct < 13) step(0, ct, sc_k, rts_k, nv_k, false);
     });
-    scores(ka, 1, [&](int j) {
-      if (j % 3 == 0) step(0, 12 + j / 3, sc_k, rts_k, nv_k, false);
-    });
+    scores(ka, 1, [&](int j) { stage_c(k, t2, j, sc_k, rts_k, nv_k); });
   }
   {
     const int k = n_tiles - 1;
     const uint32_t sc_p = sc_buf(k), rts_p = rts_buf(k);
     const int nv_p = tile_rows(k);
 #pragma unroll
-    for (int i = 0; i < 18; ++i) step(1, i, sc_p, rts_p, nv_p, true);
+    for (int i = 1; i < 18; ++i) step(1, i, sc_p, rts_p, nv_p, i == 1);
     rescale_o();
     pv(lat_buf(k), [&](int) {});
   }

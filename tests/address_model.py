@@ -381,6 +381,17 @@ def check_fp8(L, max_items=None):
                     _need(byte + 16 <= 512, "latent copy outside the row")
                     dst = lat + r0 * 512 + 16 * lanes
                     _need((dst >= lat) & (dst + 16 <= lat + lay["kLat8"]), "latent copy outside its buffer")
+                    # full tiles take the lane-constant form: half w // 2, offset
+                    # ((lane chunk ^ lg) << 4 ^ (c << 5)) + (16 (w % 2) + lg + 2c) rows,
+                    # LDS lat + 16 w rows + 1024 c (the M0 immediate)
+                    full = last == T8 - 1
+                    lg = lanes >> 5
+                    fast = (((((lanes & 31) ^ lg) << 4) ^ (c << 5)) + (16 * (w & 1) + lg) * L.kv_sb
+                            + 2 * c * L.kv_sb)
+                    _need(~full | ((hf == w >> 1) & (fast == rc * L.kv_sb + byte)),
+                          "full-tile latent copy differs from the clamped form")
+                    _need(~full | (lat + 16 * w * 512 + 1024 * c + 16 * lanes == dst),
+                          "full-tile latent copy destination differs")
                 elif c == 8:
                     r0 = 16 * w
                     hf = np.minimum(r0, last) >> 5
@@ -389,6 +400,9 @@ def check_fp8(L, max_items=None):
                     _need((rc >= 0) & (rc < 32), "RoPE row outside its half")
                     byte = ((lanes & 3) ^ ((r >> 2) & 3)) << 4
                     _need(byte + 16 <= 64, "RoPE copy outside the row")
+                    fast = (16 * (w & 1) + (lanes >> 2)) * L.pe_sb + (((lanes & 3) ^ ((lanes >> 4) & 3)) << 4)
+                    _need((last != T8 - 1) | ((hf == w >> 1) & (fast == rc * L.pe_sb + byte)),
+                          "full-tile RoPE copy differs from the clamped form")
                     dst = pe + r0 * 64 + 16 * lanes
                     _need((dst >= pe) & (dst + 16 <= pe + lay["kPe8"]), "RoPE copy outside its buffer")
                 elif w < 2:
@@ -396,6 +410,8 @@ def check_fp8(L, max_items=None):
                     r = 32 * w + (lanes & 31)
                     rc = np.minimum(r, last) - 32 * hf
                     _need((rc >= 0) & (rc < 32), "scale row outside its half")
+                    _need((last != T8 - 1) | ((hf == w) & ((lanes & 31) == rc)),
+                          "full-tile scale copy differs from the clamped form")
                     dst = sc + 256 * w + 4 * lanes
                     _need((dst >= sc) & (dst + 4 <= sc + lay["kSc8"]), "scale copy outside its buffer")
                 else:
