@@ -310,7 +310,10 @@ void decode_latent_kernel(DecodeArgs a) {
   // score loop (one every kCopyStride steps) so the address unit drains them
   // while the MFMAs run instead of stalling the waves at the issue.
   constexpr int kCopyStride = 18 / (KV_PW + PE_PW) > 0 ? 18 / (KV_PW + PE_PW) : 1;
-  static_assert(FP8 || NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18, "copies must fit in the score loop");
+  constexpr int kCopiesPerStep = (KV_PW + PE_PW + 17) / 18;  // one wave (16 heads): 36 copies, two per step
+  static_assert(FP8 || NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18 * kCopiesPerStep,
+                "copies must fit in the score loop");
+  static_assert(kCopiesPerStep == 1 || kCopyStride == 1, "several copies per step only at stride 1");
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = NBUF == 1 ? 0 : it % NBUF;
     {
@@ -376,8 +379,12 @@ void decode_latent_kernel(DecodeArgs a) {
         ka[(s + 2) % 3] = lds_read_b128(ad);
         kb[(s + 2) % 3] = lds_read_b128(ad + k_hi(s + 2));
       }
-      if (!FP8 && NBUF > 1 && s % kCopyStride == 0 && s / kCopyStride < KV_PW + PE_PW) {
-        if (copy_next && s / kCopyStride < n_copy) issue_copy(nts, s / kCopyStride, ln16);
+      if (!FP8 && NBUF > 1 && s % kCopyStride == 0) {
+#pragma unroll
+        for (int c = 0; c < kCopiesPerStep; ++c) {
+          const int idx = (s / kCopyStride) * kCopiesPerStep + c;
+          if (idx < KV_PW + PE_PW && copy_next && idx < n_copy) issue_copy(nts, idx, ln16);
+        }
       }
       s0 = mfma16(ka[s % 3], q[s], s0);
       s1 = mfma16(kb[s % 3], q[s], s1);
@@ -575,7 +582,7 @@ hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_group > 1) return launch_decode_latent_wide(a, stream);
   switch (a.num_heads) {
     case 128: return launch_decode_latent_wide(a, stream);
-    case 16: return launch_nw<1, 1, false>(a, grid, stream);
+    case 16: return launch_nw<1, 2, false>(a, grid, stream);
     case 32: return launch_nw<2, 1, false>(a, grid, stream);
     case 64: return launch_nw<4, 2, false>(a, grid, stream);
     default: return hipErrorInvalidValue;

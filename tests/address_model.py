@@ -435,7 +435,7 @@ def check_fp8(L, max_items=None):
 
 def narrow_config(H, fp8):
     NW = H // 16
-    NBUF = 4 if fp8 else {1: 1, 2: 1, 4: 2}[NW]
+    NBUF = 4 if fp8 else {1: 2, 2: 1, 4: 2}[NW]
     return NW, NBUF
 
 

@@ -20,7 +20,9 @@ def lib():
 
 
 def _slots(H, cus):
-    per_cu = 1 if H >= 128 else (2 if H >= 64 else 4)
+    # resident workgroups per CU of the bf16 decode kernels (LDS-bound):
+    # 128 heads 1, 64 heads 2, 32 heads 4, 16 heads 2 (two tile buffers)
+    per_cu = 1 if H >= 128 else (2 if H >= 64 else (4 if H >= 32 else 2))
     return cus * per_cu
 
 
