@@ -203,13 +203,11 @@ mla_status latent_attention_rows(const char* where, const mla_dims* dims, const 
 }
 
 // Workgroups of the bf16 decode kernel resident per CU, as its LDS allows:
-// 16 heads, one wave with two 36 KiB tile buffers: 2; 32 heads, two waves
-// with one buffer: 4; 64 heads, four waves with two buffers: 2; the 128-head
-// kernel holds a whole CU.  (At 16 heads, 64 x 4,096 tokens, two double-
-// buffered workgroups per CU with 8 splits take 74.5 us per step against
-// 81.8 us for four single-buffered ones with 16 splits.)
+// 16 heads, a ring of four 36 KiB tiles: 1; 32 heads, two waves with one
+// buffer: 4; 64 heads, four waves with two buffers: 2; the 128-head kernel
+// holds a whole CU.
 int wg_per_cu(int num_heads) {
-  return num_heads >= 128 ? 1 : (num_heads >= 64 ? 2 : (num_heads >= 32 ? 4 : 2));
+  return num_heads >= 128 ? 1 : (num_heads >= 64 ? 2 : (num_heads >= 32 ? 4 : 1));
 }
 
 // Shortest split: 1/32 of the context, within [32, 256] tokens (each split

@@ -435,16 +435,35 @@ def check_fp8(L, max_items=None):
 
 def narrow_config(H, fp8):
     NW = H // 16
-    NBUF = 4 if fp8 else {1: 2, 2: 1, 4: 2}[NW]
+    NBUF = 4 if fp8 else {1: 4, 2: 1, 4: 2}[NW]
     return NW, NBUF
+
+
+COPY_ROWS = 11   # latent rows per copy wave of a 16-head bf16 workgroup
+
+
+def narrow_copy_plan(NW, NBUF):
+    """bf16 tile copies per wave: [(latent rows, RoPE copies)], one entry per
+    wave.  A 16-head workgroup's computing wave copies nothing; its three
+    copy waves take latent rows from COPY_ROWS * j (the last the rest) and
+    RoPE copy j (the last also the fourth)."""
+    if NW == 1 and NBUF == 4:
+        plan = [([], [])]
+        for j in range(3):
+            r0 = COPY_ROWS * j
+            r1 = r0 + COPY_ROWS if j < 2 else TILE
+            plan.append((list(range(r0, r1)), [j] + ([3] if j == 2 else [])))
+        return plan
+    KV_PW = TILE // NW
+    PE_W = NW if NW < 4 else 4
+    PE_PW = 4 // PE_W
+    return [(list(range(w * KV_PW, (w + 1) * KV_PW)), [w * PE_PW + k for k in range(PE_PW)] if w < PE_W else [])
+            for w in range(NW)]
 
 
 def check_narrow(L, max_items=None):
     H = L.H
     NW, NBUF = narrow_config(H, L.fp8)
-    KV_PW = TILE // NW
-    PE_W = NW if NW < 4 else 4
-    PE_PW = 4 // PE_W
     KV8 = 16 // NW
     E8 = (3 + NW - 1) // NW
     kRawTileBytes = 18944
@@ -499,10 +518,14 @@ def check_narrow(L, max_items=None):
                 _need(t0 % TILE == 0 and (t0 % L.block_size) + last < L.block_size, "tile crosses a block")
             buf = 0 if NBUF == 1 else tile % NBUF
             dst0 = buf * (kRawTileBytes if L.fp8 else kTileBytes)
-            for w in range(NW):
+            plan = narrow_copy_plan(NW, NBUF)
+            if not L.fp8:
+                rows_all = sorted(r for rows, _ in plan for r in rows)
+                pes_all = sorted(i for _, pes in plan for i in pes)
+                _need(rows_all == list(range(TILE)) and pes_all == [0, 1, 2, 3], "copies do not cover the tile once")
+            for w in range(len(plan) if not L.fp8 else NW):
                 if not L.fp8:
-                    for k in range(KV_PW):
-                        r = w * KV_PW + k
+                    for r in plan[w][0]:
                         tok = t0 + min(r, last)
                         byte = (16 * lanes) ^ (kv_swizzle(r) << 4)
                         _need((tok >= tb) & (tok < te) & (byte + 16 <= 1024), "latent copy out of bounds")
@@ -512,16 +535,14 @@ def check_narrow(L, max_items=None):
                         dst = dst0 + r * 1024 + 16 * lanes
                         _need(dst + 16 <= dst0 + kTileBytes, "latent copy outside its tile")
                         counts["copies"] += 64
-                    if w < PE_W:
-                        for k in range(PE_PW):
-                            i = w * PE_PW + k
-                            r = 8 * i + (lanes >> 3)
-                            c = (lanes & 7) ^ pe_swizzle(r)
-                            tok = t0 + np.minimum(r, last)
-                            _need((tok >= tb) & (tok < te) & ((c << 4) + 16 <= 128), "RoPE copy out of bounds")
-                            dst = dst0 + TILE * 1024 + i * 1024 + 16 * lanes
-                            _need(dst + 16 <= dst0 + kTileBytes, "RoPE copy outside its tile")
-                            counts["copies"] += 64
+                    for i in plan[w][1]:
+                        r = 8 * i + (lanes >> 3)
+                        c = (lanes & 7) ^ pe_swizzle(r)
+                        tok = t0 + np.minimum(r, last)
+                        _need((tok >= tb) & (tok < te) & ((c << 4) + 16 <= 128), "RoPE copy out of bounds")
+                        dst = dst0 + TILE * 1024 + i * 1024 + 16 * lanes
+                        _need(dst + 16 <= dst0 + kTileBytes, "RoPE copy outside its tile")
+                        counts["copies"] += 64
                 else:
                     for k in range(KV8 + E8):
                         if k < KV8:

@@ -171,7 +171,7 @@ def test_combine_and_expand_validation(lib):
 
 def test_recommended_splits(lib):
     assert binding.mla_recommended_splits(binding.dims(32, 128, 0.07), 4096, 256) == 8
-    assert binding.mla_recommended_splits(binding.dims(64, 16, 0.07), 4096, 256) == 8
+    assert binding.mla_recommended_splits(binding.dims(64, 16, 0.07), 4096, 256) == 4
     assert binding.mla_recommended_splits(binding.dims(1, 16, 0.07), 26, 256) == 1
 
 

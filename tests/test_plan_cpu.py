@@ -21,8 +21,8 @@ def lib():
 
 def _slots(H, cus):
     # resident workgroups per CU of the bf16 decode kernels (LDS-bound):
-    # 128 heads 1, 64 heads 2, 32 heads 4, 16 heads 2 (two tile buffers)
-    per_cu = 1 if H >= 128 else (2 if H >= 64 else (4 if H >= 32 else 2))
+    # 128 heads 1, 64 heads 2, 32 heads 4, 16 heads 1 (a ring of four tiles)
+    per_cu = 1 if H >= 128 else (2 if H >= 64 else (4 if H >= 32 else 1))
     return cus * per_cu
 
 
