@@ -444,7 +444,7 @@ mla_status mla_combine_expand_v_planned(const mla_dims *dims, const void *o_part
 /*
  * Recommended num_splits for mla_decode_latent on a device with `num_cus`
  * compute units: enough workgroups to fill the chip with the bf16 kernels'
- * resident workgroups per CU (2 at 16 heads, 4 at 32, 2 at 64, 1 at 128),
+ * resident workgroups per CU (1 at 16 heads, 4 at 32, 2 at 64, 1 at 128),
  * each split at least max_seq_len / 32 tokens, kept within [32, 256]
  * (measured on MI355X: with few sequences, shorter splits cut latency until
  * the merge and the per-split setup dominate).  Host-only.
