@@ -388,7 +388,7 @@ mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const 
  * while short sequences leave workgroups idle.  This plan instead cuts each
  * sequence into near-equal runs of whole 32-token tiles, with the fewest
  * tiles per run such that all runs fit the device at once (num_cus times
- * the resident workgroups per CU: 1 at 128 heads, 2 at 64, 4 at 16 or 32)
+ * the resident workgroups per CU: 1 at 128 heads, 2 at 64, 4 at 32, 1 at 16)
  * and no run is shorter than max(32, min(256, max_seq_len / 32)) tokens.
  * Every sequence gets at least one item (an empty sequence one item with no
  * tiles); items of a sequence are consecutive.
