@@ -8,6 +8,9 @@
 // §6.1: absorbed decode is MQA with a 576-wide key whose first 512 elements
 // are also the value).
 //
+// This kernel runs 32 and 64 heads with a bf16 cache and 16, 32 and 64 heads
+// with an E4M3 cache (16 heads with a bf16 cache: decode_latent16.hip).
+//
 // Work decomposition: one workgroup per (sequence, split), NW = H/16 waves.
 //   - The workgroup streams its token range in tiles of 32 cache rows
 //     (36,864 bytes) from HBM into LDS with 16-byte direct-to-LDS loads; each
@@ -33,36 +36,25 @@
 
 namespace mla {
 
-// A 16-head bf16 workgroup (one computing wave, a ring of NBUF tiles, one
-// workgroup per CU) has NBUF - 1 more waves that only copy tiles: a 64-lane
-// load that misses the cache holds its wave for ~155 cycles (about 20 per
-// 128-byte line, measured), so one wave could not both compute and keep
-// NBUF - 1 tiles in flight.  Copy wave j copies kCopyRows latent rows from
-// row kCopyRows * j (fewer for the last) and RoPE copy j (the last wave
-// also the fourth).
+// Waves per SIMD: the bf16 rings (one tile at 32 heads, two at 64) leave room
+// for two workgroups per CU, so a wave is held to half the registers; an E4M3
+// ring (four raw tiles and the bf16 tile) takes one workgroup per CU.
 template <int NW, int NBUF, bool FP8>
-constexpr int copy_waves() { return (!FP8 && NW == 1 && NBUF == 4) ? NBUF - 1 : 0; }
-constexpr int kCopyRows = 11;
+constexpr int narrow_waves_per_simd() { return FP8 ? 1 : 2; }
 
 template <int NW, int NBUF, bool PAGED, bool FP8>
-__global__ __launch_bounds__((NW + copy_waves<NW, NBUF, FP8>()) * 64)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(narrow_waves_per_simd<NW, NBUF, FP8>(), narrow_waves_per_simd<NW, NBUF, FP8>())))
 void decode_latent_kernel(DecodeArgs a) {
   constexpr int H = NW * 16;
-  constexpr int NCW = copy_waves<NW, NBUF, FP8>();
-  constexpr bool kHelper = NCW > 0;
-  static_assert(!kHelper || (NCW == 3 && kCopyRows * 2 < kTile && kTile - 2 * kCopyRows <= kCopyRows + 1),
-                "copy waves split a tile's 32 latent rows and 4 RoPE copies");
   // bf16 tile copies: each wave copies KV_PW latent rows; the 4 RoPE copies
-  // (8 rows each) go to waves 0..3 (or are shared evenly among fewer).  With
-  // copy waves, the computing wave copies nothing.
-  constexpr int KV_PW = kHelper ? 0 : kTile / NW;  // latent rows per computing wave
-  constexpr int PE_W = kHelper ? 0 : (NW < 4 ? NW : 4);   // computing waves that copy RoPE rows
-  constexpr int PE_PW = kHelper ? 0 : 4 / PE_W;           // RoPE copies per such wave
+  // (8 rows each) go to waves 0..3 (or are shared evenly among fewer).
+  constexpr int KV_PW = kTile / NW;       // latent rows per wave
+  constexpr int PE_W = NW < 4 ? NW : 4;   // waves that copy RoPE rows
+  constexpr int PE_PW = 4 / PE_W;         // RoPE copies per such wave
   constexpr int CB = 32 / NW;             // 16-column blocks of O owned by a wave
   constexpr int C = 512 / NW;             // latent columns owned by a wave
-  static_assert(kTile % NW == 0 && (kHelper || 4 % PE_W == 0), "tile copies must split evenly");
-  static_assert(kHelper || FP8 || KV_PW + PE_PW > 0, "a computing wave copies when no copy wave does");
+  static_assert(kTile % NW == 0 && 4 % PE_W == 0, "tile copies must split evenly");
   // E4M3 tiles (FP8): the raw tile (latent rows, RoPE rows, per-token scales)
   // streams into a ring of raw buffers and its codes are widened once per
   // tile into a single bf16 tile in the layout the bf16 path reads (exact:
@@ -117,7 +109,6 @@ void decode_latent_kernel(DecodeArgs a) {
   const int col0 = w * C;     // first latent column of this wave's P.V share
 
   if (t_begin >= t_end) {
-    if (kHelper && w >= NW) return;
     // No tokens in this range: zero weight (o = 0, lse = -inf).
     for (int r = 0; r < 16; ++r) {
       const size_t row = (size_t)(w * 16 + r);
@@ -229,44 +220,6 @@ void decode_latent_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- the copy waves (16 heads, bf16): every copy of every tile, NBUF - 1
-  // tiles ahead; they follow the computing wave's barriers (two per tile,
-  // one in the epilogue) and compute nothing ----
-  if constexpr (kHelper) {
-    if (w >= NW) {
-      const int j = w - NW;
-      const int r0 = kCopyRows * j;
-      const int nr = j < NCW - 1 ? kCopyRows : kTile - r0;   // wave-uniform
-      auto helper_tile = [&](int tile, int buf) {
-        const TileSrc ts = tile_src(tile, buf);
-        const uint32_t ln16 = lane_id() << 4;
-#pragma unroll
-        for (int k = 0; k < kCopyRows + 1; ++k)
-          if (k < nr) copy_kv(ts, r0 + k, ln16);
-        copy_pe(ts, j, ln16);
-        if (j == NCW - 1) copy_pe(ts, 3, ln16);
-      };
-      // copies a copy wave has in flight per tile (vmcnt counts them)
-      const bool two_pe = j == NCW - 1;
-#pragma unroll
-      for (int i = 0; i < NBUF - 1; ++i)
-        if (i < n_tiles) helper_tile(i, i);
-      for (int it = 0; it < n_tiles; ++it) {
-        // its copies of tile it have landed (later tiles may stay in flight)
-        const int later = min(NBUF - 2, n_tiles - 1 - it);
-        constexpr int kA = kCopyRows + 1, kB = kTile - 2 * kCopyRows + 2;  // copies per tile: waves 0..1 / the last
-        if (later <= 0) wait_vmcnt<0>();
-        else if (later == 1) { if (two_pe) wait_vmcnt<kB>(); else wait_vmcnt<kA>(); }
-        else { if (two_pe) wait_vmcnt<2 * kB>(); else wait_vmcnt<2 * kA>(); }
-        barrier();  // tile it landed; every wave is done with iteration it-1
-        if (it + NBUF - 1 < n_tiles) helper_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
-        barrier();  // the computing wave's probabilities are published
-      }
-      barrier();    // the computing wave's epilogue
-      return;
-    }
-  }
-
   // ---- query block of this wave (B operand of the score MFMA) ----
   // lane (hl, g4) holds q[h][32 s + 8 g4 .. +7] for s = 0..17 (16 latent + 2 rope)
   bf16x8 q[18];
@@ -366,7 +319,7 @@ void decode_latent_kernel(DecodeArgs a) {
   // With a ring of several tiles the next tile's copies are spread over the
   // score loop (one every kCopyStride steps) so the address unit drains them
   // while the MFMAs run instead of stalling the waves at the issue.
-  constexpr int kCompCopies = KV_PW + PE_PW;   // 0 with copy waves
+  constexpr int kCompCopies = KV_PW + PE_PW;
   constexpr int kCopyStride = kCompCopies > 0 && 18 / kCompCopies > 0 ? 18 / kCompCopies : 1;
   constexpr int kCopiesPerStep = (kCompCopies + 17) / 18;
   static_assert(FP8 || NBUF == 1 || (KV_PW + PE_PW) * kCopyStride <= 18 * kCopiesPerStep,
@@ -617,7 +570,7 @@ void decode_latent_kernel(DecodeArgs a) {
 
 template <int NW, int NBUF, bool FP8>
 static hipError_t launch_nw(const DecodeArgs& a, int grid, hipStream_t stream) {
-  const int threads = (NW + copy_waves<NW, NBUF, FP8>()) * 64;
+  const int threads = NW * 64;
   if (a.block_table != nullptr) {
     hipLaunchKernelGGL((decode_latent_kernel<NW, NBUF, true, FP8>), dim3(grid), dim3(threads), 0, stream, a);
   } else {
@@ -641,7 +594,7 @@ hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_group > 1) return launch_decode_latent_wide(a, stream);
   switch (a.num_heads) {
     case 128: return launch_decode_latent_wide(a, stream);
-    case 16: return launch_nw<1, 4, false>(a, grid, stream);
+    case 16: return launch_decode_latent16(a, stream);
     case 32: return launch_nw<2, 1, false>(a, grid, stream);
     case 64: return launch_nw<4, 2, false>(a, grid, stream);
     default: return hipErrorInvalidValue;

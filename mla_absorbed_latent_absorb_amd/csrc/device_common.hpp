@@ -115,7 +115,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+// Workgroup barrier for LDS hand-offs between waves.  s_barrier does not
+// wait for this wave's memory operations (the compiler adds no wait before
+// it on gfx950), so LDS writes issued just before it could still be pending
+// when another wave reads after it: the LDS (and scalar) operations of the
+// wave are completed first (lgkmcnt(0)).  Vector-memory loads, the
+// direct-to-LDS tile copies among them, stay in flight; their completion is
+// awaited explicitly with wait_vmcnt.  The memory clobbers keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
 
 // XOR swizzles of the 16-byte chunk index inside the rows of an LDS cache
 // tile, as functions of the row.  gfx950's LDS has 64 four-byte banks, i.e.

@@ -146,6 +146,8 @@ hipError_t scratch_region(void** ptr);
 hipError_t launch_decode_latent(const DecodeArgs& a, hipStream_t stream);
 // 128 heads, bf16 cache: 32-head waves with P.V woven into the next tile's scores.
 hipError_t launch_decode_latent_wide(const DecodeArgs& a, hipStream_t stream);
+// 16 heads, bf16 cache: two computing waves split each tile by tokens
+hipError_t launch_decode_latent16(const DecodeArgs& a, hipStream_t stream);
 // 128 heads, E4M3 cache: the stored codes on fp8 MFMAs.
 hipError_t launch_decode_latent_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream);

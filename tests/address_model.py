@@ -430,6 +430,148 @@ def check_fp8(L, max_items=None):
 
 
 # ---------------------------------------------------------------------------
+# 16-head bf16 kernel (decode_latent16_kernel<NCW, NBUF, PAGED>)
+# ---------------------------------------------------------------------------
+
+L16_NCW = 3       # copy waves
+L16_NBUF = 3      # ring of tiles
+L16_TILE_BYTES = 36864
+
+
+def latent16_copy_plan(ncw=L16_NCW):
+    """Copy i of a tile (0..35: latent row i, then RoPE copies i - 32) goes to
+    copy wave i % ncw, which issues j, j + ncw, ..."""
+    return [[j + ncw * k for k in range(36 // ncw)] for j in range(ncw)]
+
+
+def _range_of(L, item, B, H):
+    """(b, cache sequence, t_begin, t_end, output row range) of a workgroup,
+    as the narrow kernels compute them."""
+    max_tiles = -(-L.max_seq_len // 32)
+    planned = L.items is not None
+    if planned:
+        s, f, n = L.items[item]
+        ok = 0 <= s < len(L.lens) and 0 <= f < max_tiles and n >= 1
+        pl = (s, 32 * f, 32 * (f + min(n, max_tiles - f))) if ok else (0, 0, 0)
+        qrow, split = pl[0], item
+    else:
+        qrow, split = item // L.P, item % L.P
+    b = qrow if L.q_start is None else B - 1 - qrow
+    cb = b // L.q_per_seq
+    T = L.lens[b] if L.q_start is None else max(L.q_start[cb], 0) + (b - cb * L.q_per_seq) + 1
+    T = 0 if T < 0 else min(int(T), L.max_seq_len)
+    tb = pl[1] if planned else split * L.chunk
+    te = min(T, pl[2] if planned else tb + L.chunk)
+    final = (not planned) and L.P == 1
+    part = item if planned else b * L.P + split
+    row_lo = (b * H) if final else part * H
+    return b, cb, tb, te, row_lo, row_lo + H
+
+
+def check_latent16(L, max_items=None):
+    """Copies, LDS reads (with the swizzle of the copy undone: each fragment
+    must be the token row and 16-byte chunk the MFMA operand needs), the
+    merge's LDS regions and the output stores of the 16-head bf16 kernel."""
+    H, NBUF = 16, L16_NBUF
+    assert H == L.H and not L.fp8
+    kRing = NBUF * L16_TILE_BYTES
+    kStage, kStat = 2 * 16384, 2 * 16384 + 2 * 8192
+    lanes = np.arange(64)
+    counts = dict(copies=0, stores=0, workgroups=0, lds_reads=0)
+    B = len(L.lens) if L.q_start is None else len(L.q_start) * L.q_per_seq
+    n_wg = len(L.items) if L.items is not None else B * L.P
+    if max_items is not None:
+        n_wg = min(n_wg, max_items)
+    plan = latent16_copy_plan()
+    _need(sorted(i for p in plan for i in p) == list(range(36)), "copies do not cover the tile once")
+    # fragment reads of one tile buffer (the same for every tile)
+    r16, g = lanes & 15, lanes >> 4
+    for u in range(2):
+        kb0 = u * 16 * 1024 + r16 * 1024 + ((g ^ kv_swizzle(r16)) << 4)
+        pb0 = TILE * 1024 + u * 16 * 128 + r16 * 128 + ((g ^ pe_swizzle(r16)) << 4)
+        for s_ in range(18):
+            if s_ < 16:
+                ad = (kb0 ^ ((s_ & 3) << 6)) + 256 * (s_ >> 2)
+                row, slot = ad // 1024, (ad % 1024) // 16
+                _need((row == 16 * u + r16) & ((slot ^ kv_swizzle(row)) == 4 * s_ + g), "K fragment is not its chunk")
+            else:
+                ad = pb0 ^ ((s_ - 16) << 6)
+                off = ad - TILE * 1024
+                row, slot = off // 128, (off % 128) // 16
+                _need((row == 16 * u + r16) & ((slot ^ pe_swizzle(row)) == 4 * (s_ - 16) + g),
+                      "RoPE fragment is not its chunk")
+            _need((ad >= 0) & (ad + 16 <= L16_TILE_BYTES), "K read outside the tile")
+            counts["lds_reads"] += 64
+        rv = 4 * g + ((lanes & 15) >> 2)
+        vb0 = u * 16 * 1024 + rv * 1024 + ((((lanes & 3) >> 1) ^ kv_swizzle(rv)) << 4) + ((lanes & 1) << 3)
+        for cb_ in range(32):
+            ad = vb0 ^ (cb_ << 5)
+            row, slot, half = ad // 1024, (ad % 1024) // 16, (ad % 16) // 8
+            # transposing read: lane l points at token row 4 (l/16) + (l%16)/4,
+            # columns 16 cb + 4 (l%4) .. +3 (chunk 2 cb + (l%4)/2, half (l%4)%2)
+            _need((row == 16 * u + rv) & ((slot ^ kv_swizzle(row)) == 2 * cb_ + ((lanes & 3) >> 1))
+                  & (half == (lanes & 1)), "V fragment is not its chunk")
+            counts["lds_reads"] += 64
+    # merge: exchange, staging and statistics inside the ring
+    for u in range(2):
+        x_other = (1 - u) * 16384 + 16 * lanes
+        _need((x_other + 15 * 1024 + 16 <= kStage), "exchange outside its region")
+        stage_w = kStage + u * 8192 + r16 * 512 + ((((2 * np.arange(16)[:, None] + (g >> 1)) ^ r16) << 4)
+                                                 + ((g & 1) << 3))
+        _need((stage_w >= kStage + u * 8192) & (stage_w + 8 <= kStage + (u + 1) * 8192), "staging write outside")
+        _need(kStat + ((u * H + r16) * 8) + 8 <= kRing, "statistics outside the ring")
+    for item in range(n_wg):
+        counts["workgroups"] += 1
+        b, cb, tb, te, row_lo, row_hi = _range_of(L, item, B, H)
+        if tb >= te:
+            counts["stores"] += H
+            continue
+        n_tiles = -(-(te - tb) // TILE)
+        issued = list(range(min(NBUF - 1, n_tiles)))
+        for it in range(n_tiles):
+            if it + NBUF - 1 < n_tiles:
+                issued.append(it + NBUF - 1)
+        _need(sorted(issued) == list(range(n_tiles)), "tiles not copied exactly once")
+        for tile in issued:
+            t0 = tb + tile * TILE
+            last = min(TILE, te - t0) - 1
+            _need(last >= 0, "tile past the range")
+            if L.block_table is not None:
+                _need(t0 % TILE == 0 and (t0 % L.block_size) + last < L.block_size, "tile crosses a block")
+            dst0 = (tile % NBUF) * L16_TILE_BYTES
+            for copies in plan:
+                for i in copies:
+                    if i < TILE:
+                        tok = t0 + min(i, last)
+                        byte = (16 * lanes) ^ (kv_swizzle(i) << 4)
+                        _need((byte + 16 <= 1024), "latent copy outside the row")
+                        dst = dst0 + i * 1024 + 16 * lanes
+                    else:
+                        pi = i - TILE
+                        r = 8 * pi + (lanes >> 3)
+                        c = (lanes & 7) ^ pe_swizzle(r)
+                        tok = t0 + np.minimum(r, last)
+                        _need((c << 4) + 16 <= 128, "RoPE copy outside the row")
+                        dst = dst0 + TILE * 1024 + pi * 1024 + 16 * lanes
+                    _need((tok >= tb) & (tok < te), "copy outside the range")
+                    if L.num_slots is not None:
+                        sl = L.slot(cb, tok)
+                        _need((sl >= 0) & (sl < L.num_slots), "cache slot outside the allocation")
+                    _need((dst >= dst0) & (dst + 16 <= dst0 + L16_TILE_BYTES) & (dst + 16 <= kRing),
+                          "copy outside its tile")
+                    counts["copies"] += 64
+        # stores: wave u, rows (L >> 5), columns 256 u + 8 (L & 31)
+        for u in range(2):
+            for k in range(8):
+                Lr = 64 * k + lanes
+                row, ch = Lr >> 5, Lr & 31
+                col = 256 * u + ch * 8
+                _need((row_lo + row < row_hi) & (col + 8 <= 512), "o store outside the rows")
+                counts["stores"] += 64
+    return counts
+
+
+# ---------------------------------------------------------------------------
 # 16/32/64-head kernel (decode_latent_kernel<NW, NBUF, PAGED, FP8>)
 # ---------------------------------------------------------------------------
 

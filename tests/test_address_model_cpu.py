@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from mla_absorbed_latent_absorb_amd import binding
-from tests.address_model import Launch, Violation, check_fp8, check_narrow, check_wide
+from tests.address_model import Launch, Violation, check_fp8, check_latent16, check_narrow, check_wide
 
 
 def _paged(lens, bs, seed):
@@ -27,6 +27,8 @@ def _paged(lens, bs, seed):
 def _check(L, max_items=None):
     if L.H == 128:
         return (check_fp8 if L.fp8 else check_wide)(L, max_items)
+    if L.H == 16 and not L.fp8:
+        return check_latent16(L, max_items)
     return check_narrow(L, max_items)
 
 
@@ -98,7 +100,7 @@ def test_prefill_rows(H, L_, starts, P, qg):
     L = Launch(H, lens, S, num_splits=P, seq_stride=S, num_slots=len(starts) * S, q_start=starts, q_per_seq=L_,
                q_group=qg)
     # grouped queries (q_group > 1) run on the 128-row kernel
-    (check_wide if qg > 1 or H == 128 else check_narrow)(L)
+    (check_wide if qg > 1 or H == 128 else _check)(L)
 
 
 def test_checker_catches_a_cache_too_small_for_the_lengths():
@@ -107,6 +109,9 @@ def test_checker_catches_a_cache_too_small_for_the_lengths():
     with pytest.raises(Violation):
         check_wide(L)
     L = Launch(16, [100, 100], 100, seq_stride=100, num_slots=150)
+    with pytest.raises(Violation):
+        check_latent16(L)
+    L = Launch(32, [100, 100], 100, seq_stride=100, num_slots=150)
     with pytest.raises(Violation):
         check_narrow(L)
     L = Launch(128, [100, 100], 100, fp8=True, seq_stride=100, num_slots=150)

@@ -2,12 +2,17 @@
 same values (code * scale, exact in bf16 when the token scales are powers of
 two).
 
-16, 32 and 64 heads: the codes are widened to bf16 exactly, the token scale
+32 and 64 heads: the codes are widened to bf16 exactly, the token scale
 multiplies the fp32 score, and the probability that multiplies the codes in
 P.V carries the scale; with power-of-two scales every one of these products
 is exact, so the E4M3 cache gives bit-identical o_lat / lse (or partials) to
 the bf16 cache, with and without splits, contiguous and paged, and in
 prefill.
+
+16 heads: the same holds for the E4M3 path, but a bf16 cache runs the
+kernel whose two computing waves split each tile by tokens (another
+summation order), so both results are checked against the oracle at the
+bf16 bar and against each other.
 
 128 heads: the stored codes go to fp8 MFMAs and the P.V weights are E4M3
 with a power-of-two scale per (head, 32 tokens), so o differs from the bf16
@@ -25,7 +30,7 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import TOL_FP8, cache_args, f64, rel_err
+from tests.gpu_helpers import TOL_BF16, TOL_FP8, cache_args, f64, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -87,10 +92,33 @@ def test_fp8_pow2_scales_equal_bf16_cache(workload, H, B, T, P):
     r16 = binding.mla_decode_latent(d, c16, q_lat, x.q_pe, x.seq_lens, x.max_seq_len, P)
     torch.cuda.synchronize()
     assert torch.isfinite(r8[0].float()).all()
+    if H == 16:
+        _check_two_orders(x, d, q_lat, r8, r16, P)
+        return
     if H < 128:
         assert torch.equal(r8[0], r16[0]) and torch.equal(r8[1], r16[1])
         return
     _check_fp8_mfma(x, d, q_lat, r8, r16, P)
+
+
+def _check_two_orders(x, d, q_lat, r8, r16, P):
+    """16 heads: E4M3 (codes widened exactly) and bf16 (token-split kernel)
+    both at the bf16 bar of the oracle, and within it of each other."""
+    if P > 1:
+        o8, l8 = binding.mla_combine_splits(d, *r8)
+        o16, l16 = binding.mla_combine_splits(d, *r16)
+    else:
+        (o8, l8), (o16, l16) = r8, r16
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=x.seq_lens.cpu().numpy(), scale=x.scale,
+                                        **cache_args(x))
+    e8, e16 = rel_err(f64(o8), ref_o), rel_err(f64(o16), ref_o)
+    el8 = float(np.max(np.abs(l8.cpu().numpy() - ref_l)))
+    el16 = float(np.max(np.abs(l16.cpu().numpy() - ref_l)))
+    e_b = rel_err(f64(o8), f64(o16))
+    print(f"  vs oracle: E4M3 o_lat {e8:.2e} lse {el8:.2e}, bf16 o_lat {e16:.2e} lse {el16:.2e}; "
+          f"between them {e_b:.2e}")
+    assert max(e8, e16, e_b) <= TOL_BF16 and max(el8, el16) <= 1e-4
 
 
 def _check_fp8_mfma(x, d, q_lat, r8, r16, P):
