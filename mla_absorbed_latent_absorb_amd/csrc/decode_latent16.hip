@@ -108,6 +108,15 @@ void decode_latent16_kernel(DecodeArgs a) {
     const int j = w - kComp;
     const char* kv_base = uniform_ptr(a.kv);
     const char* pe_base = uniform_ptr(a.pe);
+    // Decode reads every cache row once: non-temporal copies (V2-Lite 64 x
+    // 4096: decode 49.3 us against 55.0 us with plain copies).  Query rows of
+    // a prefill re-read their sequence's prefix, which plain copies find in
+    // L2 or the Infinity Cache.
+    const bool nt = a.q_start == nullptr;
+    auto copy16 = [&](const char* src, uint32_t voff, uint32_t dst) {
+      if (nt) dma16<true>(src, voff, dst);
+      else dma16<false>(src, voff, dst);
+    };
     auto copy_tile = [&](int tile, int buf) {
       const int t0 = t_begin + tile * kTile;
       const int last = min(kTile, t_end - t0) - 1;   // rows past the end re-read the last valid row
@@ -128,13 +137,13 @@ void decode_latent16_kernel(DecodeArgs a) {
         const int i = j + NCW * k;
         if (i < kTile) {
           const uint32_t voff = ln16 ^ (kv_swizzle((uint32_t)i) << 4);
-          dma16(uniform_ptr(kv_base + (slot0 + min(i, last)) * a.kv_sb), voff, dst + (uint32_t)(i * kKvRow));
+          copy16(uniform_ptr(kv_base + (slot0 + min(i, last)) * a.kv_sb), voff, dst + (uint32_t)(i * kKvRow));
         } else {
           const int pi = i - kTile;
           const uint32_t r = (uint32_t)(8 * pi) + (ln16 >> 7);
           const uint32_t c = ((ln16 >> 4) & 7u) ^ pe_swizzle(r);
           const uint32_t voff = (uint32_t)min((int)r, last) * (uint32_t)a.pe_sb + (c << 4);
-          dma16(uniform_ptr(pe_base + slot0 * a.pe_sb), voff, dst + (uint32_t)(kPeRegion + pi * 1024));
+          copy16(uniform_ptr(pe_base + slot0 * a.pe_sb), voff, dst + (uint32_t)(kPeRegion + pi * 1024));
         }
       }
     };

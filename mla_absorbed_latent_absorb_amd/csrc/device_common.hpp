@@ -51,35 +51,58 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t byte_off) {
 // vmcnt(0) before every later LDS read; completion is tracked explicitly with
 // wait_vmcnt() followed by a workgroup barrier.  An SALU write of M0 needs one
 // wait state before a load with LDS = 1 reads it (s_nop 0).
+// NT sets the instruction's non-temporal bit, for data read exactly once
+// (the cache tiles): streaming a V3-sized cache into LDS with it ran at 6.5
+// TB/s against 5.75 TB/s without (copies alone, one workgroup per CU).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(sbase)
-               : "memory");
+  if (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
 }
 // The same with the instruction's immediate offset OFF, which the hardware
 // adds to both addresses, and M0 = lds_base + MADD: lane i reads
 // sbase + voff + OFF and writes bytes [lds_base + MADD + OFF + 16*i, +16)
 // (checked on gfx950 with an in-bounds probe).
-template <int OFF, int MADD>
+template <int OFF, int MADD, bool NT = false>
 __device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
   static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
-               :
-               : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF), "n"(MADD)
-               : "memory");
+  if (NT)
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3 nt"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF), "n"(MADD)
+                 : "memory");
+  else
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:%3"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase), "n"(OFF), "n"(MADD)
+                 : "memory");
 }
 
 // The same with 4 bytes per lane (global_load_lds_dword): lane i writes
 // [lds_base + 4*i, +4).
+template <bool NT = false>
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :
-               : "s"(m0), "v"(voff), "s"(sbase)
-               : "memory");
+  if (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 nt"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
 }
 
 // The same with the immediate offset OFF (added to both addresses, as for
