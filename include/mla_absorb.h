@@ -386,23 +386,31 @@ mla_status mla_cache_append(const mla_dims *dims, const mla_cache *cache, const 
  * The uniform rule of mla_decode_latent cuts every sequence at multiples of
  * ceil(max_seq_len / P), so the launch lasts as long as the longest chunk
  * while short sequences leave workgroups idle.  This plan instead cuts each
- * sequence into near-equal runs of whole 32-token tiles, with the fewest
- * tiles per run such that all runs fit the device at once (num_cus times
- * the resident workgroups per CU: 1 at 128 heads, 2 at 64, 4 at 32, 1 at 16)
- * and no run is shorter than max(32, min(256, max_seq_len / 32)) tokens.
- * Every sequence gets at least one item (an empty sequence one item with no
- * tiles); items of a sequence are consecutive.
+ * sequence into near-equal runs of whole 32-token tiles (no run shorter than
+ * max(32, min(256, max_seq_len / 32)) tokens unless the sequence is) and
+ * orders the runs longest first, the launch order of
+ * mla_decode_latent_planned.  It compares tile budgets per run: the fewest
+ * tiles such that every run has a resident workgroup slot (num_cus times the
+ * resident workgroups per CU: 1 at 128 heads, 2 at 64, 4 at 32, 1 at 16), and
+ * budgets that give about 1.1 .. 3 runs per slot, each run then starting on
+ * the first slot of its XCD to free up (workgroup i runs on XCD i % 8); it
+ * keeps the budget with the shortest predicted launch, counting a run as its
+ * tiles plus a fixed cost of 4 tiles.  Every sequence gets at least one item
+ * (an empty sequence one item with no tiles).
  *
  *   host_seq_lens  HOST int32 [batch], clamped to [0, max_seq_len]
- *   capacity       rows of `items` the caller provides (the plan never
- *                  needs more than max(batch, num_cus * 4) rows)
- *   items          HOST int32 [capacity, 3], written: (sequence, first tile,
- *                  tile count) per work item; item i covers tokens
- *                  [32 * first, min(32 * (first + count), seq_lens[seq]))
- *   seq_first      HOST int32 [batch + 1], written: sequence b's items are
- *                  seq_first[b] .. seq_first[b + 1] - 1 (the merge map)
+ *   capacity       rows of `items` the caller provides; budgets whose plan
+ *                  needs more rows are not considered, and batch + 12 *
+ *                  num_cus rows are enough for every budget
+ *   items          HOST int32 [capacity, 4], written in launch order: (sequence,
+ *                  first tile, tile count, partial row) per work item; item i
+ *                  covers tokens [32 * first, min(32 * (first + count),
+ *                  seq_lens[seq])); the partial rows are 0 .. num_items - 1,
+ *                  a sequence's items on consecutive rows in token order
+ *   seq_first      HOST int32 [batch + 1], written: sequence b's partial rows
+ *                  are seq_first[b] .. seq_first[b + 1] - 1 (the merge map)
  *   num_items      written: number of items
- * MLA_ERR_BUFFER if the plan needs more than `capacity` items.
+ * MLA_ERR_BUFFER if even the one-round plan needs more than `capacity` items.
  */
 mla_status mla_plan_decode_splits(const mla_dims *dims, const int32_t *host_seq_lens, int32_t max_seq_len,
                                   int32_t num_cus, int32_t capacity, int32_t *items, int32_t *seq_first,
@@ -410,13 +418,16 @@ mla_status mla_plan_decode_splits(const mla_dims *dims, const int32_t *host_seq_
 
 /*
  * Latent attention (as mla_decode_latent) over the work items of a plan
- * (mla_plan_decode_splits, copied to the device by the caller): one
- * workgroup per item, whose partial (o_i, lse_i) over its token range goes to
- * row i of the partial arrays.
- *   items     device int32 [num_items, 3] (sequence, first 32-token tile,
- *             tile count); an item naming a sequence outside [0, batch), a
- *             negative or out-of-range first tile, or no tiles covers no
- *             tokens (o = 0, lse = -inf); ranges end at seq_lens[seq]
+ * (mla_plan_decode_splits, copied to the device by the caller): workgroup i
+ * runs item i and writes its partial (o, lse) over the item's token range to
+ * the item's partial row.
+ *   items     device int32 [num_items, 4] (sequence, first 32-token tile,
+ *             tile count, partial row); an item naming a sequence outside
+ *             [0, batch), a negative or out-of-range first tile, or no tiles
+ *             covers no tokens (o = 0, lse = -inf); ranges end at
+ *             seq_lens[seq]; an item whose partial row is outside
+ *             [0, num_items) writes nothing.  Two items with one partial row
+ *             race on it (still inside the arrays).
  *   o_part    device bf16 [num_items, H, 512], lse_part device fp32
  *             [num_items, H] (outputs)
  *   other arguments as mla_decode_latent.

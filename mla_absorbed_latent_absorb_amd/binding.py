@@ -274,7 +274,8 @@ def mla_decode_latent_noalloc(d, cache, q_lat, q_pe, seq_lens, max_seq_len, num_
 
 class SplitPlan:
     """A length-aware split plan (mla_plan_decode_splits) on the host and its
-    device copy: items [n, 3] and seq_first [B + 1] int32."""
+    device copy: items [n, 4] (sequence, first tile, tile count, partial row)
+    in launch order and seq_first [B + 1] int32."""
 
     def __init__(self, items, seq_first, device):
         self.items_host, self.seq_first_host = items, seq_first
@@ -289,8 +290,8 @@ def mla_plan_decode_splits(d, host_seq_lens, max_seq_len, num_cus, device=None):
     lens = torch.as_tensor([int(v) for v in host_seq_lens], dtype=torch.int32)
     if lens.numel() != B:
         raise ValueError(f"host_seq_lens must have {B} entries")
-    cap = max(B, 4 * int(num_cus))
-    items = torch.empty((cap, 3), dtype=torch.int32)
+    cap = B + 12 * int(num_cus)  # enough for every budget the planner compares
+    items = torch.empty((cap, 4), dtype=torch.int32)
     first = torch.empty((B + 1,), dtype=torch.int32)
     n = ctypes.c_int32(0)
     _check(load().mla_plan_decode_splits(ctypes.byref(d), ctypes.c_void_p(lens.data_ptr()), int(max_seq_len),
@@ -311,7 +312,7 @@ def mla_decode_latent_planned(d, cache, q_lat, q_pe, seq_lens, max_seq_len, plan
     _expect(q_lat, "q_lat", torch.bfloat16, (B, H, d.kv_lora_rank))
     _expect(q_pe, "q_pe", torch.bfloat16, (B, H, d.qk_rope_head_dim), dev)
     _expect(seq_lens, "seq_lens", torch.int32, (B,), dev)
-    _expect(plan.items, "plan.items", torch.int32, (n, 3), dev)
+    _expect(plan.items, "plan.items", torch.int32, (n, 4), dev)
     if o_part is None:
         o_part = torch.empty((n, H, d.kv_lora_rank), dtype=torch.bfloat16, device=dev)
     if lse_part is None:

@@ -193,11 +193,13 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
   const int w = wave_id();
   const int li = lane & 31;   // head 32w + li
   const int lg = lane >> 5;   // lane half
-  // decode: a sequence's splits share an XCD (and its L2 copy of the
-  // queries); prefill rows go round-robin over the XCDs, longest first
-  const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // uniform splits: a sequence's splits share an XCD (and its L2 copy of the
+  // queries); planned decode: workgroup i runs item i, in the order the plan
+  // gives; prefill rows go round-robin over the XCDs, longest first
   const bool planned = a.items != nullptr;
-  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len) : PlanItem{0, 0, 0};
+  const int item = planned || a.q_start != nullptr ? (int)blockIdx.x : xcd_grouped_index(blockIdx.x, gridDim.x);
+  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len, a.num_items) : PlanItem{0, 0, 0, 0};
+  if (pl.slot < 0) return;  // no partial row to write
   const int qrow = planned ? pl.seq : item / a.num_splits;
   const int split = planned ? item : item - qrow * a.num_splits;
   const int b = a.q_start == nullptr ? qrow : a.batch - 1 - qrow;  // query row
@@ -207,7 +209,7 @@ void decode_latent_fp8_kernel(DecodeArgs a) {
   const int t_begin = planned ? pl.t_begin : split * a.chunk;
   const int t_end = min(T, planned ? pl.t_end : t_begin + a.chunk);
   const bool final_out = !planned && a.num_splits == 1;
-  const size_t part = planned ? (size_t)item : (size_t)b * a.num_splits + split;
+  const size_t part = planned ? (size_t)pl.slot : (size_t)b * a.num_splits + split;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   uint16_t* const out_rows = final_out ? a.o_lat + (size_t)b * H * kDc : a.o_part + part * H * kDc;
   float* const lse_out = final_out ? a.lse + (size_t)b * H : a.lse_part + part * H;

@@ -153,15 +153,17 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   // P.V / output layout (32x32 tiles): head 32 n + h32, columns 8 (j/4) + 4 g2 + j%4
   const int h32 = lane & 31;
   const int g2 = lane >> 5;
-  // decode: a sequence's splits share an XCD (and its L2 copy of the
-  // queries); prefill rows go round-robin over the XCDs, longest first
-  const int item = a.q_start == nullptr ? xcd_grouped_index(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  // uniform splits: a sequence's splits share an XCD (and its L2 copy of the
+  // queries); planned decode: workgroup i runs item i, in the order the plan
+  // gives; prefill rows go round-robin over the XCDs, longest first
+  const bool planned = a.items != nullptr;
+  const int item = planned || a.q_start != nullptr ? (int)blockIdx.x : xcd_grouped_index(blockIdx.x, gridDim.x);
   // query row: its queries and outputs.  Prefill rows run last query first:
   // the longest causal prefixes start earliest, so the launch ends balanced.
-  // A planned decode reads its sequence and token range from the plan and
-  // writes the partial of its item.
-  const bool planned = a.items != nullptr;
-  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len) : PlanItem{0, 0, 0};
+  // A planned decode reads its sequence, token range and partial row from
+  // the plan.
+  const PlanItem pl = planned ? plan_item(a.items, item, a.batch, a.max_seq_len, a.num_items) : PlanItem{0, 0, 0, 0};
+  if (pl.slot < 0) return;  // no partial row to write
   const int qrow = planned ? pl.seq : item / a.num_splits;
   const int split = planned ? item : item - qrow * a.num_splits;
   // Workgroup rows: decode, one sequence (128 heads); prefill, one query (128
@@ -196,7 +198,7 @@ void decode_latent_wide_kernel(DecodeArgs a) {
   }
   const bool final_out = !planned && a.num_splits == 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const size_t part = planned ? (size_t)item : (size_t)b * a.num_splits + split;  // partial slot
+  const size_t part = planned ? (size_t)pl.slot : (size_t)b * a.num_splits + split;  // partial slot
   uint16_t* const out_rows = final_out ? a.o_lat + row0 * Hq * kDc : a.o_part + part * Hq * kDc;
   float* const lse_out = final_out ? a.lse + row0 * Hq : a.lse_part + part * Hq;
 

@@ -204,20 +204,25 @@ __device__ __forceinline__ int32_t scalar_load(const int32_t* p, size_t i) {
   return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p))[i];
 }
 
-// Work item of a planned decode: (sequence, first 32-token tile, tile count).
-// A malformed item (sequence outside [0, batch), negative tile index, no
-// tiles) covers no tokens; ranges are clamped to max_tiles.
+// Work item of a planned decode: (sequence, first 32-token tile, tile count,
+// partial row).  Workgroup i of the launch runs item i and writes partial row
+// `slot`.  A malformed item (sequence outside [0, batch), negative tile index,
+// no tiles) covers no tokens; ranges are clamped to max_tiles; an item whose
+// partial row lies outside [0, num_items) writes nothing.
 struct PlanItem {
   int seq;       // valid sequence (0 for a malformed item)
   int t_begin;   // first token
   int t_end;     // one past the last token (before clamping to the sequence length)
+  int slot;      // partial row, or -1: write nothing
 };
-__device__ __forceinline__ PlanItem plan_item(const int32_t* items, int item, int batch, int max_seq_len) {
-  const int s = scalar_load(items, 3 * (size_t)item);
-  const int f = scalar_load(items, 3 * (size_t)item + 1);
-  const int n = scalar_load(items, 3 * (size_t)item + 2);
+__device__ __forceinline__ PlanItem plan_item(const int32_t* items, int item, int batch, int max_seq_len,
+                                              int num_items) {
+  const int s = scalar_load(items, 4 * (size_t)item);
+  const int f = scalar_load(items, 4 * (size_t)item + 1);
+  const int n = scalar_load(items, 4 * (size_t)item + 2);
+  const int slot = scalar_load(items, 4 * (size_t)item + 3);
   const int max_tiles = (max_seq_len + 31) / 32;
-  PlanItem p{0, 0, 0};
+  PlanItem p{0, 0, 0, (slot >= 0 && slot < num_items) ? slot : -1};
   if (s >= 0 && s < batch && f >= 0 && f < max_tiles && n >= 1) {
     p.seq = s;
     p.t_begin = 32 * f;

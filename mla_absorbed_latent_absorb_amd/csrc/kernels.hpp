@@ -27,8 +27,8 @@ struct DecodeArgs {
   int32_t batch;              // query rows (decode: sequences; prefill: sequences * L)
   int32_t num_heads;
   int32_t num_splits;
-  const int32_t* items;       // planned decode: [num_items, 3] (sequence, first 32-token tile,
-                              // tile count) per workgroup, partials per item; null: uniform splits
+  const int32_t* items;       // planned decode: [num_items, 4] (sequence, first 32-token tile,
+                              // tile count, partial row), item i on workgroup i; null: uniform splits
   int32_t num_items;
   int32_t chunk;              // tokens per split, multiple of 32
   int32_t max_seq_len;

@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -566,52 +568,108 @@ mla_status mla_plan_decode_splits(const mla_dims* dims, const int32_t* host_seq_
   if (num_cus < 1) return fail(MLA_ERR_BAD_LENGTH, "num_cus %d < 1 (%s)", num_cus, where);
   const int B = dims->batch;
   // 32-token tiles per sequence (lengths clamped to [0, max_seq_len] as the kernels do)
-  int64_t max_tiles = 0;
-  for (int b = 0; b < B; ++b) {
-    const int64_t t = host_seq_lens[b] < 0 ? 0 : (host_seq_lens[b] > max_seq_len ? max_seq_len : host_seq_lens[b]);
-    max_tiles = std::max<int64_t>(max_tiles, (t + 31) / 32);
-  }
   auto tiles_of = [&](int b) -> int64_t {
     const int64_t t = host_seq_lens[b] < 0 ? 0 : (host_seq_lens[b] > max_seq_len ? max_seq_len : host_seq_lens[b]);
     return (t + 31) / 32;
   };
+  int64_t max_tiles = 0, total_tiles = 0;
+  for (int b = 0; b < B; ++b) {
+    max_tiles = std::max<int64_t>(max_tiles, tiles_of(b));
+    total_tiles += tiles_of(b);
+  }
   auto items_for = [&](int64_t per) -> int64_t {  // items when no item exceeds `per` tiles
     int64_t n = 0;
     for (int b = 0; b < B; ++b) n += std::max<int64_t>(1, (tiles_of(b) + per - 1) / per);
     return n;
   };
-  // The longest item sets the launch time: the fewest tiles per item such
-  // that every item runs at once (at most one resident workgroup slot each),
-  // and no shorter than the shortest useful split.
-  const int64_t slots = std::max<int64_t>((int64_t)num_cus * wg_per_cu(dims->num_heads), B);
-  int64_t lo = std::max<int64_t>(1, (min_split_tokens(max_seq_len) + 31) / 32), hi = std::max<int64_t>(lo, max_tiles);
-  while (lo < hi) {
-    const int64_t mid = lo + (hi - lo) / 2;
-    if (items_for(mid) <= slots) hi = mid;
-    else lo = mid + 1;
-  }
-  const int64_t per = lo;
-  const int64_t total = items_for(per);
-  if (total > capacity)
-    return fail(MLA_ERR_BUFFER, "the plan has %lld items, above capacity %d (%s)", (long long)total, capacity, where);
-  // each sequence's tiles in near-equal consecutive items (sizes differ by at most one tile)
-  int32_t k = 0;
-  for (int b = 0; b < B; ++b) {
-    seq_first[b] = k;
-    const int64_t tiles = tiles_of(b);
-    const int64_t n = std::max<int64_t>(1, (tiles + per - 1) / per);
-    int64_t first = 0;
-    for (int64_t i = 0; i < n; ++i) {
-      const int64_t cnt = tiles / n + (i < tiles % n ? 1 : 0);
-      items[3 * k] = b;
-      items[3 * k + 1] = (int32_t)first;
-      items[3 * k + 2] = (int32_t)cnt;
-      first += cnt;
-      ++k;
+  // Resident workgroup slots; a budget below the shortest useful split is never used.
+  const int64_t slots = std::max<int64_t>((int64_t)num_cus * wg_per_cu(dims->num_heads), 1);
+  const int64_t lo = std::max<int64_t>(1, (min_split_tokens(max_seq_len) + 31) / 32);
+  // One round: the fewest tiles per item such that every item has a slot.
+  int64_t one_round;
+  {
+    int64_t l = lo, h = std::max<int64_t>(lo, max_tiles);
+    const int64_t cap = std::max<int64_t>(slots, B);
+    while (l < h) {
+      const int64_t mid = l + (h - l) / 2;
+      if (items_for(mid) <= cap) h = mid;
+      else l = mid + 1;
     }
+    one_round = l;
   }
-  seq_first[B] = k;
-  *num_items = k;
+  // Items of a budget: each sequence's tiles in near-equal consecutive items
+  // (sizes differ by at most one tile), partial rows in sequence order.
+  struct Item {
+    int32_t seq, first, count, slot;
+  };
+  std::vector<Item> cand, best;
+  auto build = [&](int64_t per, std::vector<Item>& out) {
+    out.clear();
+    int32_t k = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t tiles = tiles_of(b);
+      const int64_t n = std::max<int64_t>(1, (tiles + per - 1) / per);
+      int64_t first = 0;
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t cnt = tiles / n + (i < tiles % n ? 1 : 0);
+        out.push_back({b, (int32_t)first, (int32_t)cnt, k++});
+        first += cnt;
+      }
+    }
+    // launch order: longest first (ties in sequence order)
+    std::stable_sort(out.begin(), out.end(), [](const Item& x, const Item& y) { return x.count > y.count; });
+  };
+  // Predicted launch time of an item order, in tiles: workgroup i goes to XCD
+  // i % 8, and each XCD starts its next item on the first of its slots to
+  // free up; an item costs its tiles plus a fixed kItemCost (prologue,
+  // epilogue, partial row).
+  constexpr int64_t kItemCost = 4;
+  std::vector<int64_t> heap;
+  auto makespan = [&](const std::vector<Item>& order) -> int64_t {
+    const int64_t groups = slots % 8 == 0 ? 8 : 1;
+    const int64_t per_group = slots / groups;
+    int64_t worst = 0;
+    for (int64_t x = 0; x < groups; ++x) {
+      heap.assign((size_t)per_group, 0);  // all zero: a valid min-heap
+      for (size_t i = (size_t)x; i < order.size(); i += (size_t)groups) {
+        std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+        heap.back() += kItemCost + order[i].count;
+        std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+      }
+      worst = std::max(worst, *std::max_element(heap.begin(), heap.end()));
+    }
+    return worst;
+  };
+  // Candidate budgets: the one-round budget and ~m items per slot on average
+  // for m = 1.1 .. 3.0; the lowest predicted time wins (ties: fewer items).
+  int64_t best_time = -1;
+  auto consider = [&](int64_t per) {
+    per = std::max(lo, std::min(per, std::max<int64_t>(lo, max_tiles)));
+    if (items_for(per) > capacity) return;
+    build(per, cand);
+    const int64_t t = makespan(cand);
+    if (best_time < 0 || t < best_time || (t == best_time && cand.size() < best.size())) {
+      best_time = t;
+      best.swap(cand);
+    }
+  };
+  consider(one_round);
+  for (int m10 = 11; m10 <= 30; ++m10) consider((10 * total_tiles + slots * m10 - 1) / (slots * m10));
+  if (best_time < 0)
+    return fail(MLA_ERR_BUFFER, "the plan has %lld items, above capacity %d (%s)", (long long)items_for(one_round),
+                capacity, where);
+  // merge map: sequence b's partial rows are seq_first[b] .. seq_first[b + 1] - 1
+  std::vector<int32_t> count_of(B, 0);
+  for (const Item& it : best) ++count_of[it.seq];
+  seq_first[0] = 0;
+  for (int b = 0; b < B; ++b) seq_first[b + 1] = seq_first[b] + count_of[b];
+  for (size_t i = 0; i < best.size(); ++i) {
+    items[4 * i] = best[i].seq;
+    items[4 * i + 1] = best[i].first;
+    items[4 * i + 2] = best[i].count;
+    items[4 * i + 3] = best[i].slot;
+  }
+  *num_items = (int32_t)best.size();
   return ok();
 }
 

@@ -46,7 +46,7 @@ class Launch:
     lens: device lengths per sequence (clamped like the kernels do);
     kv_sb / pe_sb: bytes between slots; seq_stride (contiguous) or
     block_table [B, max_blocks] + block_size (paged); num_slots: slots the
-    cache allocation holds; items: planned (seq, first_tile, count) rows or
+    cache allocation holds; items: planned (seq, first_tile, count, partial row) rows or
     None; q_start / q_per_seq / q_group: prefill.
     """
 
@@ -130,7 +130,9 @@ def wide_items(L):
     for item in range(n_wg):
         planned = L.items is not None
         if planned:
-            s, f, n = L.items[item]
+            s, f, n, slot = L.items[item]
+            if not 0 <= slot < len(L.items):
+                continue  # no partial row: the workgroup returns at once
             ok = 0 <= s < len(L.lens) and 0 <= f < max_tiles and n >= 1
             pl = (s, 32 * f, 32 * (f + min(n, max_tiles - f))) if ok else (0, 0, 0)
             qrow, split = pl[0], item
@@ -152,7 +154,7 @@ def wide_items(L):
         t_begin = pl[1] if planned else split * L.chunk
         t_end = min(T, pl[2] if planned else t_begin + L.chunk)
         final = (not planned) and L.P == 1
-        part = item if planned else b * L.P + split
+        part = slot if planned else b * L.P + split
         out.append(dict(item=item, b=b, cb=cb, row0=row0, nq=nq, t_begin=t_begin, t_end=t_end, part=part,
                         final=final, rot=(split * 2) & 15, T=T))
     return out
@@ -450,7 +452,9 @@ def _range_of(L, item, B, H):
     max_tiles = -(-L.max_seq_len // 32)
     planned = L.items is not None
     if planned:
-        s, f, n = L.items[item]
+        s, f, n, slot = L.items[item]
+        if not 0 <= slot < len(L.items):
+            return None  # no partial row: the workgroup returns at once
         ok = 0 <= s < len(L.lens) and 0 <= f < max_tiles and n >= 1
         pl = (s, 32 * f, 32 * (f + min(n, max_tiles - f))) if ok else (0, 0, 0)
         qrow, split = pl[0], item
@@ -463,7 +467,7 @@ def _range_of(L, item, B, H):
     tb = pl[1] if planned else split * L.chunk
     te = min(T, pl[2] if planned else tb + L.chunk)
     final = (not planned) and L.P == 1
-    part = item if planned else b * L.P + split
+    part = slot if planned else b * L.P + split
     row_lo = (b * H) if final else part * H
     return b, cb, tb, te, row_lo, row_lo + H
 
@@ -522,7 +526,10 @@ def check_latent16(L, max_items=None):
         _need(kStat + ((u * H + r16) * 8) + 8 <= kRing, "statistics outside the ring")
     for item in range(n_wg):
         counts["workgroups"] += 1
-        b, cb, tb, te, row_lo, row_hi = _range_of(L, item, B, H)
+        r = _range_of(L, item, B, H)
+        if r is None:
+            continue
+        b, cb, tb, te, row_lo, row_hi = r
         if tb >= te:
             counts["stores"] += H
             continue
@@ -624,7 +631,9 @@ def check_narrow(L, max_items=None):
         counts["workgroups"] += 1
         planned = L.items is not None
         if planned:
-            s, f, n = L.items[item]
+            s, f, n, slot = L.items[item]
+            if not 0 <= slot < len(L.items):
+                continue  # no partial row: the workgroup returns at once
             ok = 0 <= s < len(L.lens) and 0 <= f < max_tiles and n >= 1
             pl = (s, 32 * f, 32 * (f + min(n, max_tiles - f))) if ok else (0, 0, 0)
             qrow, split = pl[0], item
@@ -637,7 +646,7 @@ def check_narrow(L, max_items=None):
         tb = pl[1] if planned else split * L.chunk
         te = min(T, pl[2] if planned else tb + L.chunk)
         final = (not planned) and L.P == 1
-        part = item if planned else b * L.P + split
+        part = slot if planned else b * L.P + split
         row_lo = (b * H) if final else part * H
         row_hi = row_lo + H
         if tb >= te:

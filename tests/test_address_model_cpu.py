@@ -87,7 +87,8 @@ def test_paged_block_sizes(bs, H, fp8):
 
 def test_planned_items_including_malformed():
     lens = [200, 200, 200]
-    items = [[0, 0, 7], [-1, 0, 3], [3, 0, 3], [1, -3, 2], [1, 0, 0], [2, 100, 1], [2, 0, 7], [1, 2, 10 ** 6]]
+    items = [[0, 0, 7, 0], [-1, 0, 3, 1], [3, 0, 3, 2], [1, -3, 2, 3], [1, 0, 0, 4], [2, 100, 1, 5], [2, 0, 7, 6],
+             [1, 2, 10 ** 6, 7], [0, 0, 7, -1], [2, 0, 7, 9]]
     for H in (128, 32):
         _check(Launch(H, lens, 200, seq_stride=200, num_slots=600, items=items))
 

@@ -66,12 +66,13 @@ def test_planned_partials_and_merge_vs_oracle(workload, H, B, T, cus):
     q64, qpe64 = f64(q_lat), f64(x.q_pe)
     op, lp = f64(gp.tensor), glp.tensor.cpu().numpy()
     items, first = plan.items_host.numpy(), plan.seq_first_host.numpy()
+    by_row = items[np.argsort(items[:, 3])]  # items in partial-row order
     for b in range(B):
         T_b = int(lens[b])
         slots = oracle.token_slots(b, T_b, args["seq_stride"], args["block_table"], args["block_size"])
         c, k_r = oracle.load_rows(args["kv_codes"], args["pe_codes"], slots, args["dtype"], args["token_scale"])
-        its = items[first[b]:first[b + 1]]
-        bounds = [min(32 * int(f), T_b) for _, f, _ in its] + [T_b]
+        its = by_row[first[b]:first[b + 1]]
+        bounds = [min(32 * int(f), T_b) for _, f, _, _ in its] + [T_b]
         ro, rl = oracle.latent_attention_ranges(q64[b], qpe64[b], c, k_r, x.scale, bounds)
         for i, row in enumerate(range(first[b], first[b + 1])):
             assert rel_err(op[row], ro[i]) <= tol, (b, i)
@@ -80,6 +81,15 @@ def test_planned_partials_and_merge_vs_oracle(workload, H, B, T, cus):
     e_o, e_l = rel_err(f64(go.tensor), ref_o), float(np.max(np.abs(gl.tensor.cpu().numpy() - ref_l)))
     print(f"  {n} items: o_lat {e_o:.2e} lse {e_l:.2e}")
     assert e_o <= tol and e_l <= tol
+    # the partial row comes from the item, not from its launch position: the
+    # same items launched in a shuffled order give the same bits
+    perm = torch.from_numpy(np.random.default_rng(7).permutation(n))
+    shuffled = binding.SplitPlan(plan.items_host[perm].contiguous(), plan.seq_first_host, DEV)
+    op2, lp2 = binding.mla_decode_latent_planned(d, _cache(x), q_lat, x.q_pe, x.seq_lens, x.max_seq_len, shuffled)
+    o2, l2 = binding.mla_combine_splits_planned(d, op2, lp2, shuffled)
+    torch.cuda.synchronize()
+    assert torch.equal(op2, gp.tensor) and torch.equal(lp2, glp.tensor)
+    assert torch.equal(o2, go.tensor) and torch.equal(l2, gl.tensor)
 
 
 def test_planned_equal_lengths_equal_uniform_splits_bitwise():
@@ -132,16 +142,17 @@ def test_planned_full_size_paged_v3_every_sequence():
 @pytest.mark.parametrize("H", [128, 32])
 def test_planned_malformed_items_and_ranges(H):
     """Items naming a sequence outside the batch, a negative or too-large
-    first tile, or no tiles write o = 0, lse = -inf into their own rows; merge
-    ranges that are empty or leave the partials give o = 0, lse = -inf, out = 0;
-    nothing is written outside the outputs."""
+    first tile, or no tiles write o = 0, lse = -inf into their own rows; items
+    whose partial row is outside [0, n) write nothing; merge ranges that are
+    empty or leave the partials give o = 0, lse = -inf, out = 0; nothing is
+    written outside the outputs."""
     announce(f"planned malformed items / ranges H={H}")
     B, T = 3, 200
     x = _inputs("v3_b32_s4096", batch=B, seq_len=T, heads=H)
     q_lat = datagen.random_latent_queries(B, H, 43, device=DEV)
     d = binding.dims(B, H, x.scale)
-    items = torch.tensor([[0, 0, 7], [-1, 0, 3], [B, 0, 3], [1, -3, 2], [1, 0, 0], [2, 100, 1], [2, 0, 7]],
-                         dtype=torch.int32)
+    items = torch.tensor([[0, 0, 7, 0], [-1, 0, 3, 1], [B, 0, 3, 2], [1, -3, 2, 3], [1, 0, 0, 4], [2, 100, 1, 5],
+                          [2, 0, 7, 6], [0, 0, 7, -1], [2, 0, 7, 9]], dtype=torch.int32)
     first = torch.tensor([0, 1, 5, 99], dtype=torch.int32)
     plan = binding.SplitPlan(items, first, DEV)
     n = plan.num_items
@@ -155,6 +166,9 @@ def test_planned_malformed_items_and_ranges(H):
     op, lp = gp.tensor, glp.tensor
     for i in (1, 2, 3, 4, 5):
         assert torch.all(op[i] == 0) and torch.all(torch.isneginf(lp[i])), i
+    # rows 7 and 8 belong to no valid item: still the initial NaN fill
+    for i in (7, 8):
+        assert torch.all(torch.isnan(op[i].float())) and torch.all(torch.isnan(lp[i])), i
     args = cache_args(x)
     ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=np.array([T] * B), scale=x.scale, **args)
     # sequence 0: item 0 covers all 200 tokens
