@@ -7,8 +7,8 @@
 // and o[h] = sum_t softmax_t(s[h,.]) c_t over one split of the sequence.
 //
 // Work decomposition: one workgroup per (sequence, split) and one per CU (the
-// ring of tiles takes most of the LDS); five waves:
-//   - three copy waves issue all 36 wave-wide 1 KiB copies of every tile of 32
+// ring of tiles takes most of the LDS); six waves:
+//   - four copy waves issue all 36 wave-wide 1 KiB copies of every tile of 32
 //     cache rows into a ring of NBUF LDS tiles, NBUF - 1 tiles ahead (a 64-lane
 //     load that misses the cache holds its wave for ~155 cycles, so the waves
 //     that compute do not copy, and two copy waves would spend most of a
@@ -25,7 +25,7 @@
 //     refilled).
 // After the last tile the two states merge (log-sum-exp of the two halves)
 // through LDS; each computing wave normalises and stores 256 of the columns.
-// Five waves on four SIMDs leave a wave at most 256 registers: the 128 O
+// Six waves on four SIMDs leave a wave at most 256 registers: the 128 O
 // accumulators live in ordinary VGPRs (the library compiles this file with
 // VGPR-form MFMAs), next to the 72 of the query block.
 // The running max moves (O and the sum are rescaled by exp2 of the
@@ -333,13 +333,14 @@ void decode_latent16_kernel(DecodeArgs a) {
   }
 }
 
-// Three copy waves and a ring of three tiles (two in flight ahead of the one
-// being computed).  Measured at 64 sequences x 4096 tokens: streaming alone
-// (the computing waves skipping their work) runs at the same rate with two
-// tiles ahead as with three, and the whole kernel ran ~1 us faster with the
-// smaller ring.
+// Four copy waves (nine copies each per tile) and a ring of three tiles (two
+// in flight ahead of the one being computed).  Measured at 64 sequences x
+// 4096 tokens: streaming alone (the computing waves skipping their work) runs
+// at the same rate with two tiles ahead as with three, and the whole kernel
+// ran ~1 us faster with the smaller ring; four copy waves 50.3 us, three
+// 51.2 us, six 50.5 us (same box, alternated).
 hipError_t launch_decode_latent16(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int kNcw = 3, kNbuf = 3;
+  constexpr int kNcw = 4, kNbuf = 3;
   const int grid = a.items != nullptr ? a.num_items : a.batch * a.num_splits;
   const int threads = (kComp + kNcw) * 64;
   if (a.block_table != nullptr) {

@@ -435,7 +435,7 @@ def check_fp8(L, max_items=None):
 # 16-head bf16 kernel (decode_latent16_kernel<NCW, NBUF, PAGED>)
 # ---------------------------------------------------------------------------
 
-L16_NCW = 3       # copy waves
+L16_NCW = 4       # copy waves
 L16_NBUF = 3      # ring of tiles
 L16_TILE_BYTES = 36864
 
