@@ -365,28 +365,37 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine_expand: the split merge and value absorption of one head for 16
-// sequences in one launch: out[b][h][:] = W_UV[h] . merge_i(o_part[b][i][h]).
-// Workgroup = (head h, sequences R bg .. R bg + R - 1), R = 4, 8 or 16 (fewer
-// when batch x heads is small, so the launch still spans the chip), 16 waves
-// in two roles, so that no wave waits for loads it does not need:
-//   - waves w < R / 2 merge sequences R bg + 2 w, + 1 with combine_row_issue /
-//     _finish (the same arithmetic as combine_kernel; both rows' loads are
-//     issued first) into rows of a 16-row bf16 tile in LDS (chunk ^ b % 16),
-//     also stored as o_lat / lse if asked for (tile rows past R are not
-//     written: the MFMA columns they feed are not stored);
+// combine_expand: the split merge and value absorption of one head for up to
+// 32 sequences in one launch: out[b][h][:] = W_UV[h] . merge_i(o_part[b][i][h]).
+// Workgroup = (head h, sequences R bg .. R bg + R - 1), R = 4, 8, 16 or 32
+// (fewer when batch x heads is small, so the launch still spans the chip),
+// 16 waves in two roles, so that no wave waits for loads it does not need:
+//   - waves w < min(8, R / 2) merge sequences R bg + 16 p + 2 w, + 1 (pass p
+//     < R / 16, at least one) with combine_row_issue / _finish (the same
+//     arithmetic as combine_kernel; both rows' loads are issued first) into
+//     rows of a bf16 tile of up to 32 rows in LDS (chunk ^ b % 16), also
+//     stored as o_lat / lse if asked for (tile rows past R are not written:
+//     the MFMA columns they feed are not stored);
 //   - waves 8 .. 15 copy W_UV[h] (128 rows of 1 KiB) direct-to-LDS, 16 rows
 //     each (chunk ^ j % 16).
 //   Then D[j][b] = W . O^T as in expand_v_kernel (wave w < 8: rows 16 w ..
-//   +15, the same MFMA order), so out matches the two-launch path bit for bit.
+//   +15, the same MFMA order per 16 sequences), so out matches the two-launch
+//   path bit for bit.
 // The head's sequence groups are consecutive items on one XCD, which then
-// fetches W_UV[h] once.
+// fetches W_UV[h] once.  With 32 sequences per workgroup each copy of W_UV[h]
+// into LDS serves twice as many sequences (at 128 x 128 rows the copies move
+// 67 MB instead of 134 MB from L2).
 // ---------------------------------------------------------------------------
-constexpr int kCeRows = 16;                  // most sequences per workgroup
+constexpr int kCeRows = 32;                  // most sequences per workgroup
 constexpr int kCeW = kDv * kDc * 2;          // 128 KiB
-constexpr int kCeO = kCeRows * kDc * 2;      // 16 KiB
 
+// RMAX: most sequences per workgroup of the instantiation (16 or 32); the
+// 16-row form keeps its loops at one pass.
+template <int RMAX>
 __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs a) {
+  static_assert(RMAX == 16 || RMAX == 32, "one or two 16-row passes");
+  constexpr int kCeO = RMAX * kDc * 2;  // the merged rows, 1 KiB each
+  static_assert(kCeW + kCeO <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[kCeW + kCeO];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t wl = lds0, ol = lds0 + kCeW;
@@ -398,32 +407,34 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
   const int lane = threadIdx.x & 63;
   const int nl = lane & 15, g = lane >> 4;
 
-  if (2 * w < R) {
-    // rows 2 w, 2 w + 1 (sequences past the batch repeat the last one and
+  if (2 * w < R && w < 8) {
+    // rows 16 p + 2 w, + 1 (sequences past the batch repeat the last one and
     // are not stored)
-    int b[2];
-    SplitRange sr[2];
-    CombineRow row[2];
+    for (int p = 0; p < RMAX / 16 && 16 * p < R; ++p) {
+      int b[2];
+      SplitRange sr[2];
+      CombineRow row[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      b[i] = min(R * bg + 2 * w + i, a.batch - 1);
-      sr[i] = split_range(a.seq_first, a.num_splits, b[i]);
-      row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, sr[i].P, sr[i].first, h, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 2 * w + i;
-      const bool store = R * bg + r < a.batch;
-      float lse;
-      u32x4 o = combine_row_finish(row[i], a.num_heads, sr[i].P, lane, lse);
-      if (!sr[i].valid) {
-        o = u32x4{0u, 0u, 0u, 0u};
-        lse = -INFINITY;
+      for (int i = 0; i < 2; ++i) {
+        b[i] = min(R * bg + 16 * p + 2 * w + i, a.batch - 1);
+        sr[i] = split_range(a.seq_first, a.num_splits, b[i]);
+        row[i] = combine_row_issue(a.o_part, a.lse_part, a.num_heads, sr[i].P, sr[i].first, h, lane);
       }
-      lds_write_u32x4(ol + (uint32_t)r * 1024u + (((uint32_t)lane ^ ((uint32_t)r & 15u)) << 4), o);
-      if (store && a.o_lat != nullptr)
-        *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b[i] * a.num_heads + h) * kDc + lane * 8) = o;
-      if (store && a.lse != nullptr && lane == 0) a.lse[(size_t)b[i] * a.num_heads + h] = lse;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 16 * p + 2 * w + i;
+        const bool store = R * bg + r < a.batch;
+        float lse;
+        u32x4 o = combine_row_finish(row[i], a.num_heads, sr[i].P, lane, lse);
+        if (!sr[i].valid) {
+          o = u32x4{0u, 0u, 0u, 0u};
+          lse = -INFINITY;
+        }
+        lds_write_u32x4(ol + (uint32_t)r * 1024u + (((uint32_t)lane ^ ((uint32_t)r & 15u)) << 4), o);
+        if (store && a.o_lat != nullptr)
+          *reinterpret_cast<u32x4*>(a.o_lat + ((size_t)b[i] * a.num_heads + h) * kDc + lane * 8) = o;
+        if (store && a.lse != nullptr && lane == 0) a.lse[(size_t)b[i] * a.num_heads + h] = lse;
+      }
     }
   } else if (w >= 8) {
     // W_UV[h] rows 16 (w - 8) .. +15: copy k = row k, chunk slot ^ (k % 16)
@@ -441,19 +452,22 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
   if (w >= kDv / 16) return;
 
   const uint32_t jrow = 16 * w + nl;  // A row of this lane
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < RMAX / 16 && 16 * nb < R; ++nb) {
+    const uint32_t brow = 16 * (uint32_t)nb + nl;  // B row (sequence) of this lane
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const uint32_t chunk = (uint32_t)(4 * s + g);
-    const bf16x8 aw = lds_read_b128(wl + jrow * 1024 + ((chunk ^ (jrow & 15u)) << 4));
-    const bf16x8 bo = lds_read_b128(ol + (uint32_t)nl * 1024 + ((chunk ^ ((uint32_t)nl & 15u)) << 4));
-    acc = mfma16(aw, bo, acc);
-  }
-  // D[j = 16 w + 4 g + r][b = 16 bg + nl]: four consecutive output columns
-  const int bo = R * bg + nl;
-  if (nl < R && bo < a.batch) {
-    const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    *reinterpret_cast<u32x2*>(a.out + ((size_t)bo * a.num_heads + h) * kDv + 16 * w + 4 * g) = v;
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t chunk = (uint32_t)(4 * s + g);
+      const bf16x8 aw = lds_read_b128(wl + jrow * 1024 + ((chunk ^ (jrow & 15u)) << 4));
+      const bf16x8 bo = lds_read_b128(ol + brow * 1024 + ((chunk ^ (brow & 15u)) << 4));
+      acc = mfma16(aw, bo, acc);
+    }
+    // D[j = 16 w + 4 g + r][b = R bg + 16 nb + nl]: four consecutive output columns
+    const int bo = R * bg + (int)brow;
+    if ((int)brow < R && bo < a.batch) {
+      const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+      *reinterpret_cast<u32x2*>(a.out + ((size_t)bo * a.num_heads + h) * kDv + 16 * w + 4 * g) = v;
+    }
   }
 }
 
@@ -469,11 +483,16 @@ hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine_expand(const CombineExpandArgs& a_in, hipStream_t stream) {
   CombineExpandArgs a = a_in;
-  // sequences per workgroup: 16 while the grid has >= 256 workgroups, else fewer
+  // sequences per workgroup: the most (up to 32) that keeps the grid at >= 256
+  // workgroups, at least 4
   const int64_t rows_total = (int64_t)a.batch * a.num_heads;
-  a.rows = rows_total >= 256 * kCeRows ? kCeRows : (rows_total >= 256 * 8 ? 8 : 4);
+  a.rows = 4;
+  while (a.rows < kCeRows && rows_total >= 256 * (int64_t)(2 * a.rows)) a.rows *= 2;
   const int groups = (a.batch + a.rows - 1) / a.rows;
-  hipLaunchKernelGGL(combine_expand_kernel, dim3(a.num_heads * groups), dim3(1024), 0, stream, a);
+  if (a.rows > 16)
+    hipLaunchKernelGGL(combine_expand_kernel<32>, dim3(a.num_heads * groups), dim3(1024), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_expand_kernel<16>, dim3(a.num_heads * groups), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
