@@ -23,9 +23,11 @@ def _weights(H, seed):
     return x.w_uv
 
 
-# batch sizes around the 16-sequence workgroup (ragged groups), split counts
-# up to past 64 (the lse re-read path), 16 .. 128 heads
-CASES = [(2, 3, 16), (32, 8, 128), (17, 8, 64), (1, 1, 64), (3, 16, 32), (5, 70, 16), (1, 130, 32), (40, 9, 128)]
+# batch sizes around the 16- and 32-sequence workgroups (ragged groups; 32
+# sequences per workgroup once batch x heads >= 8,192: the last three), split
+# counts up to past 64 (the lse re-read path), 16 .. 128 heads
+CASES = [(2, 3, 16), (32, 8, 128), (17, 8, 64), (1, 1, 64), (3, 16, 32), (5, 70, 16), (1, 130, 32), (40, 9, 128),
+         (64, 4, 128), (70, 5, 128), (100, 3, 128)]
 
 
 @pytest.mark.parametrize("B,P,H", CASES)
