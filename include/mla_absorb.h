@@ -35,8 +35,10 @@
  * --------------------------------
  * - Pointers named "device" are HIP device pointers; the library never
  *   dereferences them on the host.  All device buffers are owned by the
- *   caller, who allocates and frees them; the library allocates nothing,
- *   frees nothing, keeps no state between calls and never synchronises.
+ *   caller, who allocates and frees them; the library allocates and frees
+ *   no device memory, keeps no state between calls and never synchronises
+ *   (only the host planner mla_plan_decode_splits uses temporary host memory
+ *   while it runs).
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   Every kernel is launched asynchronously on it.
  * - bf16 = IEEE bfloat16 stored as uint16; fp8 = OCP FP8 E4M3 ("FN") stored
