@@ -90,19 +90,12 @@ __device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint
 
 // The same with 4 bytes per lane (global_load_lds_dword): lane i writes
 // [lds_base + 4*i, +4).
-template <bool NT = false>
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-  if (NT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 nt"
-                 :
-                 : "s"(m0), "v"(voff), "s"(sbase)
-                 : "memory");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 :
-                 : "s"(m0), "v"(voff), "s"(sbase)
-                 : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory");
 }
 
 // The same with the immediate offset OFF (added to both addresses, as for
