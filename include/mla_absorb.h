@@ -288,7 +288,7 @@ mla_status mla_expand_v(const mla_dims *dims, const void *o_lat, const void *w_u
  *   out    device bf16 [B, H, 128] (output)
  *   o_lat  device bf16 [B, H, 512] (output, may be NULL)
  *   lse    device fp32 [B, H] (output, may be NULL)
- * One workgroup per (head, up to 16 sequences): W_UV[h] and the partial rows
+ * One workgroup per (head, up to 32 sequences): W_UV[h] and the partial rows
  * are read once, and o_lat need not make a round trip through memory.
  */
 mla_status mla_combine_expand_v(const mla_dims *dims, const void *o_part, const float *lse_part,
