@@ -12,7 +12,9 @@ HBM (the working set exceeds the 256 MB Infinity Cache).
 Prints one JSON line:
   value           latent-KV GB/s of the headline workload (V3, B=32, 4096
                   tokens) over the whole step: W untimed steps, then the K
-                  steps as one HIP graph replay between two synchronisations
+                  steps as one HIP graph replay between two synchronisations,
+                  its GPU time from HIP events at the replay's ends (the host
+                  clock around it: ms_per_step_host_clock)
   step_us_stats   per-step time over 7 more replays, each timed with HIP
                   events at its ends: median / p10 / p90
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
@@ -603,10 +605,21 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
             run(i)
     graph.replay()  # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
+    # The timed region: exactly the K steps, one graph replay between two
+    # synchronisations.  Its GPU time comes from HIP events recorded at the
+    # replay's two ends on the launch stream; the host clock around the same
+    # region also holds one graph launch and one synchronisation and is
+    # reported beside it.  (A replay of few steps costs more per step than a
+    # long one on the GPU too: ~66 us per V3 step at K = 20 against ~62 us at
+    # K = 200.)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e_start.record()
     graph.replay()
+    e_end.record()
     torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / steps
+    t_host = (time.perf_counter() - t0) / steps
+    t_step = e_start.elapsed_time(e_end) * 1e-3 / steps
     # repeated replays: per-step time from HIP events at each replay's ends
     per_step = []
     n_rep = 7
@@ -687,6 +700,7 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
                           "max(cache bytes / 8 TB/s, core FLOPs / 2.5 PFLOP/s bf16 MFMA)" +
                           ("; E4M3 codes enter bf16 MFMAs exactly" if fp8 else ""))},
         "headline_step_us": round(t_step * 1e6, 3),
+        "headline_step_us_host_clock": round(t_host * 1e6, 3),
         "step_us": _stats(per_step),
         "step_eager_us": round(t_eager * 1e6, 3),
         "decode_us": _stats(dec),
@@ -698,7 +712,7 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
         obj["sclk"] = sclk
     if x0.max_seq_len <= FUSED_MAX_CONTEXT:
         obj["fused_step"] = bench_fused_step(x0, d, dev, steps)
-    out = dict(obj=obj, t_step=t_step, t_dec=t_dec, x0=x0, d=d, P=P, R=R, cache_bytes=cache_bytes, flops=flops,
+    out = dict(obj=obj, t_step=t_step, t_host=t_host, t_dec=t_dec, x0=x0, d=d, P=P, R=R, cache_bytes=cache_bytes, flops=flops,
                t_eager=t_eager, steps=steps_objs)
     return out
 
@@ -792,10 +806,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
+        "ms_per_step_host_clock": round(head["t_host"] * 1e3, 5),
         "ms_per_step_eager": round(head["t_eager"] * 1e3, 5),
         "step_timing": "the K steps as one HIP graph replay between two synchronisations (three launches per "
-                       "step: absorb_q, decode_latent, combine_expand_v or expand_v); step_us: 7 more replays "
-                       "timed with HIP events",
+                       "step: absorb_q, decode_latent, combine_expand_v or expand_v), GPU time from HIP events "
+                       "at the replay's ends (ms_per_step_host_clock: the host clock around the same region, "
+                       "which adds one graph launch and one synchronisation); step_us: 7 more replays timed "
+                       "with HIP events",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
