@@ -7,8 +7,9 @@
 // combine_expand: combine, then expand_v, in one launch
 //
 // Both projections are per-head batched GEMMs that are bound by reading the
-// weights once (16 MiB each for 128 heads); two workgroups per head, every
-// operand copied into LDS as whole rows, 16x16x32 bf16 MFMAs.
+// weights once (16 MiB each for 128 heads): absorb_q with eight one-wave
+// workgroups per head, expand_v with two, every operand copied into LDS as
+// whole row segments, 16x16x32 bf16 MFMAs.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -24,49 +25,53 @@ namespace mla {
 constexpr int kProjRows = 32;  // batch rows per chunk
 
 // ---------------------------------------------------------------------------
-// absorb_q: workgroup = (head h, column half ch): q_lat[b][h][256 ch + c].
-//   LDS: W_UK[h][d][256 ch .. +256] as 128 rows of 512 B (chunk ^ 2d % 32),
-//        q_nope[b][h][:] as 32 rows of 256 B (chunk ^ b % 16), and the output
-//        chunk as 32 rows of 512 B (chunk ^ b % 32) for row-wise stores.
-//   D^T[c][b] = W^T . Q^T on 16x16x32 MFMAs; wave w owns columns 64 w .. +63:
-//   A[c][d] via transposing reads of the W rows, B[d][b] from the query rows.
+// absorb_q: workgroup = one wave = (head h, 64-column block cb):
+//   q_lat[b][h][64 cb + c].
+//   LDS: W_UK[h][d][64 cb .. +64] as 128 rows of 128 B, 16-byte chunk c of row
+//        d at slot c ^ 2 ((d / 8) % 4); q_nope[b][h][:] as 32 rows of 256 B
+//        (chunk ^ b % 16); the output block as 32 rows of 128 B (chunk ^ b % 8)
+//        for row-wise stores.
+//   D^T[c][b] = W^T . Q^T on 16x16x32 MFMAs: A[c][d] via transposing reads of
+//   the W rows (one read covers 16 rows x 32 bytes; the four 8-row groups sit
+//   on four different slot pairs, so the read hits every LDS bank twice, no
+//   more), B[d][b] from the query rows.
+// Eight small workgroups per head (16 KiB of W_UK each): with few heads the
+// launch still spans many CUs, and no CU waits for a large slab.  (Two
+// workgroups of 64 KiB per head took 4.3 us at 16 heads.)
 // ---------------------------------------------------------------------------
-constexpr int kAbsCols = 256;                      // output columns per workgroup
-constexpr int kAbsW = kDn * kAbsCols * 2;          // 64 KiB W slab
+constexpr int kAbsCols = 64;                       // output columns per workgroup
+constexpr int kAbsBlocks = kDc / kAbsCols;         // workgroups per head
+constexpr int kAbsW = kDn * kAbsCols * 2;          // 16 KiB W block
 constexpr int kAbsQ = kProjRows * kDn * 2;         // 8 KiB query rows
-constexpr int kAbsOut = kProjRows * kAbsCols * 2;  // 16 KiB output staging
+constexpr int kAbsOut = kProjRows * kAbsCols * 2;  // 4 KiB output staging
 
-__global__ __launch_bounds__(256) void absorb_q_kernel(ProjArgs a) {
+__global__ __launch_bounds__(64) void absorb_q_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kAbsW + kAbsQ + kAbsOut];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t wl = lds0, ql = lds0 + kAbsW, ol = lds0 + kAbsW + kAbsQ;
-  // both halves of a head run on one XCD (its query rows are fetched once)
+  // a head's column blocks run on one XCD (its query rows are fetched once)
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int h = item >> 1, ch = item & 1;
-  const int w = wave_id();
-  const int nl = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const int h = item / kAbsBlocks, cb = item - h * kAbsBlocks;
+  const uint32_t ln = lane_id();
+  const uint32_t nl = ln & 15u, g = ln >> 4;
   const size_t qrow_bytes = (size_t)a.num_heads * kDn * 2;  // stride of q_nope rows
 
-  // W slab: copy k (16 per wave) = rows 2k, 2k+1 (lane l: row 2k + l/32, slot l % 32)
+  // W block: copy k (16) = rows 8k .. 8k+7 (lane l: row 8k + l/8, slot l % 8,
+  // holding chunk slot ^ 2 (k % 4))
   {
-    const uint32_t ln = lane_id();
-    const char* wsrc = reinterpret_cast<const char*>(a.w + (size_t)h * kDn * kDc + ch * kAbsCols);
+    const char* wsrc = reinterpret_cast<const char*>(a.w + (size_t)h * kDn * kDc + cb * kAbsCols);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = 16 * w + i;
-      const uint32_t row = 2 * k + (ln >> 5);
-      const uint32_t src = (ln & 31u) ^ ((2u * row) & 30u);
-      dma16(uniform_ptr(wsrc + (size_t)(2 * k) * (kDc * 2)), (ln >> 5) * (kDc * 2) + src * 16, wl + k * 1024);
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t src = (ln & 7u) ^ (2u * ((uint32_t)k & 3u));
+      dma16(uniform_ptr(wsrc + (size_t)(8 * k) * (kDc * 2)), (ln >> 3) * (kDc * 2) + src * 16, wl + k * 1024);
     }
   }
-  // query rows b0 .. b0+31: copy k (2 per wave) = rows 4k .. 4k+3 (lane l:
-  // row 4k + l/16, slot l % 16); rows past the batch re-read the last one
+  // query rows b0 .. b0+31: copy k (8) = rows 4k .. 4k+3 (lane l: row 4k +
+  // l/16, slot l % 16); rows past the batch re-read the last one
   auto stage_q = [&](int b0) {
-    const uint32_t ln = lane_id();
     const char* qbase = reinterpret_cast<const char*>(a.x + (size_t)h * kDn);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k = 2 * w + i;
+    for (int k = 0; k < 8; ++k) {
       const int r0 = min(b0 + 4 * k, a.batch - 1);
       const uint32_t row = 4 * k + (ln >> 4);
       const int br = min(b0 + (int)row, a.batch - 1);
@@ -79,27 +84,23 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(ProjArgs a) {
   wait_vmcnt<0>();
   barrier();
 
-  // A fragments (column tile ct = 64 w + 16 ct, k-step s): lane (nl, g) gets
-  // W[32 s + 8 g + i][c = 64 w + 16 ct + nl], two transposing reads of 4 rows
+  // A fragments (column tile ct = 16 ct .. +15, k-step s): lane (nl, g) gets
+  // W[32 s + 8 g + i][c = 16 ct + nl], two transposing reads of 4 rows
   bf16x8 af[4][4];
-  {
-    const uint32_t ln = lane_id();
-    const uint32_t lnl = ln & 15u, lg = ln >> 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const uint32_t colb = (uint32_t)(64 * w + 16 * ct) * 2 + (lnl & 3u) * 8;  // byte in the 512 B row
-        bf16x4 half[2];
+    for (int ct = 0; ct < 4; ++ct) {
+      const uint32_t colb = (uint32_t)(32 * ct) + (nl & 3u) * 8;  // byte in the 128 B row
+      bf16x4 half[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t row = 32 * s + 8 * lg + 4 * e + (lnl >> 2);
-          const uint32_t chunk = (colb >> 4) ^ ((2u * row) & 30u);
-          half[e] = lds_read_tr16(wl + row * 512 + (chunk << 4) + (colb & 15u));
-        }
-        af[ct][s] = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t row = 32 * s + 8 * g + 4 * e + (nl >> 2);
+        const uint32_t chunk = (colb >> 4) ^ (2u * ((row >> 3) & 3u));
+        half[e] = lds_read_tr16(wl + row * 128 + (chunk << 4) + (colb & 15u));
       }
-  }
+      af[ct][s] = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
 
   for (int b0 = 0; b0 < a.batch; b0 += kProjRows) {
     if (b0 > 0) {
@@ -113,29 +114,29 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(ProjArgs a) {
       bf16x8 bq[4];
       const uint32_t brow = 16 * mb + nl;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bq[s] = lds_read_b128(ql + brow * 256 + (((uint32_t)(4 * s + g) ^ (brow & 15u)) << 4));
+      for (int s = 0; s < 4; ++s) bq[s] = lds_read_b128(ql + brow * 256 + (((uint32_t)(4 * s) + g) ^ (brow & 15u)) * 16);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma16(af[ct][s], bq[s], acc);
-        // D^T[c = 64 w + 16 ct + 4 g + j][b = 16 mb + nl] -> staging row b, 8 bytes
-        const uint32_t c = 64 * w + 16 * ct + 4 * g;
-        const uint32_t chunk = (c >> 3) ^ (brow & 31u);
+        // D^T[c = 16 ct + 4 g + j][b = 16 mb + nl] -> staging row b, 8 bytes
+        const uint32_t c = 16 * ct + 4 * g;
+        const uint32_t chunk = (c >> 3) ^ (brow & 7u);
         const u32x2 v = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-        lds_write_b64(ol + brow * 512 + (chunk << 4) + (c & 7u) * 2, v);
+        lds_write_b64(ol + brow * 128 + (chunk << 4) + (c & 7u) * 2, v);
       }
     }
     barrier();
-    // 32 rows x 32 chunks of 16 B -> q_lat rows (512 contiguous bytes per row)
+    // 32 rows x 8 chunks of 16 B -> q_lat row segments (128 contiguous bytes per row)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t idx = (uint32_t)(k * 256) + threadIdx.x;
-      const uint32_t row = idx >> 5, chunk = idx & 31u;
+      const uint32_t idx = (uint32_t)(k * 64) + ln;
+      const uint32_t row = idx >> 3, chunk = idx & 7u;
       const int b = b0 + (int)row;
-      const u32x4 v = lds_read_u32x4(ol + row * 512 + ((chunk ^ (row & 31u)) << 4));
+      const u32x4 v = lds_read_u32x4(ol + row * 128 + ((chunk ^ (row & 7u)) << 4));
       if (b < a.batch)
-        *reinterpret_cast<u32x4*>(a.y + ((size_t)b * a.num_heads + h) * kDc + ch * kAbsCols + chunk * 8) = v;
+        *reinterpret_cast<u32x4*>(a.y + ((size_t)b * a.num_heads + h) * kDc + cb * kAbsCols + chunk * 8) = v;
     }
     barrier();  // the query rows and the staging area are reused
   }
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
 }
 
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(a.num_heads * (kDc / kAbsCols)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(a.num_heads * kAbsBlocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
