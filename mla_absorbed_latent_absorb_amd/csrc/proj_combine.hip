@@ -7,9 +7,10 @@
 // combine_expand: combine, then expand_v, in one launch
 //
 // Both projections are per-head batched GEMMs that are bound by reading the
-// weights once (16 MiB each for 128 heads): absorb_q with eight one-wave
-// workgroups per head, expand_v with two, every operand copied into LDS as
-// whole row segments, 16x16x32 bf16 MFMAs.
+// weights once (16 MiB each for 128 heads): absorb_q with one wave per 64
+// output columns (workgroups of one or four waves), expand_v with two
+// workgroups per head, every operand copied into LDS as whole row segments,
+// 16x16x32 bf16 MFMAs.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -25,39 +26,48 @@ namespace mla {
 constexpr int kProjRows = 32;  // batch rows per chunk
 
 // ---------------------------------------------------------------------------
-// absorb_q: workgroup = one wave = (head h, 64-column block cb):
-//   q_lat[b][h][64 cb + c].
-//   LDS: W_UK[h][d][64 cb .. +64] as 128 rows of 128 B, 16-byte chunk c of row
-//        d at slot c ^ 2 ((d / 8) % 4); q_nope[b][h][:] as 32 rows of 256 B
-//        (chunk ^ b % 16); the output block as 32 rows of 128 B (chunk ^ b % 8)
-//        for row-wise stores.
+// absorb_q: wave = (head h, 64-column block cb): q_lat[b][h][64 cb + c];
+// workgroup = NW waves on consecutive blocks of one head, sharing its query
+// rows.
+//   LDS per wave: W_UK[h][d][64 cb .. +64] as 128 rows of 128 B, 16-byte chunk
+//        c of row d at slot c ^ 2 ((d / 8) % 4), and its output block as 32
+//        rows of 128 B (chunk ^ b % 8) for row-wise stores; shared:
+//        q_nope[b][h][:] as 32 rows of 256 B (chunk ^ b % 16).
 //   D^T[c][b] = W^T . Q^T on 16x16x32 MFMAs: A[c][d] via transposing reads of
 //   the W rows (one read covers 16 rows x 32 bytes; the four 8-row groups sit
 //   on four different slot pairs, so the read hits every LDS bank twice, no
 //   more), B[d][b] from the query rows.
-// Eight small workgroups per head (16 KiB of W_UK each): with few heads the
-// launch still spans many CUs, and no CU waits for a large slab.  (Two
-// workgroups of 64 KiB per head took 4.3 us at 16 heads.)
+// With few heads, one-wave workgroups (8 per head, 16 KiB of W_UK each) spread
+// the launch over more CUs: at 16 heads the step is 0.5 us shorter than with
+// two workgroups of 64 KiB per head; with 64 or more heads the launch already
+// spans the chip and four-wave workgroups (2 per head) measured 0.5 us
+// shorter per V3 step than one-wave ones.
 // ---------------------------------------------------------------------------
-constexpr int kAbsCols = 64;                       // output columns per workgroup
-constexpr int kAbsBlocks = kDc / kAbsCols;         // workgroups per head
-constexpr int kAbsW = kDn * kAbsCols * 2;          // 16 KiB W block
+constexpr int kAbsCols = 64;                       // output columns per wave
+constexpr int kAbsBlocks = kDc / kAbsCols;         // waves per head
+constexpr int kAbsW = kDn * kAbsCols * 2;          // 16 KiB W block per wave
 constexpr int kAbsQ = kProjRows * kDn * 2;         // 8 KiB query rows
-constexpr int kAbsOut = kProjRows * kAbsCols * 2;  // 4 KiB output staging
+constexpr int kAbsOut = kProjRows * kAbsCols * 2;  // 4 KiB output staging per wave
 
-__global__ __launch_bounds__(64) void absorb_q_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kAbsW + kAbsQ + kAbsOut];
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void absorb_q_kernel(ProjArgs a) {
+  static_assert(kAbsBlocks % NW == 0 && 8 % NW == 0, "blocks and query copies split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[NW * kAbsW + kAbsQ + NW * kAbsOut];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t wl = lds0, ql = lds0 + kAbsW, ol = lds0 + kAbsW + kAbsQ;
-  // a head's column blocks run on one XCD (its query rows are fetched once)
+  const int w = wave_id();
+  const uint32_t wl = lds0 + (uint32_t)w * kAbsW;
+  const uint32_t ql = lds0 + NW * kAbsW;
+  const uint32_t ol = ql + kAbsQ + (uint32_t)w * kAbsOut;
+  // a head's workgroups run on one XCD (its query rows are fetched once)
+  constexpr int kGroups = kAbsBlocks / NW;  // workgroups per head
   const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int h = item / kAbsBlocks, cb = item - h * kAbsBlocks;
+  const int h = item / kGroups, cb = (item - h * kGroups) * NW + w;
   const uint32_t ln = lane_id();
   const uint32_t nl = ln & 15u, g = ln >> 4;
   const size_t qrow_bytes = (size_t)a.num_heads * kDn * 2;  // stride of q_nope rows
 
-  // W block: copy k (16) = rows 8k .. 8k+7 (lane l: row 8k + l/8, slot l % 8,
-  // holding chunk slot ^ 2 (k % 4))
+  // W block of this wave: copy k (16) = rows 8k .. 8k+7 (lane l: row 8k +
+  // l/8, slot l % 8, holding chunk slot ^ 2 (k % 4))
   {
     const char* wsrc = reinterpret_cast<const char*>(a.w + (size_t)h * kDn * kDc + cb * kAbsCols);
 #pragma unroll
@@ -66,12 +76,14 @@ __global__ __launch_bounds__(64) void absorb_q_kernel(ProjArgs a) {
       dma16(uniform_ptr(wsrc + (size_t)(8 * k) * (kDc * 2)), (ln >> 3) * (kDc * 2) + src * 16, wl + k * 1024);
     }
   }
-  // query rows b0 .. b0+31: copy k (8) = rows 4k .. 4k+3 (lane l: row 4k +
-  // l/16, slot l % 16); rows past the batch re-read the last one
+  // query rows b0 .. b0+31: copy k (8 per workgroup, k % NW = w) = rows 4k ..
+  // 4k+3 (lane l: row 4k + l/16, slot l % 16); rows past the batch re-read
+  // the last one
   auto stage_q = [&](int b0) {
     const char* qbase = reinterpret_cast<const char*>(a.x + (size_t)h * kDn);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int i = 0; i < 8 / NW; ++i) {
+      const int k = NW * i + w;
       const int r0 = min(b0 + 4 * k, a.batch - 1);
       const uint32_t row = 4 * k + (ln >> 4);
       const int br = min(b0 + (int)row, a.batch - 1);
@@ -84,8 +96,8 @@ __global__ __launch_bounds__(64) void absorb_q_kernel(ProjArgs a) {
   wait_vmcnt<0>();
   barrier();
 
-  // A fragments (column tile ct = 16 ct .. +15, k-step s): lane (nl, g) gets
-  // W[32 s + 8 g + i][c = 16 ct + nl], two transposing reads of 4 rows
+  // A fragments (column tile ct = 16 ct .. +15 of the block, k-step s): lane
+  // (nl, g) gets W[32 s + 8 g + i][c = 16 ct + nl], two transposing reads of 4 rows
   bf16x8 af[4][4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -473,7 +485,10 @@ __global__ __launch_bounds__(1024) void combine_expand_kernel(CombineExpandArgs 
 }
 
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(a.num_heads * kAbsBlocks), dim3(64), 0, stream, a);
+  if (a.num_heads >= 64)
+    hipLaunchKernelGGL(absorb_q_kernel<4>, dim3(a.num_heads * (kAbsBlocks / 4)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(absorb_q_kernel<1>, dim3(a.num_heads * kAbsBlocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
