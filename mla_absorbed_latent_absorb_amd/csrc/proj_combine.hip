@@ -7,10 +7,10 @@
 // combine_expand: combine, then expand_v, in one launch
 //
 // Both projections are per-head batched GEMMs that are bound by reading the
-// weights once (16 MiB each for 128 heads): absorb_q with one wave per 64
-// output columns (workgroups of one or four waves), expand_v with two
-// workgroups per head, every operand copied into LDS as whole row segments,
-// 16x16x32 bf16 MFMAs.
+// weights once (16 MiB each for 128 heads): one wave per 64 output columns
+// (absorb_q) or 16 output rows (expand_v), in workgroups of one wave (fewer
+// than 64 heads) or four, every operand copied into LDS as whole row
+// segments, 16x16x32 bf16 MFMAs.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -155,52 +155,58 @@ __global__ __launch_bounds__(64 * NW) void absorb_q_kernel(ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// expand_v: workgroup = (head h, row half jh): out[b][h][64 jh + j].
-//   LDS: W_UV[h][64 jh .. +64][:] as 64 rows of 1 KiB (chunk ^ j % 16) and
-//        o_lat[b][h][:] as 32 rows of 1 KiB (chunk ^ b % 16).
-//   D[j][b] = W . O^T on 16x16x32 MFMAs over the 512 latent columns; wave w
-//   owns rows 16 w .. +15 of the half.
+// expand_v: wave = (head h, 16 output rows jb): out[b][h][16 jb + j];
+// workgroup = NW waves on consecutive row blocks of one head, sharing its
+// o_lat rows.
+//   LDS: W_UV[h][16 jb .. +16][:] as 16 rows of 1 KiB per wave (chunk ^ j % 16)
+//        and o_lat[b][h][:] as 32 rows of 1 KiB (chunk ^ b % 16), shared.
+//   D[j][b] = W . O^T on 16x16x32 MFMAs over the 512 latent columns.
+// NW = 4 (two workgroups per head) from 64 heads; below, one wave per
+// workgroup (8 per head) spreads the launch over more CUs.  o_lat rows past
+// the batch are not copied: the MFMA columns they feed are not stored.
 // ---------------------------------------------------------------------------
-constexpr int kExpRows = 64;                       // output rows (j) per workgroup
-constexpr int kExpW = kExpRows * kDc * 2;          // 64 KiB
+constexpr int kExpRows = 16;                       // output rows (j) per wave
+constexpr int kExpBlocks = kDv / kExpRows;         // waves per head
+constexpr int kExpW = kExpRows * kDc * 2;          // 16 KiB per wave
 constexpr int kExpO = kProjRows * kDc * 2;         // 32 KiB
 
-__global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kExpW + kExpO];
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void expand_v_kernel(ProjArgs a) {
+  static_assert(kExpBlocks % NW == 0 && kProjRows % NW == 0, "blocks and rows split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[NW * kExpW + kExpO];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  const uint32_t wl = lds0, ol = lds0 + kExpW;
-  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
-  const int h = item >> 1, jh = item & 1;
   const int w = wave_id();
+  const uint32_t wl = lds0 + (uint32_t)w * kExpW, ol = lds0 + NW * kExpW;
+  constexpr int kGroups = kExpBlocks / NW;  // workgroups per head
+  const int item = xcd_grouped_index(blockIdx.x, gridDim.x);
+  const int h = item / kGroups, jb = (item - h * kGroups) * NW + w;
   const int nl = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
   const size_t orow_bytes = (size_t)a.num_heads * kDc * 2;
 
-  // W rows 64 jh .. +63 (contiguous 64 KiB): copy k (16 per wave) = row k
+  // W rows 16 jb .. +15 (contiguous 16 KiB): copy k (16) = row k
   {
     const uint32_t ln = lane_id();
-    const char* wsrc = reinterpret_cast<const char*>(a.w + ((size_t)h * kDv + kExpRows * jh) * kDc);
+    const char* wsrc = reinterpret_cast<const char*>(a.w + ((size_t)h * kDv + kExpRows * jb) * kDc);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = 16 * w + i;
+    for (int k = 0; k < 16; ++k)
       dma16(uniform_ptr(wsrc + (size_t)k * (kDc * 2)), (ln ^ (uint32_t)(k & 15)) * 16, wl + k * 1024);
-    }
   }
-  // o_lat rows b0 .. b0+31: copy k (8 per wave) = row k
+  // o_lat rows b0 .. b0+31 below the batch: copy k (k % NW = w) = row k
   auto stage_o = [&](int b0) {
     const uint32_t ln = lane_id();
     const char* obase = reinterpret_cast<const char*>(a.x + (size_t)h * kDc);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = 8 * w + i;
-      const int br = min(b0 + k, a.batch - 1);
-      dma16(uniform_ptr(obase + (size_t)br * orow_bytes), (ln ^ (uint32_t)(k & 15)) * 16, ol + k * 1024);
+    for (int i = 0; i < kProjRows / NW; ++i) {
+      const int k = NW * i + w;
+      if (b0 + k < a.batch)
+        dma16(uniform_ptr(obase + (size_t)(b0 + k) * orow_bytes), (ln ^ (uint32_t)(k & 15)) * 16, ol + k * 1024);
     }
   };
   stage_o(0);
   wait_vmcnt<0>();
   barrier();
 
-  const uint32_t jrow = 16 * w + nl;  // A row of this lane
+  const uint32_t jrow = (uint32_t)nl;  // A row of this lane (within the wave's 16 rows)
   for (int b0 = 0; b0 < a.batch; b0 += kProjRows) {
     if (b0 > 0) {
       stage_o(b0);
@@ -219,13 +225,13 @@ __global__ __launch_bounds__(256) void expand_v_kernel(ProjArgs a) {
         acc[mb] = mfma16(aw, bo, acc[mb]);
       }
     }
-    // D[j = 16 w + 4 g + r][b = 16 mb + nl]: four consecutive output columns
+    // D[j = 16 jb + 4 g + r][b = b0 + 16 mb + nl]: four consecutive output columns
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int b = b0 + 16 * mb + nl;
       if (b < a.batch) {
         const u32x2 v = {pack_bf16x2(acc[mb][0], acc[mb][1]), pack_bf16x2(acc[mb][2], acc[mb][3])};
-        *reinterpret_cast<u32x2*>(a.y + ((size_t)b * a.num_heads + h) * kDv + kExpRows * jh + 16 * w + 4 * g) = v;
+        *reinterpret_cast<u32x2*>(a.y + ((size_t)b * a.num_heads + h) * kDv + kExpRows * jb + 4 * g) = v;
       }
     }
     barrier();  // the o_lat rows are reused
@@ -493,7 +499,10 @@ hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_expand_v(const ProjArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(expand_v_kernel, dim3(a.num_heads * (kDv / kExpRows)), dim3(256), 0, stream, a);
+  if (a.num_heads >= 64)
+    hipLaunchKernelGGL(expand_v_kernel<4>, dim3(a.num_heads * (kExpBlocks / 4)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(expand_v_kernel<1>, dim3(a.num_heads * kExpBlocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
