@@ -78,13 +78,15 @@ __global__ __launch_bounds__(64 * NW) void absorb_q_kernel(ProjArgs a) {
   }
   // query rows b0 .. b0+31: copy k (8 per workgroup, k % NW = w) = rows 4k ..
   // 4k+3 (lane l: row 4k + l/16, slot l % 16); rows past the batch re-read
-  // the last one
+  // the last one, and copies that hold no row of the batch are skipped (the
+  // MFMA columns of those rows are not stored)
   auto stage_q = [&](int b0) {
     const char* qbase = reinterpret_cast<const char*>(a.x + (size_t)h * kDn);
 #pragma unroll
     for (int i = 0; i < 8 / NW; ++i) {
       const int k = NW * i + w;
-      const int r0 = min(b0 + 4 * k, a.batch - 1);
+      if (b0 + 4 * k >= a.batch) continue;
+      const int r0 = b0 + 4 * k;
       const uint32_t row = 4 * k + (ln >> 4);
       const int br = min(b0 + (int)row, a.batch - 1);
       const uint32_t src = (ln & 15u) ^ (row & 15u);
