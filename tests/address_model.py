@@ -1,4 +1,5 @@
-"""Host-side model of every memory access the three decode kernels make.
+"""Host-side model of every memory access the decode kernels make (and, at
+the end, the absorb_q / expand_v projection kernels).
 
 For a launch description (the kernel arguments) this module enumerates, per
 workgroup, wave and lane, the address arithmetic of the kernels as written in
@@ -735,4 +736,182 @@ def check_narrow(L, max_items=None):
                     col = w * C + ch * 8
                     _need((grow < row_hi) & (col + 8 <= 512), "o store outside the rows")
                     counts["stores"] += 64
+    return counts
+
+
+# ---------------------------------------------------------------------------
+# Projection kernels (csrc/proj_combine.hip): absorb_q_kernel<NW> and
+# expand_v_kernel<NW>, NW = 4 waves per workgroup from 64 heads, else 1.
+# Byte offsets are relative to each buffer's start: W [H, 128, 512] bf16,
+# q_nope [B, H, 128], q_lat [B, H, 512], o_lat [B, H, 512], out [B, H, 128].
+# Besides the bounds, the model checks that every fragment read finds the
+# bytes the MFMA operand needs (the copies' swizzle undone).
+# ---------------------------------------------------------------------------
+PROJ_ROWS = 32
+
+
+def proj_waves(H):
+    return 4 if H >= 64 else 1
+
+
+def check_absorb_q(B, H):
+    """Every copy, LDS access and store of absorb_q_kernel<NW> for B x H."""
+    NW = proj_waves(H)
+    groups = 8 // NW
+    lds_w, lds_q, lds_o = 16384, 8192, 4096
+    smem = NW * lds_w + lds_q + NW * lds_o
+    ln = np.arange(64)
+    nl, g = ln & 15, ln >> 4
+    qrow_bytes = H * 128 * 2
+    counts = dict(workgroups=0, copies=0, stores=0)
+    for item in range(H * groups):
+        counts["workgroups"] += 1
+        h = item // groups
+        full = h == 0  # the fragment contents do not depend on the head: check them for one
+        for w in range(NW):
+            cb = (item % groups) * NW + w
+            wl, ol = w * lds_w, NW * lds_w + lds_q + w * lds_o
+            _need(cb < 8, "column block past the head")
+            # W block copies: LDS slot (row, slot) <- W[h][row][64 cb + 8 chunk ..]
+            lds_src = {}
+            for k in range(16):
+                src = (ln & 7) ^ (2 * (k & 3))
+                row = 8 * k + (ln >> 3)
+                off = (h * 128 * 512 + cb * 64) * 2 + 8 * k * 1024 + (ln >> 3) * 1024 + src * 16
+                row_start = (h * 128 + row) * 1024
+                _need((off >= row_start + cb * 128) & (off + 16 <= row_start + cb * 128 + 128),
+                      "W_UK read outside the block's row segment")
+                dst = wl + k * 1024 + ln * 16
+                _need((dst >= wl) & (dst + 16 <= wl + lds_w), "W block copy outside the wave's LDS region")
+                if full:
+                    for i in range(64):
+                        lds_src[int(dst[i]) - wl] = (int(row[i]), int(src[i]))
+                counts["copies"] += 1
+            # A fragments: transposing reads of 4 rows x 8 bytes
+            for s in range(4 if full else 0):
+                for ct in range(4):
+                    colb = 32 * ct + (nl & 3) * 8
+                    for e in range(2):
+                        row = 32 * s + 8 * g + 4 * e + (nl >> 2)
+                        chunk = (colb >> 4) ^ (2 * ((row >> 3) & 3))
+                        addr = wl + row * 128 + (chunk << 4) + (colb & 15)
+                        _need((addr >= wl) & (addr + 8 <= wl + lds_w), "W fragment read outside the region")
+                        for i in range(64):
+                            slot_start = int(addr[i]) - wl - (int(colb[i]) & 15)
+                            r, c = lds_src[slot_start]
+                            _need(r == int(row[i]) and c == int(colb[i]) >> 4, "W fragment is not its chunk")
+            for b0 in range(0, B, PROJ_ROWS):
+                q_src = {}
+                for w2 in range(NW):
+                    for i2 in range(8 // NW):
+                        k = NW * i2 + w2
+                        if b0 + 4 * k >= B:
+                            continue
+                        r0 = b0 + 4 * k
+                        row = 4 * k + (ln >> 4)
+                        br = np.minimum(b0 + row, B - 1)
+                        src = (ln & 15) ^ (row & 15)
+                        off = h * 256 + r0 * qrow_bytes + (br - r0) * qrow_bytes + src * 16
+                        _need((off >= br * qrow_bytes + h * 256) & (off + 16 <= br * qrow_bytes + h * 256 + 256),
+                              "q_nope read outside the head's row")
+                        _need(br < B, "q_nope row past the batch")
+                        dst = NW * lds_w + k * 1024 + ln * 16
+                        _need((dst >= NW * lds_w) & (dst + 16 <= NW * lds_w + lds_q), "query copy outside its LDS")
+                        if full:
+                            for i in range(64):
+                                q_src[int(dst[i]) - NW * lds_w] = (int(row[i]), int(src[i]))
+                for mb in range(2):
+                    brow = 16 * mb + nl
+                    for s in range(4):
+                        addr = NW * lds_w + brow * 256 + (((4 * s) + g) ^ (brow & 15)) * 16
+                        _need((addr >= NW * lds_w) & (addr + 16 <= NW * lds_w + lds_q), "query read outside")
+                        for i in range(64 if full else 0):
+                            if b0 + int(brow[i]) < B:  # rows past the batch feed columns that are not stored
+                                r, c = q_src[int(addr[i]) - NW * lds_w]
+                                _need(r == int(brow[i]) and c == 4 * s + int(g[i]), "query fragment is not its chunk")
+                    for ct in range(4):
+                        c = 16 * ct + 4 * g
+                        chunk = (c >> 3) ^ (brow & 7)
+                        addr = ol + brow * 128 + (chunk << 4) + (c & 7) * 2
+                        _need((addr >= ol) & (addr + 8 <= ol + lds_o), "output staging write outside")
+                for k in range(4):
+                    idx = 64 * k + ln
+                    row, chunk = idx >> 3, idx & 7
+                    addr = ol + row * 128 + ((chunk ^ (row & 7)) << 4)
+                    _need((addr >= ol) & (addr + 16 <= ol + lds_o), "output staging read outside")
+                    b = b0 + row
+                    st = ((b * H + h) * 512 + cb * 64 + chunk * 8) * 2
+                    ok = b < B
+                    _need(~ok | ((st >= ((b * H + h) * 512 + cb * 64) * 2) & (st + 16 <= ((b * H + h) * 512 + cb * 64 + 64) * 2)),
+                          "q_lat store outside the block's row segment")
+                    counts["stores"] += int(ok.sum())
+        _need(smem <= 160 * 1024, "LDS budget")
+    return counts
+
+
+def check_expand_v(B, H):
+    """Every copy, LDS access and store of expand_v_kernel<NW> for B x H."""
+    NW = proj_waves(H)
+    groups = 8 // NW
+    lds_w, lds_o = 16384, 32768
+    ln = np.arange(64)
+    nl, g = ln & 15, ln >> 4
+    orow_bytes = H * 512 * 2
+    counts = dict(workgroups=0, copies=0, stores=0)
+    for item in range(H * groups):
+        counts["workgroups"] += 1
+        h = item // groups
+        full = h == 0  # the fragment contents do not depend on the head: check them for one
+        for w in range(NW):
+            jb = (item % groups) * NW + w
+            wl = w * lds_w
+            _need(jb < 8, "row block past the head")
+            w_src = {}
+            for k in range(16):
+                off = ((h * 128 + 16 * jb) * 512) * 2 + k * 1024 + (ln ^ (k & 15)) * 16
+                row_start = (h * 128 + 16 * jb + k) * 1024
+                _need((off >= row_start) & (off + 16 <= row_start + 1024), "W_UV read outside its row")
+                dst = wl + k * 1024 + ln * 16
+                _need((dst >= wl) & (dst + 16 <= wl + lds_w), "W copy outside the wave's LDS region")
+                for i in range(64 if full else 0):
+                    w_src[int(dst[i]) - wl] = (k, int(ln[i]) ^ (k & 15))
+                counts["copies"] += 1
+            for b0 in range(0, B, PROJ_ROWS):
+                o_src = {}
+                for w2 in range(NW):
+                    for i2 in range(PROJ_ROWS // NW):
+                        k = NW * i2 + w2
+                        if b0 + k >= B:
+                            continue
+                        off = h * 1024 + (b0 + k) * orow_bytes + (ln ^ (k & 15)) * 16
+                        rs = (b0 + k) * orow_bytes + h * 1024
+                        _need((off >= rs) & (off + 16 <= rs + 1024), "o_lat read outside its row")
+                        dst = NW * lds_w + k * 1024 + ln * 16
+                        _need((dst >= NW * lds_w) & (dst + 16 <= NW * lds_w + lds_o), "o_lat copy outside its LDS")
+                        for i in range(64 if full else 0):
+                            o_src[int(dst[i]) - NW * lds_w] = (k, int(ln[i]) ^ (k & 15))
+                jrow = nl
+                for s in range(16):
+                    chunk = 4 * s + g
+                    addr = wl + jrow * 1024 + ((chunk ^ (jrow & 15)) << 4)
+                    _need((addr >= wl) & (addr + 16 <= wl + lds_w), "W fragment read outside")
+                    for i in range(64 if full else 0):
+                        r, c = w_src[int(addr[i]) - wl]
+                        _need(r == int(jrow[i]) and c == int(chunk[i]), "W fragment is not its chunk")
+                    for mb in range(2):
+                        brow = 16 * mb + nl
+                        addr = NW * lds_w + brow * 1024 + ((chunk ^ (brow & 15)) << 4)
+                        _need((addr >= NW * lds_w) & (addr + 16 <= NW * lds_w + lds_o), "o_lat fragment read outside")
+                        for i in range(64 if full else 0):
+                            if b0 + int(brow[i]) < B:
+                                r, c = o_src[int(addr[i]) - NW * lds_w]
+                                _need(r == int(brow[i]) and c == int(chunk[i]), "o_lat fragment is not its chunk")
+                for mb in range(2):
+                    b = b0 + 16 * mb + nl
+                    st = ((b * H + h) * 128 + 16 * jb + 4 * g) * 2
+                    ok = b < B
+                    rs = ((b * H + h) * 128 + 16 * jb) * 2
+                    _need(~ok | ((st >= rs) & (st + 8 <= rs + 32)), "out store outside the block's row segment")
+                    counts["stores"] += int(ok.sum())
+    _need(NW * lds_w + lds_o <= 160 * 1024, "LDS budget")
     return counts

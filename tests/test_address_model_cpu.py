@@ -1,6 +1,7 @@
-"""Every cache read, LDS access and output store of the three decode kernels
-stays in bounds (tests/address_model.py: the kernels' address arithmetic on
-the host), for the shapes the GPU tests use and the five benchmark
+"""Every cache read, LDS access and output store of the decode kernels (and
+of the absorb_q / expand_v projections) stays in bounds
+(tests/address_model.py: the kernels' address arithmetic on the host), for
+the shapes the GPU tests use and the five benchmark
 workloads at full size -- including the copies issued past the last tile,
 the clamped rows of ragged tiles, split boundaries, planned items, paged
 caches with 32-, 64- and 256-token blocks, E4M3 tiles (64-row tiles in two
@@ -9,7 +10,8 @@ import numpy as np
 import pytest
 
 from mla_absorbed_latent_absorb_amd import binding
-from tests.address_model import Launch, Violation, check_fp8, check_latent16, check_narrow, check_wide
+from tests.address_model import (Launch, Violation, check_absorb_q, check_expand_v, check_fp8, check_latent16,
+                                 check_narrow, check_wide)
 
 
 def _paged(lens, bs, seed):
@@ -139,3 +141,16 @@ def test_checker_catches_unclamped_ragged_rows(monkeypatch):
     monkeypatch.setattr(am, "CLAMP_RAGGED_ROWS", False)
     with pytest.raises(Violation):
         check_wide(L)
+
+
+# The projection kernels (absorb_q_kernel<NW>, expand_v_kernel<NW>): the GPU
+# tests' shapes and the five workloads' (batch, heads).
+@pytest.mark.parametrize("B,H", [(1, 16), (5, 16), (64, 16), (3, 32), (17, 64), (130, 64), (200, 16), (32, 128),
+                                 (64, 128), (128, 128)])
+def test_projection_kernels_in_bounds(B, H):
+    a = check_absorb_q(B, H)
+    e = check_expand_v(B, H)
+    # one 16-byte q_lat store per 8 columns, one 8-byte out store per 4 columns
+    assert a["stores"] == B * H * 512 // 8
+    assert e["stores"] == B * H * 128 // 4
+    assert a["copies"] == e["copies"] == H * 8 * 16
