@@ -13,10 +13,12 @@ Prints one JSON line:
   value           latent-KV GB/s of the headline workload (V3, B=32, 4096
                   tokens) over the whole step: W untimed steps, then the K
                   steps as one HIP graph replay between two synchronisations,
-                  its GPU time from HIP events at the replay's ends (the host
-                  clock around it: ms_per_step_host_clock)
-  step_us_stats   per-step time over 7 more replays, each timed with HIP
-                  events at its ends: median / p10 / p90
+                  its GPU time from HIP events at the replay's ends, with a
+                  spin kernel ahead of the first event so that the host's
+                  submission of the graph is not timed (the host clock around
+                  another replay: ms_per_step_host_clock)
+  step_us_stats   per-step time over 7 more replays, each timed the same
+                  way: median / p10 / p90
   roofline        the dominant kernel (mla_decode_latent): algorithmic cache
                   bytes per launch / its mean launch duration (HIP events at the
                   ends of graph replays of 16 back-to-back launches on the
@@ -541,9 +543,11 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
     rotate so the working set exceeds the 256 MB Infinity Cache.
 
       headline      `steps` steps as ONE HIP graph replay between two
-                    synchronisations (host clock)
-      step_us       per-step time of >= 5 more replays (HIP events at the
-                    start and end of each replay): median / p10 / p90
+                    synchronisations (HIP events at its ends, a spin kernel
+                    ahead of them while the host submits the graph; the host
+                    clock around another replay beside it)
+      step_us       per-step time of 7 more replays timed the same way:
+                    median / p10 / p90
       decode_us     mla_decode_latent[_planned] alone: 16 launches (inputs
                     rotating over the replicas) captured in a HIP graph, 9
                     replays each timed with HIP events at its ends on the
@@ -605,29 +609,35 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
             run(i)
     graph.replay()  # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
-    # The timed region: exactly the K steps, one graph replay between two
-    # synchronisations.  Its GPU time comes from HIP events recorded at the
-    # replay's two ends on the launch stream; the host clock around the same
-    # region also holds one graph launch and one synchronisation and is
-    # reported beside it.  (A replay of few steps costs more per step than a
-    # long one on the GPU too: ~66 us per V3 step at K = 20 against ~62 us at
-    # K = 200.)
-    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The host clock around one replay between two synchronisations (one
+    # graph launch and one synchronisation included).
     t0 = time.perf_counter()
-    e_start.record()
     graph.replay()
-    e_end.record()
     torch.cuda.synchronize()
     t_host = (time.perf_counter() - t0) / steps
-    t_step = e_start.elapsed_time(e_end) * 1e-3 / steps
-    # repeated replays: per-step time from HIP events at each replay's ends
-    per_step = []
-    n_rep = 7
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
-    for e0, e1 in evs:
+    # The timed region: exactly the K steps, one graph replay between two
+    # synchronisations, its GPU time from HIP events recorded at the replay's
+    # two ends on the launch stream.  A spin kernel queued before the first
+    # event keeps the GPU busy while the host submits the graph's launches
+    # (~1 us each), so the events time the steps' execution, not the
+    # submission lag that an idle GPU would wait through (at K = 20 that lag
+    # adds ~3-6 us per V3 step; at K = 200 the figures agree).
+    spin_cycles = int(2e6 + 4000 * 3 * steps)
+
+    def timed_replay():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(spin_cycles)
         e0.record()
         graph.replay()
         e1.record()
+        return e0, e1
+
+    e_start, e_end = timed_replay()
+    torch.cuda.synchronize()
+    t_step = e_start.elapsed_time(e_end) * 1e-3 / steps
+    # repeated replays, each timed the same way
+    n_rep = 7
+    evs = [timed_replay() for _ in range(n_rep)]
     torch.cuda.synchronize()
     per_step = [e0.elapsed_time(e1) * 1e-3 / steps for e0, e1 in evs]
     sclk = None
@@ -810,13 +820,15 @@ def main():
         "ms_per_step_eager": round(head["t_eager"] * 1e3, 5),
         "step_timing": "the K steps as one HIP graph replay between two synchronisations (three launches per "
                        "step: absorb_q, decode_latent, combine_expand_v or expand_v), GPU time from HIP events "
-                       "at the replay's ends (ms_per_step_host_clock: the host clock around the same region, "
-                       "which adds one graph launch and one synchronisation); step_us: 7 more replays timed "
-                       "with HIP events",
+                       "at the replay's ends, a spin kernel queued before the first event so that the host's "
+                       "submission of the graph's launches is not timed (ms_per_step_host_clock: the host clock "
+                       "around another replay between two synchronisations, which adds one graph launch and the "
+                       "GPU's wait for it); step_us: 7 more replays timed the same way",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "fp8_e4m3 cache / bf16 MFMA",
+        "dtype": "bf16" if wl.dtype == "bf16" else
+                 "fp8_e4m3 cache / " + ("fp8 MFMA" if x0.heads == 128 else "bf16 MFMA"),
         "data": "synthetic (seeded N(0,1) cache and queries, N(0,1/512) weights; no checkpoint)",
         "config": {"workload": wl.name, "batch": x0.batch, "heads": x0.heads, "seq_len": x0.max_seq_len,
                    "kv_lora_rank": 512, "qk_rope_head_dim": 64, "layout": wl.layout, "cache_dtype": wl.dtype,
