@@ -77,6 +77,24 @@ GUARD_BYTES = 64 * 1024
 _PATTERN16 = -63  # int16 view of 0xFFC1
 
 
+def mismatch_report(a, c, names=None):
+    """Where two equally shaped tensors differ bit for bit: the count, the
+    first differing indices (named by `names`), NaN counts and the largest
+    difference -- printed by bitwise tests before they fail."""
+    a_bits = a.contiguous().view(-1).view(torch.int16 if a.element_size() == 2 else torch.int32)
+    c_bits = c.contiguous().view(-1).view(torch.int16 if c.element_size() == 2 else torch.int32)
+    diff = (a_bits != c_bits).nonzero().view(-1).cpu()
+    if diff.numel() == 0:
+        return "bit-identical"
+    idx = [np.unravel_index(int(i), tuple(a.shape)) for i in diff[:8]]
+    fa, fc = a.float(), c.float()
+    both = torch.isfinite(fa) & torch.isfinite(fc)
+    md = float((fa - fc)[both].abs().max()) if bool(both.any()) else float("nan")
+    head = ", ".join(names) if names else "index"
+    return (f"{diff.numel()} of {a.numel()} differ; first ({head}): {[tuple(int(v) for v in i) for i in idx]}; "
+            f"NaN {int(torch.isnan(fa).sum())} / {int(torch.isnan(fc).sum())}; max |diff| {md:.3g}")
+
+
 class Guarded:
     def __init__(self, shape, dtype, device):
         elem = torch.empty((), dtype=dtype).element_size()

@@ -17,7 +17,8 @@ import torch
 
 import oracle
 from mla_absorbed_latent_absorb_amd import binding, datagen
-from tests.gpu_helpers import (TOL_BF16, TOL_FP8, assert_guards, bits8, bits16, cache_args, f64, guarded, rel_err, tol_for,
+from tests.gpu_helpers import (TOL_BF16, TOL_FP8, assert_guards, bits8, bits16, cache_args, f64, guarded,
+                               mismatch_report, rel_err, tol_for,
                                split_bounds)
 
 pytestmark = pytest.mark.gpu
@@ -248,6 +249,10 @@ def test_paged_block_sizes(bs, H, workload):
         a = binding.mla_decode_latent(d, contig, q_lat, x.q_pe, x.seq_lens, T, P)
         c = binding.mla_decode_latent(d, paged, q_lat, x.q_pe, x.seq_lens, T, P)
         torch.cuda.synchronize()
+        if not (torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])):
+            names = ("b", "split", "head", "col") if P > 1 else ("b", "head", "col")
+            print(f"P={P} o: {mismatch_report(a[0], c[0], names)}", flush=True)
+            print(f"P={P} lse: {mismatch_report(a[1], c[1], names[:-1])}", flush=True)
         assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1]), P
         if P == 1:
             ref_o, ref_l = oracle.latent_decode(f64(q_lat), f64(x.q_pe), seq_lens=x.seq_lens.cpu().numpy(),
