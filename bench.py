@@ -623,10 +623,12 @@ def measure_config(name, dev, steps, warmup, splits=0, replicas=0, sample_sclk=F
     # submission lag that an idle GPU would wait through (at K = 20 that lag
     # adds ~3-6 us per V3 step; at K = 200 the figures agree).
     spin_cycles = int(2e6 + 4000 * 3 * steps)
+    spin = getattr(torch.cuda, "_sleep", None)  # torch's bounded spin kernel
 
     def timed_replay():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(spin_cycles)
+        if spin is not None:
+            spin(spin_cycles)
         e0.record()
         graph.replay()
         e1.record()
