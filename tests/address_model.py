@@ -261,7 +261,7 @@ def check_wide(L, max_items=None):
 
 
 # ---------------------------------------------------------------------------
-# 128-head E4M3 kernel (decode_latent_fp8_kernel<PAGED>)
+# 128-head E4M3 kernel (decode_latent_fp8_kernel<PAGED, STREAM>)
 # ---------------------------------------------------------------------------
 
 T8 = 64   # rows per tile
